@@ -1,0 +1,209 @@
+/*
+ * lora.h -- C ABI of the routed multi-tenant LoRA delta for MI355X (gfx950).
+ *
+ * The operation (metrale docs, module lora_delta, function apply_lora_bgmv;
+ * vLLM punica_base.py, PunicaWrapperBase.add_shrink / add_expand /
+ * add_lora_linear): every row i of a batch that names an adapter slot
+ * s = slot[i] >= 0 gets
+ *
+ *     y[i, :] += scale[s] * (x[i, :] @ A_s^T) @ B_s^T
+ *
+ * computed as a shrink (xa = scale * x @ A^T, fp32) then an expand
+ * (y += xa @ B^T).  A row with a negative slot gets no delta.  The routed-MoE
+ * variant (FlashInfer docs, flashinfer.fused_moe.bgmv_moe_gemm1_lora_delta)
+ * gives one gate/up delta per (token, top-k slot).
+ *
+ * Conventions for every function below:
+ *  - bf16 values travel as uint16_t bit patterns; float is IEEE binary32.
+ *  - Every array pointer is a DEVICE pointer unless marked [host].
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it: no call allocates, frees, synchronizes, prints or
+ *    aborts (metrale docs, module lora_delta invariants: launchers only
+ *    launch).  Pointers must stay valid until the stream reaches the call.
+ *  - The caller owns every buffer, including metadata and workspaces.  The
+ *    library keeps no pointer after a call returns and holds no state
+ *    besides the MFMA row threshold (lora_set_mfma_min_rows).
+ *  - Every check that can run on the host runs before any launch and
+ *    returns an error code; nothing is enqueued then.
+ *  - Workspaces hold counters that must be zero before their first use
+ *    (allocate them zero-filled); every call leaves them zero again.
+ *    Calls that share a workspace must be ordered (same stream).
+ *
+ * Layouts (metrale docs, LoraPair and LoraRoute; the slices follow vLLM's
+ * add_shrink / add_expand, one A and one block of B rows per output slice):
+ *    x       [n][ldx]                       bf16, row-major, k_in used columns
+ *    a_pool  [num_slots][num_slices][max_rank][k_in]   bf16
+ *    b_pool  [num_slots][N][max_rank]       bf16, N = sum(slice_sizes);
+ *                                            slice l owns rows off_l .. off_l+w_l
+ *    scale   [num_slots]                    float (applied to the fp32 shrink
+ *                                            result, never folded into B)
+ *    xa      [num_slices][n][max_rank]      float
+ *    y       [n][ldy]                       bf16, slice l's window is columns
+ *                                            offset_start+off_l .. +w_l
+ * An adapter of true rank r < max_rank is stored zero-padded: rows r.. of A
+ * and columns r.. of B are zero, and both stages contract at max_rank.
+ *
+ * Shape limits: k_in (H) and every slice width a multiple of 8; max_rank
+ * (rank) a multiple of 8, at most 128; 1 <= num_slices <= 8; ldx, ldy,
+ * offset_start multiples of 8; x, y, xa, pools 16-byte aligned;
+ * num_slots <= 1<<20; n <= 1<<22.
+ */
+#ifndef TENANT_LORA_H
+#define TENANT_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    LORA_OK = 0,
+    LORA_EINVAL = -1,       /* bad pointer, size, alignment or leading dimension */
+    LORA_EUNSUPPORTED = -2, /* a shape outside the limits above */
+    LORA_EWORKSPACE = -3,   /* workspace or metadata buffer too small */
+    LORA_ELAUNCH = -4       /* the HIP runtime refused a launch */
+};
+
+/* Rows per tile of the per-segment work lists built by lora_meta_build. */
+#define LORA_TILE_ROWS 16
+/* int32 words per tile record. */
+#define LORA_TILE_WORDS 32
+
+/*
+ * Per-step routing metadata, built once per batch by lora_meta_build and read
+ * by every shrink / expand / fused call of that batch (vLLM punica_base.py,
+ * PunicaWrapperBase: metadata updated once per step and reused by all LoRA
+ * layers; prefill_metadata groups rows of one adapter into segments).
+ * Active rows (0 <= slot < num_slots) are sorted by (slot, row); a segment is
+ * a run of one slot.  Sizes in elements:
+ *   sorted_rows  [n]                 active rows in (slot, row) order
+ *   seg_offsets  [min(n,S) + 1]      segment starts in sorted_rows, then n_active
+ *   seg_slot     [min(n,S)]          each segment's slot, strictly ascending
+ *   counts       [8]                 {n_active, n_segments, n_invalid,
+ *                                     n_segments_with_at_least_16_rows,
+ *                                     n_tiles, 0, 0, 0}
+ *   tiles        [lora_meta_max_tiles(n,S) * LORA_TILE_WORDS]
+ *       Each segment is cut into tiles of at most 16 consecutive sorted rows.
+ *       Record t (32 int32): [0] slot, [1] first sorted position, [2] rows in
+ *       the tile (0 marks an unused record), [3] rows in the whole segment,
+ *       [4] segment index, [8..23] the tile's original row ids.
+ * Entries past n_active / n_segments are left unwritten.
+ */
+typedef struct {
+    int32_t *sorted_rows;
+    int32_t *seg_offsets;
+    int32_t *seg_slot;
+    int32_t *counts;
+    int32_t *tiles;
+} lora_meta_t;
+
+/* Number of tile records the tiles array must hold for n rows and S slots:
+ * min(n, ceil(n/16) + min(n, S)). */
+int32_t lora_meta_max_tiles(int32_t n, int32_t num_slots);
+
+/* Workspace bytes lora_meta_build needs for n rows and S slots. */
+size_t lora_meta_workspace_bytes(int32_t n, int32_t num_slots);
+
+/*
+ * Build the metadata for slot[n] (int32; negative = no delta; >= num_slots =
+ * invalid, excluded and counted in counts[2]).  All meta arrays are written
+ * on the device; the result is unique (bit-exact).  n == 0 writes
+ * counts = 0 and seg_offsets[0] = 0.  num_slots in [1, 1<<20]; when n > 1024
+ * num_slots must be at most 16384 (LORA_EUNSUPPORTED otherwise).
+ */
+int lora_meta_build(const int32_t *slot, int32_t n, int32_t num_slots, lora_meta_t meta,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Shrink (vLLM punica_base.py, add_shrink semantics; metrale lora_delta,
+ * apply_lora_bgmv): for every active row i with slot s, slice l, rank r:
+ *     xa[l][i][r] = scale[s] * sum_k x[i][k] * a_pool[s][l][r][k]
+ * accumulated in fp32 from exact bf16 products.  Rows without an active slot
+ * are not written.  xa is [num_slices][n][max_rank] float.
+ */
+int lora_shrink(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in,
+                const uint16_t *a_pool, const float *scale, int32_t num_slots,
+                int32_t num_slices, int32_t max_rank, lora_meta_t meta, float *xa,
+                void *stream);
+
+/*
+ * Expand (vLLM punica_base.py, add_expand semantics): for every active row i
+ * with slot s, slice l of width w_l at offset off_l, column c < w_l:
+ *     y[i][offset_start + off_l + c] = (add_inputs ? y[i][...] : 0)
+ *                                      + sum_r xa[l][i][r] * b_pool[s][off_l + c][r]
+ * accumulated in fp32, rounded once to bf16 (nearest-even).  Every other
+ * element of y is left untouched.  slice_sizes is a [host] array of
+ * num_slices widths.
+ */
+int lora_expand(const float *xa, const uint16_t *b_pool, int32_t num_slots,
+                int32_t num_slices, const int32_t *slice_sizes, int32_t max_rank, int32_t n,
+                lora_meta_t meta, uint16_t *y, int64_t ldy, int32_t offset_start,
+                int32_t add_inputs, void *stream);
+
+/* Workspace bytes lora_delta_fused needs. */
+size_t lora_fused_workspace_bytes(int32_t n, int32_t num_slots, int32_t num_slices,
+                                  int32_t max_rank, int32_t k_in);
+
+/*
+ * Fused delta (vLLM punica_base.py, add_lora_linear semantics; metrale
+ * lora_delta, apply_lora_bgmv): the shrink then the expand with
+ * add_inputs = 1, in one launch; xa stays in the workspace (fp32).
+ *     y[i][window] += (scale[s] * x[i] @ A_s^T) @ B_s^T
+ * Rows without an active slot and columns outside the slice windows are
+ * left untouched.  Segments with at least 16 rows run on bf16 MFMA with the
+ * fp32 xa split into two bf16 terms; shorter ones on the vector ALU.
+ */
+int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in,
+                     const uint16_t *a_pool, const uint16_t *b_pool, const float *scale,
+                     int32_t num_slots, int32_t num_slices, const int32_t *slice_sizes,
+                     int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
+                     int32_t offset_start, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_lora_gemm1_delta needs. */
+size_t moe_lora_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts,
+                                int32_t num_loras, int32_t rank, int32_t H);
+
+/*
+ * Routed-MoE gemm1 (gate_up) LoRA delta (FlashInfer docs,
+ * flashinfer.fused_moe.bgmv_moe_gemm1_lora_delta).  For pair (t, j) with
+ * expert e = topk_ids[t][j] and adapter l = lora_ids[t]:
+ *   regular (shared_a == 0): w_ptr_a / w_ptr_b are [2][num_experts] int64
+ *     tables of device addresses (gate row 0, up row 1); adapter l's matrices
+ *     for expert e start lora_stride elements * l past the table entry;
+ *     A is [rank][H], B is [inter][rank] (bf16), and
+ *       out[t][j][:] = scale * concat(B_gate @ (A_gate @ x[t]), B_up @ (A_up @ x[t]))
+ *   shared (shared_a != 0): the tables are [num_experts]; A is [rank][H],
+ *     B is [2*inter][rank] (gate rows then up rows), and
+ *       out[t][j][:] = scale * B @ (A @ x[t])
+ * l < 0 gives a zero row.  l >= num_loras or e outside [0, num_experts) gives
+ * a zero row and is counted: after the call the first 16 bytes of ws hold
+ * counts {n_active_pairs, n_segments, n_invalid_pairs, n_long_segments}.
+ * The delta is unweighted and kept per pair (it is added before the gated
+ * activation).  out is [T][top_k][2*inter] bf16, every element written.
+ */
+int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H,
+                         const int64_t *w_ptr_a, int64_t lora_stride_a,
+                         const int64_t *w_ptr_b, int64_t lora_stride_b, int32_t shared_a,
+                         const int32_t *topk_ids, int32_t top_k, const int32_t *lora_ids,
+                         int32_t num_experts, int32_t num_loras, int32_t rank, int32_t inter,
+                         float scale, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Segments with at least this many rows take the MFMA path, shorter ones the
+ * vector-ALU path (default 16; the environment variable LORA_MFMA_MIN_ROWS,
+ * read at the first call, overrides the default).  The setter is the one
+ * piece of process-wide state: it takes effect for calls enqueued after it
+ * returns; values below 1 are clamped to 1.  Both paths compute the same
+ * result to within the tolerance of the fp32 accumulation. */
+int32_t lora_mfma_min_rows(void);
+void lora_set_mfma_min_rows(int32_t rows);
+
+/* A static, human-readable name for a status code. */
+const char *lora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TENANT_LORA_H */

@@ -1,0 +1,291 @@
+// abi.cpp -- the library's C entry points (declared in include/lora.h):
+// host-side validation, workspace carving and kernel launches.  Nothing here
+// allocates, frees or synchronizes; every check runs before any launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+
+#include "../../include/lora.h"
+#include "kernels.h"
+
+namespace {
+
+using tl::kMaxRank;
+using tl::kMaxSlices;
+
+constexpr int kMaxRows = 1 << 22;
+constexpr int kMaxSlots = 1 << 20;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+std::atomic<int> g_mfma_min{-1};
+
+int mfma_min_rows() {
+    int v = g_mfma_min.load(std::memory_order_relaxed);
+    if (v < 0) {
+        int d = 16;
+        if (const char *e = std::getenv("LORA_MFMA_MIN_ROWS")) {
+            const int x = std::atoi(e);
+            if (x > 0) d = x;
+        }
+        int expected = -1;
+        g_mfma_min.compare_exchange_strong(expected, d);
+        v = g_mfma_min.load(std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int tile_bound(int n, int S) {
+    if (n <= 0) return 0;
+    const long long a = (n + LORA_TILE_ROWS - 1) / LORA_TILE_ROWS + (long long)(n < S ? n : S);
+    return (int)(a < n ? a : n);
+}
+
+size_t meta_ws_bytes(int n, int S) {
+    (void)S;
+    const int chunks = tl::meta_chunks(n);
+    if (chunks <= 1) return 0;
+    return 64 + (size_t)3 * chunks * 1024 * sizeof(int32_t);
+}
+
+tl::MetaWs carve_meta_ws(void *ws, int n) {
+    tl::MetaWs w{};
+    if (tl::meta_chunks(n) <= 1) return w;
+    char *b = static_cast<char *>(ws);
+    const size_t per = (size_t)tl::meta_chunks(n) * 1024;
+    w.ctl = reinterpret_cast<int32_t *>(b);
+    w.rows = reinterpret_cast<int32_t *>(b + 64);
+    w.keys = w.rows + per;
+    w.offlen = w.keys + per;
+    return w;
+}
+
+bool meta_ok(const lora_meta_t &m) {
+    return m.sorted_rows && m.seg_offsets && m.seg_slot && m.counts && m.tiles;
+}
+
+int check_meta_shape(int n, int S) {
+    if (n < 0 || n > kMaxRows || S < 1 || S > kMaxSlots) return LORA_EINVAL;
+    if (tl::meta_chunks(n) > 1 && S > tl::kMetaMaxSlotsMulti) return LORA_EUNSUPPORTED;
+    return LORA_OK;
+}
+
+int check_rank(int R) { return (R >= 8 && R <= kMaxRank && R % 8 == 0) ? LORA_OK : LORA_EUNSUPPORTED; }
+
+// Validates the fields shared by shrink / expand / fused and fills `d`.
+int dense_shape(tl::DenseShape &d, int32_t n, int32_t k_in, int32_t num_slots, int32_t num_slices,
+                const int32_t *slice_sizes, int32_t max_rank) {
+    if (n < 0 || n > kMaxRows || num_slots < 1 || num_slots > kMaxSlots) return LORA_EINVAL;
+    if (num_slices < 1 || num_slices > kMaxSlices) return LORA_EINVAL;
+    if (int rc = check_rank(max_rank)) return rc;
+    d.n = n;
+    d.k_in = k_in;
+    d.num_slots = num_slots;
+    d.num_slices = num_slices;
+    d.R = max_rank;
+    d.slice_off[0] = 0;
+    for (int l = 0; l < num_slices; ++l) {
+        const int w = slice_sizes ? slice_sizes[l] : -1;
+        if (w <= 0 || w % 8 != 0) return LORA_EINVAL;
+        if ((long long)d.slice_off[l] + w > (1 << 28)) return LORA_EINVAL;
+        d.slice_off[l + 1] = d.slice_off[l] + w;
+    }
+    for (int l = num_slices + 1; l <= kMaxSlices; ++l) d.slice_off[l] = d.slice_off[num_slices];
+    return LORA_OK;
+}
+
+int check_x(const uint16_t *x, int64_t ldx, int32_t k_in) {
+    if (!x || !aligned16(x)) return LORA_EINVAL;
+    if (k_in < 8 || k_in % 8 != 0 || k_in > (1 << 20)) return LORA_EINVAL;
+    if (ldx < k_in || ldx % 8 != 0) return LORA_EINVAL;
+    return LORA_OK;
+}
+
+int check_y(const uint16_t *y, int64_t ldy, int32_t offset_start, int n_out) {
+    if (!y || !aligned16(y)) return LORA_EINVAL;
+    if (offset_start < 0 || offset_start % 8 != 0) return LORA_EINVAL;
+    if (ldy % 8 != 0 || ldy < (int64_t)offset_start + n_out) return LORA_EINVAL;
+    return LORA_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_meta_max_tiles(int32_t n, int32_t num_slots) { return tile_bound(n, num_slots); }
+
+size_t lora_meta_workspace_bytes(int32_t n, int32_t num_slots) {
+    if (check_meta_shape(n, num_slots) != LORA_OK) return 0;
+    return meta_ws_bytes(n, num_slots);
+}
+
+int lora_meta_build(const int32_t *slot, int32_t n, int32_t num_slots, lora_meta_t meta, void *ws,
+                    size_t ws_bytes, void *stream) {
+    if (int rc = check_meta_shape(n, num_slots)) return rc;
+    if (!meta_ok(meta) || (n > 0 && !slot)) return LORA_EINVAL;
+    const size_t need = meta_ws_bytes(n, num_slots);
+    if (need && (!ws || ws_bytes < need)) return LORA_EWORKSPACE;
+    tl::MetaOut out{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
+                    tile_bound(n, num_slots)};
+    return launched(tl::launch_meta_dense(slot, n, num_slots, out, carve_meta_ws(ws, n),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int lora_shrink(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
+                const float *scale, int32_t num_slots, int32_t num_slices, int32_t max_rank, lora_meta_t meta,
+                float *xa, void *stream) {
+    tl::DenseShape d{};
+    int32_t dummy[kMaxSlices];
+    for (int l = 0; l < kMaxSlices; ++l) dummy[l] = 8;
+    if (int rc = dense_shape(d, n, k_in, num_slots, num_slices, dummy, max_rank)) return rc;
+    if (int rc = check_x(x, ldx, k_in)) return rc;
+    if (!a_pool || !aligned16(a_pool) || !scale || !xa || !aligned16(xa) || !meta_ok(meta)) return LORA_EINVAL;
+    if (n == 0) return LORA_OK;
+    d.x = x;
+    d.ldx = ldx;
+    d.a_pool = a_pool;
+    d.scale = scale;
+    return launched(tl::launch_shrink(d, meta.tiles, tile_bound(n, num_slots), xa, mfma_min_rows(),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int lora_expand(const float *xa, const uint16_t *b_pool, int32_t num_slots, int32_t num_slices,
+                const int32_t *slice_sizes, int32_t max_rank, int32_t n, lora_meta_t meta, uint16_t *y,
+                int64_t ldy, int32_t offset_start, int32_t add_inputs, void *stream) {
+    tl::DenseShape d{};
+    if (int rc = dense_shape(d, n, 8, num_slots, num_slices, slice_sizes, max_rank)) return rc;
+    if (int rc = check_y(y, ldy, offset_start, d.slice_off[num_slices])) return rc;
+    if (!xa || !aligned16(xa) || !b_pool || !aligned16(b_pool) || !meta_ok(meta)) return LORA_EINVAL;
+    if (n == 0) return LORA_OK;
+    d.b_pool = b_pool;
+    d.y = y;
+    d.ldy = ldy;
+    d.offset_start = offset_start;
+    return launched(tl::launch_expand(d, xa, meta.tiles, tile_bound(n, num_slots), add_inputs, mfma_min_rows(),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_fused_workspace_bytes(int32_t n, int32_t num_slots, int32_t num_slices, int32_t max_rank,
+                                  int32_t k_in) {
+    if (n < 0 || n > kMaxRows || num_slots < 1 || num_slices < 1 || num_slices > kMaxSlices ||
+        check_rank(max_rank) != LORA_OK || k_in < 8)
+        return 0;
+    return tl::fused_plan(n, num_slots, num_slices, max_rank, k_in, 8).total_bytes;
+}
+
+int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
+                     const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
+                     const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
+                     int32_t offset_start, void *ws, size_t ws_bytes, void *stream) {
+    tl::DenseShape d{};
+    if (int rc = dense_shape(d, n, k_in, num_slots, num_slices, slice_sizes, max_rank)) return rc;
+    if (int rc = check_x(x, ldx, k_in)) return rc;
+    if (int rc = check_y(y, ldy, offset_start, d.slice_off[num_slices])) return rc;
+    if (!a_pool || !aligned16(a_pool) || !b_pool || !aligned16(b_pool) || !scale || !meta_ok(meta))
+        return LORA_EINVAL;
+    const tl::FusedPlan plan =
+        tl::fused_plan(n, num_slots, num_slices, max_rank, k_in, d.slice_off[num_slices]);
+    if (!ws || ws_bytes < plan.total_bytes || !aligned16(ws)) return LORA_EWORKSPACE;
+    if (n == 0) return LORA_OK;
+    d.x = x;
+    d.ldx = ldx;
+    d.a_pool = a_pool;
+    d.b_pool = b_pool;
+    d.scale = scale;
+    d.y = y;
+    d.ldy = ldy;
+    d.offset_start = offset_start;
+    return launched(
+        tl::launch_fused(d, meta.tiles, plan, ws, mfma_min_rows(), static_cast<hipStream_t>(stream)));
+}
+
+// MoE workspace: [counts 8 | sorted_rows n | seg_offsets cap+1 | seg_slot cap | tiles] [meta ws] [fused ws]
+namespace {
+struct MoeLayout {
+    size_t counts, sorted, segoff, segslot, tiles, meta_ws, fused, total;
+    tl::FusedPlan plan;
+};
+MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int H, int shared_a, int inter) {
+    MoeLayout m{};
+    const int n = T * top_k, S = L * E, cap = n < S ? n : S;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    size_t o = 0;
+    m.counts = o;
+    o = up(o + 8 * sizeof(int32_t));
+    m.sorted = o;
+    o = up(o + (size_t)n * sizeof(int32_t));
+    m.segoff = o;
+    o = up(o + (size_t)(cap + 1) * sizeof(int32_t));
+    m.segslot = o;
+    o = up(o + (size_t)(cap > 0 ? cap : 1) * sizeof(int32_t));
+    m.tiles = o;
+    o = up(o + (size_t)tile_bound(n, S) * LORA_TILE_WORDS * sizeof(int32_t));
+    m.meta_ws = o;
+    o = up(o + meta_ws_bytes(n, S));
+    m.plan = tl::fused_plan(n, S, shared_a ? 1 : 2, R, H, 2 * inter);
+    m.fused = o;
+    o = up(o + m.plan.total_bytes);
+    m.total = o;
+    return m;
+}
+}  // namespace
+
+size_t moe_lora_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras, int32_t rank,
+                                int32_t H) {
+    if (T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1 || check_rank(rank) != LORA_OK || H < 8)
+        return 0;
+    if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return 0;
+    // the regular form needs the larger partial buffer (two shrink slices)
+    return moe_layout(T, top_k, num_experts, num_loras, rank, H, 0, 8).total;
+}
+
+int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, const int64_t *w_ptr_a,
+                         int64_t lora_stride_a, const int64_t *w_ptr_b, int64_t lora_stride_b, int32_t shared_a,
+                         const int32_t *topk_ids, int32_t top_k, const int32_t *lora_ids, int32_t num_experts,
+                         int32_t num_loras, int32_t rank, int32_t inter, float scale, uint16_t *out, void *ws,
+                         size_t ws_bytes, void *stream) {
+    if (T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1) return LORA_EINVAL;
+    if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return LORA_EINVAL;
+    if (int rc = check_rank(rank)) return rc;
+    if (int rc = check_x(x, ldx, H)) return rc;
+    if (inter < 8 || inter % 8 != 0 || inter > (1 << 24)) return LORA_EINVAL;
+    if (lora_stride_a < 0 || lora_stride_b < 0 || lora_stride_a % 8 != 0 || lora_stride_b % 8 != 0)
+        return LORA_EINVAL;
+    if (!w_ptr_a || !w_ptr_b || !topk_ids || !lora_ids || !out || !aligned16(out)) return LORA_EINVAL;
+    const int n = T * top_k, S = num_experts * num_loras;
+    if (int rc = check_meta_shape(n, S)) return rc;
+    const MoeLayout lay = moe_layout(T, top_k, num_experts, num_loras, rank, H, shared_a, inter);
+    if (!ws || !aligned16(ws) || ws_bytes < lay.total) return LORA_EWORKSPACE;
+    char *b = static_cast<char *>(ws);
+    tl::MetaOut mo{reinterpret_cast<int32_t *>(b + lay.sorted), reinterpret_cast<int32_t *>(b + lay.segoff),
+                   reinterpret_cast<int32_t *>(b + lay.segslot), reinterpret_cast<int32_t *>(b + lay.counts),
+                   reinterpret_cast<int32_t *>(b + lay.tiles), tile_bound(n, S)};
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
+                                       carve_meta_ws(b + lay.meta_ws, n), st);
+    if (e != hipSuccess) return LORA_ELAUNCH;
+    if (n == 0) return LORA_OK;
+    tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
+                   lora_ids, num_experts, num_loras, rank, inter, scale, out};
+    return launched(tl::launch_moe_delta(m, mo.tiles, lay.plan, b + lay.fused, mfma_min_rows(), st));
+}
+
+int32_t lora_mfma_min_rows(void) { return mfma_min_rows(); }
+
+void lora_set_mfma_min_rows(int32_t rows) { g_mfma_min.store(rows < 1 ? 1 : rows, std::memory_order_relaxed); }
+
+const char *lora_status_string(int status) {
+    switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_EINVAL: return "invalid argument (pointer, size, alignment or leading dimension)";
+    case LORA_EUNSUPPORTED: return "unsupported shape";
+    case LORA_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case LORA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

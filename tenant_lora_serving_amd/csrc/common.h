@@ -1,0 +1,161 @@
+// common.h -- device helpers shared by the library's HIP kernels (gfx950 only).
+// Internal to the library; nothing here is visible through the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tl {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTileRows = 16;    // rows per tile record (the MFMA M dimension)
+constexpr int kTileWords = 32;   // int32 words per tile record
+// tile record fields
+constexpr int kRecSlot = 0, kRecPos = 1, kRecRows = 2, kRecSegRows = 3, kRecSeg = 4, kRecRowIds = 8;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------- bf16
+// bf16 is the top half of a binary32: widening is a shift (low element of a
+// packed pair) or a mask (high element).
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
+
+// acc + a.lo*b.lo + a.hi*b.hi over packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+__device__ __forceinline__ float dot8(const u32x4_t a, const u32x4_t b, float acc) {
+    acc = dot2(a.x, b.x, acc);
+    acc = dot2(a.y, b.y, acc);
+    acc = dot2(a.z, b.z, acc);
+    acc = dot2(a.w, b.w, acc);
+    return acc;
+}
+
+// ---------------------------------------------------------------- MFMA
+// D[16x16] += A[16x32] * B[32x16] in bf16 with fp32 accumulation.
+// Operand layout used throughout: lane l feeds row (A) / column (B) l % 16
+// with the 8 consecutive k values 8*(l/16) .. +8 of the 32-wide k block; the
+// same k assignment on both operands makes the product independent of how
+// the hardware orders k inside a lane group.  Result: lane l holds column
+// l % 16, rows 4*(l/16) + i for i = 0..3.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4_t ld16(const void *p) {
+    return *reinterpret_cast<const u32x4_t *>(p);
+}
+__device__ __forceinline__ void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
+// Streamed once: keep it out of the caches' way.
+__device__ __forceinline__ u32x4_t ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
+// ---------------------------------------------------------------- wave/block scans
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int t = __shfl_up(v, d, kWave);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = lane_id();
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+struct Int3 {
+    int a, b, c;
+};
+__device__ __forceinline__ Int3 operator+(Int3 x, Int3 y) { return {x.a + y.a, x.b + y.b, x.c + y.c}; }
+
+__device__ __forceinline__ Int3 wave_incl_scan3(Int3 v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        Int3 t = {__shfl_up(v.a, d, kWave), __shfl_up(v.b, d, kWave), __shfl_up(v.c, d, kWave)};
+        if (lane >= d) v = v + t;
+    }
+    return v;
+}
+
+// Exclusive scan over the NT threads of a block; every thread must call it.
+// `scratch` holds NT/64 + 1 entries.  Returns the exclusive prefix and the
+// block total.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *scratch, int &total) {
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), w = wave_id();
+    int inc = wave_incl_scan(v);
+    if (lane == kWave - 1) scratch[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        int s = lane < NW ? scratch[lane] : 0;
+        int si = wave_incl_scan(s);
+        if (lane < NW) scratch[lane] = si - s;
+        if (lane == NW - 1) scratch[NW] = si;
+    }
+    __syncthreads();
+    int r = scratch[w] + inc - v;
+    total = scratch[NW];
+    __syncthreads();
+    return r;
+}
+
+template <int NT>
+__device__ __forceinline__ Int3 block_excl_scan3(Int3 v, Int3 *scratch, Int3 &total) {
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), w = wave_id();
+    Int3 inc = wave_incl_scan3(v);
+    if (lane == kWave - 1) scratch[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        Int3 s = lane < NW ? scratch[lane] : Int3{0, 0, 0};
+        Int3 si = wave_incl_scan3(s);
+        if (lane < NW) scratch[lane] = Int3{si.a - s.a, si.b - s.b, si.c - s.c};
+        if (lane == NW - 1) scratch[NW] = si;
+    }
+    __syncthreads();
+    Int3 p = scratch[w];
+    Int3 r = {p.a + inc.a - v.a, p.b + inc.b - v.b, p.c + inc.c - v.c};
+    total = scratch[NW];
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------- device-scope sync
+__device__ __forceinline__ int atomic_add_release(int *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int atomic_add_acqrel(int *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_acquire(const int *p) {
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(int *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace tl

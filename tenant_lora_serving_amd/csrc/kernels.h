@@ -1,0 +1,89 @@
+// kernels.h -- host-side launch interface between the C ABI (abi.cpp) and the
+// HIP kernels (meta.hip, delta.hip).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tl {
+
+constexpr int kMaxSlices = 8;
+constexpr int kMaxRank = 128;
+constexpr int kMetaMaxSlotsMulti = 8192;  // slot limit when n spans several 1024-row chunks
+
+struct MetaOut {
+    int32_t *sorted_rows;
+    int32_t *seg_offsets;
+    int32_t *seg_slot;
+    int32_t *counts;
+    int32_t *tiles;
+    int tile_bound;
+};
+
+// Workspace of a multi-chunk meta build: ctl[0] ticket, ctl[1] invalid rows
+// (both zero between calls), then rows / keys / offset+length per chunk row.
+struct MetaWs {
+    int32_t *ctl;
+    int32_t *rows;
+    int32_t *keys;
+    int32_t *offlen;
+};
+
+int meta_chunks(int n);
+size_t meta_dyn_lds(int n, int S);
+hipError_t launch_meta_dense(const int32_t *slot, int n, int S, MetaOut out, MetaWs ws, hipStream_t st);
+hipError_t launch_meta_moe(const int32_t *topk, const int32_t *lora, int top_k, int E, int L, int n_pairs,
+                           MetaOut out, MetaWs ws, hipStream_t st);
+
+// Shapes of a dense call, validated by the caller.
+struct DenseShape {
+    const uint16_t *x;
+    int64_t ldx;
+    int n, k_in;
+    const uint16_t *a_pool;
+    const uint16_t *b_pool;
+    const float *scale;
+    int num_slots, num_slices, R;
+    int slice_off[kMaxSlices + 1];  // prefix sums of the slice widths
+    uint16_t *y;
+    int64_t ldy;
+    int offset_start;
+};
+
+// Fused-call workspace layout (all sizes derived from the shape).
+struct FusedPlan {
+    int tile_bound;  // tile records the meta build wrote
+    int P;           // k pieces of the shrink
+    int C;           // 512-column chunks of the expand
+    size_t part_bytes, ctr_bytes, total_bytes;
+};
+FusedPlan fused_plan(int n, int num_slots, int num_slices, int R, int k_in, int n_out);
+
+hipError_t launch_shrink(const DenseShape &d, const int32_t *tiles, int tile_bound, float *xa, int mfma_min,
+                         hipStream_t st);
+hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *tiles, int tile_bound,
+                         int add_inputs, int mfma_min, hipStream_t st);
+hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const FusedPlan &plan, void *ws,
+                        int mfma_min, hipStream_t st);
+
+struct MoeShape {
+    const uint16_t *x;
+    int64_t ldx;
+    int T, H;
+    const int64_t *w_ptr_a;
+    int64_t lora_stride_a;
+    const int64_t *w_ptr_b;
+    int64_t lora_stride_b;
+    int shared_a;
+    const int32_t *topk_ids;
+    int top_k;
+    const int32_t *lora_ids;
+    int E, L, R, inter;
+    float scale;
+    uint16_t *out;
+};
+hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const FusedPlan &plan, void *ws,
+                            int mfma_min, hipStream_t st);
+
+}  // namespace tl

@@ -1,0 +1,281 @@
+// meta.hip -- per-step routing metadata: rows sorted by (slot, row), segment
+// offsets, the active-slot list and 16-row tile records.
+//
+// What is computed follows vLLM punica_base.py (PunicaWrapperBase: per-token
+// lora indices, -1 meaning no lora; prefill_metadata grouping the rows of one
+// adapter into segments with their start and length) and metrale's lora_delta
+// docs (apply_lora_bgmv: a negative slot gets no delta).  Rows are ordered by
+// (slot, row), which makes the result unique, so it is compared bit-exactly.
+//
+// Design (gfx950): one 1024-thread workgroup per chunk of 1024 rows.
+//  1. Each chunk is sorted by slot in LDS with a stable 4-bit radix sort
+//     (per-wave 64-bit ballots give each lane its rank among equal digits;
+//     a 16 x 16 digit-by-wave histogram is scanned for the bucket starts).
+//     Inactive and invalid rows get the key S and sort to the end.
+//  2. Runs of one slot in the sorted chunk are found with a block scan.
+//  3. One chunk: the workgroup writes every output directly.
+//     Several chunks: each writes its sorted chunk to the workspace, then the
+//     last workgroup to finish (atomic ticket, release/acquire at agent
+//     scope) counts rows per slot in LDS, scans the counts, and scatters all
+//     chunks in order, so rows keep ascending order within a slot.
+// No step waits on another workgroup, so nothing can hang.
+#include "common.h"
+#include "kernels.h"
+
+namespace tl {
+
+constexpr int kMT = 1024;  // threads per workgroup = rows per chunk
+
+struct SlotSrcDense {
+    const int32_t *slot;
+    __device__ int32_t key(int i) const { return slot[i]; }
+};
+
+// MoE pair p = t*top_k + j: adapter l = lora_ids[t], expert e = topk_ids[p].
+// key = l*E + e; -1 when l < 0; L*E (invalid) when l >= L or e outside [0, E).
+struct SlotSrcMoe {
+    const int32_t *topk;
+    const int32_t *lora;
+    int top_k, E, L;
+    __device__ int32_t key(int p) const {
+        const int l = lora[p / top_k];
+        const int e = topk[p];
+        if (l < 0) return -1;
+        if (l >= L || e < 0 || e >= E) return L * E;
+        return l * E + e;
+    }
+};
+
+struct MetaShared {
+    uint32_t key[kMT];
+    int32_t val[kMT];
+    int32_t hist[256];
+    int32_t run_start[kMT];
+    int32_t run_tile[kMT];
+    int32_t scan[kMT / kWave + 1];
+    Int3 scan3[kMT / kWave + 1];
+    int flag_last;
+};
+
+// One stable pass of the LDS radix sort on digit (key >> shift) & 15.
+__device__ __forceinline__ void radix_pass(uint32_t &key, int32_t &val, int shift, MetaShared &sh) {
+    const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+    const uint32_t d = (key >> shift) & 15u;
+    const uint64_t lt = lanemask_lt();
+    uint64_t mine = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const uint64_t m = __ballot(d == (uint32_t)b);
+        if (d == (uint32_t)b) mine = m;
+        if (lane == b) sh.hist[b * 16 + w] = __popcll(m);
+    }
+    const int rank = __popcll(mine & lt);
+    __syncthreads();
+    int tot;
+    const int hv = tid < 256 ? sh.hist[tid] : 0;
+    const int hx = block_excl_scan<kMT>(hv, sh.scan, tot);
+    if (tid < 256) sh.hist[tid] = hx;
+    __syncthreads();
+    const int pos = sh.hist[d * 16 + w] + rank;
+    sh.key[pos] = key;
+    sh.val[pos] = val;
+    __syncthreads();
+    key = sh.key[tid];
+    val = sh.val[tid];
+    __syncthreads();
+}
+
+__device__ __forceinline__ void write_tile_header(int32_t *rec, int slot, int pos, int rows, int seg_rows,
+                                                  int seg) {
+    rec[kRecSlot] = slot;
+    rec[kRecPos] = pos;
+    rec[kRecRows] = rows;
+    rec[kRecSegRows] = seg_rows;
+    rec[kRecSeg] = seg;
+    rec[5] = 0;
+    rec[6] = 0;
+    rec[7] = 0;
+}
+
+template <class Src>
+__global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_chunks, MetaOut out,
+                                                   MetaWs ws) {
+    __shared__ MetaShared sh;
+    extern __shared__ int dyn[];
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x;
+    const int e = c * kMT + tid;
+    const bool real = e < n;
+    const int raw = real ? src.key(e) : -1;
+    const bool invalid = real && raw >= S;
+    uint32_t key = (real && raw >= 0 && raw < S) ? (uint32_t)raw : (uint32_t)S;
+    int32_t val = e;
+
+    const int nbits = 32 - __clz(S);  // bits holding 0..S
+    for (int shift = 0; shift < nbits; shift += 4) radix_pass(key, val, shift, sh);
+
+    // runs of equal keys in the sorted chunk
+    const uint32_t prev = tid > 0 ? sh.key[tid - 1] : 0xFFFFFFFFu;
+    const int leader = key != prev;
+    int n_runs;
+    const int run_id = block_excl_scan<kMT>(leader, sh.scan, n_runs) + leader - 1;
+    if (leader) sh.run_start[run_id] = tid;
+    __syncthreads();
+    const int rstart = sh.run_start[run_id];
+    const int rend = run_id + 1 < n_runs ? sh.run_start[run_id + 1] : kMT;
+    const int off = tid - rstart, len = rend - rstart;
+    const bool act = key < (uint32_t)S;
+    const int n_inv_chunk = __syncthreads_count(invalid);
+
+    if (n_chunks == 1) {
+        const int seg_lead = leader && act;
+        const int n_active = __syncthreads_count(act);
+        const int n_long = __syncthreads_count(seg_lead && len >= kTileRows);
+        int n_tiles;
+        const int tile_x =
+            block_excl_scan<kMT>(seg_lead ? (len + kTileRows - 1) / kTileRows : 0, sh.scan, n_tiles);
+        if (seg_lead) sh.run_tile[run_id] = tile_x;
+        const int n_seg = __syncthreads_count(seg_lead);
+        if (act) {
+            out.sorted_rows[tid] = val;
+            if (leader) {
+                out.seg_offsets[run_id] = tid;
+                out.seg_slot[run_id] = (int)key;
+            }
+            const int t = sh.run_tile[run_id] + off / kTileRows, j = off % kTileRows;
+            int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+            rec[kRecRowIds + j] = val;
+            if (j == 0) write_tile_header(rec, (int)key, tid, min(kTileRows, len - off), len, run_id);
+        }
+        if (tid == 0) {
+            out.seg_offsets[n_seg] = n_active;
+            out.counts[0] = n_active;
+            out.counts[1] = n_seg;
+            out.counts[2] = n_inv_chunk;
+            out.counts[3] = n_long;
+            out.counts[4] = n_tiles;
+            out.counts[5] = out.counts[6] = out.counts[7] = 0;
+        }
+        for (int t = n_tiles + tid; t < out.tile_bound; t += kMT)
+            write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0);
+        return;
+    }
+
+    // ---- several chunks: publish this chunk, the last workgroup assembles
+    {
+        const int64_t idx = (int64_t)c * kMT + tid;
+        ws.rows[idx] = val;
+        ws.keys[idx] = (int)key;
+        ws.offlen[idx] = off | (len << 16);
+    }
+    if (tid == 0 && n_inv_chunk) atomicAdd(&ws.ctl[1], n_inv_chunk);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sh.flag_last = atomic_add_acqrel(&ws.ctl[0], 1) == n_chunks - 1;
+    __syncthreads();
+    if (!sh.flag_last) return;
+    __threadfence();
+
+    int *start = dyn, *segidx = dyn + S, *tileoff = dyn + 2 * S, *rc = dyn + 3 * S;
+    for (int s = tid; s < S; s += kMT) rc[s] = 0;
+    __syncthreads();
+    // rows per slot (integer atomics: order does not matter)
+    for (int cc = 0; cc < n_chunks; ++cc) {
+        const int64_t idx = (int64_t)cc * kMT + tid;
+        const uint32_t k2 = (uint32_t)ws.keys[idx];
+        const int ol = ws.offlen[idx];
+        if (k2 < (uint32_t)S && (ol & 0xffff) == 0) atomicAdd(&rc[k2], ol >> 16);
+    }
+    __syncthreads();
+    // scan {rows, segments, tiles} over slots, each thread a contiguous block
+    const int per = (S + kMT - 1) / kMT;
+    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+    Int3 loc = {0, 0, 0};
+    int lng = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int v = rc[s];
+        loc = loc + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
+        lng += v >= kTileRows;
+    }
+    Int3 tot;
+    Int3 run = block_excl_scan3<kMT>(loc, sh.scan3, tot);
+    int n_long;
+    block_excl_scan<kMT>(lng, sh.scan, n_long);
+    for (int s = s0; s < s1; ++s) {
+        const int v = rc[s];
+        start[s] = run.a;
+        segidx[s] = run.b;
+        tileoff[s] = run.c;
+        if (v > 0) {
+            out.seg_offsets[run.b] = run.a;
+            out.seg_slot[run.b] = s;
+        }
+        run = run + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
+        rc[s] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        out.seg_offsets[tot.b] = tot.a;
+        out.counts[0] = tot.a;
+        out.counts[1] = tot.b;
+        out.counts[2] = __hip_atomic_load(&ws.ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        out.counts[3] = n_long;
+        out.counts[4] = tot.c;
+        out.counts[5] = out.counts[6] = out.counts[7] = 0;
+    }
+    // scatter the chunks in order; rc[s] counts the rows of slot s already placed
+    for (int cc = 0; cc < n_chunks; ++cc) {
+        const int64_t idx = (int64_t)cc * kMT + tid;
+        const uint32_t k2 = (uint32_t)ws.keys[idx];
+        const int ol = ws.offlen[idx];
+        const int off2 = ol & 0xffff, len2 = ol >> 16;
+        const bool a2 = k2 < (uint32_t)S;
+        if (a2) {
+            const int row = ws.rows[idx];
+            const int o = rc[k2] + off2;
+            const int dest = start[k2] + o;
+            const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
+            out.sorted_rows[dest] = row;
+            const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
+            int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+            rec[kRecRowIds + j] = row;
+            if (j == 0)
+                write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2]);
+        }
+        __syncthreads();
+        if (a2 && off2 == 0) rc[k2] += len2;
+        __syncthreads();
+    }
+    for (int t = tot.c + tid; t < out.tile_bound; t += kMT)
+        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0);
+    if (tid == 0) {
+        store_relaxed(&ws.ctl[0], 0);
+        store_relaxed(&ws.ctl[1], 0);
+    }
+}
+
+int meta_chunks(int n) { return n <= 0 ? 1 : (n + kMT - 1) / kMT; }
+
+size_t meta_dyn_lds(int n, int S) { return meta_chunks(n) > 1 ? (size_t)4 * S * sizeof(int) : 0; }
+
+template <class Src>
+static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hipStream_t st) {
+    const int chunks = meta_chunks(n);
+    const size_t dyn = meta_dyn_lds(n, S);
+    if (dyn > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_kernel<Src>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), dyn, st, src, n, S, chunks, out, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_meta_dense(const int32_t *slot, int n, int S, MetaOut out, MetaWs ws, hipStream_t st) {
+    return launch_meta(SlotSrcDense{slot}, n, S, out, ws, st);
+}
+
+hipError_t launch_meta_moe(const int32_t *topk, const int32_t *lora, int top_k, int E, int L, int n_pairs,
+                           MetaOut out, MetaWs ws, hipStream_t st) {
+    return launch_meta(SlotSrcMoe{topk, lora, top_k, E, L}, n_pairs, L * E, out, ws, st);
+}
+
+}  // namespace tl

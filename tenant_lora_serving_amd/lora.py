@@ -1,0 +1,286 @@
+"""Python binding of liblora.so (the C ABI in include/lora.h).
+
+Argument marshalling only: every function checks dtypes, devices and
+contiguity, passes raw device pointers, sizes and the current HIP stream to
+the library, and raises LoraError on a non-zero status.  Every step of the
+path runs in the library's kernels; there is no fallback.  torch provides the
+device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblora.so")
+
+TILE_ROWS = 16
+TILE_WORDS = 32
+
+_c_i32, _c_i64, _c_sz, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_float)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class _MetaStruct(ctypes.Structure):
+    _fields_ = [("sorted_rows", _c_p), ("seg_offsets", _c_p), ("seg_slot", _c_p),
+                ("counts", _c_p), ("tiles", _c_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load liblora.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tenant_lora_serving_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.lora_meta_max_tiles.restype = _c_i32
+        L.lora_meta_max_tiles.argtypes = [_c_i32, _c_i32]
+        L.lora_meta_workspace_bytes.restype = _c_sz
+        L.lora_meta_workspace_bytes.argtypes = [_c_i32, _c_i32]
+        L.lora_meta_build.restype = ctypes.c_int
+        L.lora_meta_build.argtypes = [_c_p, _c_i32, _c_i32, _MetaStruct, _c_p, _c_sz, _c_p]
+        L.lora_shrink.restype = ctypes.c_int
+        L.lora_shrink.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                  _MetaStruct, _c_p, _c_p]
+        L.lora_expand.restype = ctypes.c_int
+        L.lora_expand.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_p, _c_i32, _c_i32, _MetaStruct,
+                                  _c_p, _c_i64, _c_i32, _c_i32, _c_p]
+        L.lora_fused_workspace_bytes.restype = _c_sz
+        L.lora_fused_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]
+        L.lora_delta_fused.restype = ctypes.c_int
+        L.lora_delta_fused.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                       _c_p, _c_i32, _MetaStruct, _c_p, _c_i64, _c_i32, _c_p, _c_sz,
+                                       _c_p]
+        L.moe_lora_workspace_bytes.restype = _c_sz
+        L.moe_lora_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]
+        L.moe_lora_gemm1_delta.restype = ctypes.c_int
+        L.moe_lora_gemm1_delta.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64,
+                                           _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_f, _c_p, _c_p, _c_sz, _c_p]
+        L.lora_mfma_min_rows.restype = _c_i32
+        L.lora_mfma_min_rows.argtypes = []
+        L.lora_set_mfma_min_rows.restype = None
+        L.lora_set_mfma_min_rows.argtypes = [_c_i32]
+        L.lora_status_string.restype = ctypes.c_char_p
+        L.lora_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build", "lora_shrink",
+            "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused",
+            "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "lora_mfma_min_rows",
+            "lora_set_mfma_min_rows", "lora_status_string"]
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise LoraError(fn, status, lib().lora_status_string(status).decode())
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, contiguous=True):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _rows_ld(t: torch.Tensor, name: str):
+    """Row-major 2-D bf16 with unit column stride: returns (ptr, leading dim)."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return _dev(t, name, torch.bfloat16, contiguous=False), t.stride(0)
+
+
+def set_mfma_min_rows(rows: int):
+    lib().lora_set_mfma_min_rows(int(rows))
+
+
+def mfma_min_rows() -> int:
+    return int(lib().lora_mfma_min_rows())
+
+
+# ---------------------------------------------------------------- metadata
+@dataclass
+class LoraMeta:
+    """Device buffers of one batch's routing metadata (lora_meta_t) and the
+    workspace of its build."""
+    n: int
+    num_slots: int
+    sorted_rows: torch.Tensor
+    seg_offsets: torch.Tensor
+    seg_slot: torch.Tensor
+    counts: torch.Tensor
+    tiles: torch.Tensor
+    ws: torch.Tensor
+
+    @classmethod
+    def allocate(cls, n: int, num_slots: int, device="cuda"):
+        L = lib()
+        cap = min(n, num_slots)
+        tb = int(L.lora_meta_max_tiles(n, num_slots))
+        wsb = int(L.lora_meta_workspace_bytes(n, num_slots))
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(n, num_slots,
+                   torch.empty(max(n, 1), **i32), torch.empty(cap + 1, **i32),
+                   torch.empty(max(cap, 1), **i32), torch.zeros(8, **i32),
+                   torch.empty(max(tb, 1) * TILE_WORDS, **i32),
+                   torch.zeros(max(wsb, 16), dtype=torch.uint8, device=device))
+
+    def struct(self) -> _MetaStruct:
+        return _MetaStruct(self.sorted_rows.data_ptr(), self.seg_offsets.data_ptr(),
+                           self.seg_slot.data_ptr(), self.counts.data_ptr(), self.tiles.data_ptr())
+
+
+def lora_meta_build(slot: torch.Tensor, num_slots: int, meta: LoraMeta | None = None,
+                    stream=None) -> LoraMeta:
+    n = slot.numel()
+    if meta is None:
+        meta = LoraMeta.allocate(n, num_slots, slot.device)
+    assert meta.n == n and meta.num_slots == num_slots, "metadata buffers sized for another batch"
+    p = _dev(slot, "slot", torch.int32)
+    st = lib().lora_meta_build(p, n, num_slots, meta.struct(), meta.ws.data_ptr(), meta.ws.numel(),
+                               _stream(stream))
+    _check("lora_meta_build", st)
+    return meta
+
+
+# ---------------------------------------------------------------- dense delta
+def _pool_dims(a_pool=None, b_pool=None):
+    if a_pool is not None:
+        if a_pool.dim() != 4:
+            raise ValueError("a_pool must be [num_slots, num_slices, max_rank, k_in]")
+    if b_pool is not None and b_pool.dim() != 3:
+        raise ValueError("b_pool must be [num_slots, N, max_rank]")
+
+
+def lora_shrink(x: torch.Tensor, a_pool: torch.Tensor, scale: torch.Tensor, meta: LoraMeta,
+                xa: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """xa[l, i, :] = scale[s] * A_s[l] @ x[i] for active rows (others untouched)."""
+    _pool_dims(a_pool=a_pool)
+    S, Lsl, R, k_in = a_pool.shape
+    xp, ldx = _rows_ld(x, "x")
+    n = x.shape[0]
+    if x.shape[1] < k_in:
+        raise ValueError("x has fewer columns than k_in")
+    if xa is None:
+        xa = torch.zeros((Lsl, n, R), dtype=torch.float32, device=x.device)
+    st = lib().lora_shrink(xp, ldx, n, k_in, _dev(a_pool, "a_pool", torch.bfloat16),
+                           _dev(scale, "scale", torch.float32), S, Lsl, R, meta.struct(),
+                           _dev(xa, "xa", torch.float32), _stream(stream))
+    _check("lora_shrink", st)
+    return xa
+
+
+def lora_expand(xa: torch.Tensor, b_pool: torch.Tensor, slice_sizes, meta: LoraMeta,
+                y: torch.Tensor, offset_start: int = 0, add_inputs: bool = True,
+                stream=None) -> torch.Tensor:
+    """y[i, window] (+)= xa[l, i] @ B_s[slice]^T for active rows, in place."""
+    _pool_dims(b_pool=b_pool)
+    S, N, R = b_pool.shape
+    ss = (ctypes.c_int32 * len(slice_sizes))(*[int(v) for v in slice_sizes])
+    if sum(slice_sizes) != N:
+        raise ValueError("slice sizes must add up to b_pool's N")
+    yp, ldy = _rows_ld(y, "y")
+    st = lib().lora_expand(_dev(xa, "xa", torch.float32), _dev(b_pool, "b_pool", torch.bfloat16), S,
+                           len(slice_sizes), ss, R, y.shape[0], meta.struct(), yp, ldy,
+                           int(offset_start), 1 if add_inputs else 0, _stream(stream))
+    _check("lora_expand", st)
+    return y
+
+
+def fused_workspace(n: int, num_slots: int, num_slices: int, max_rank: int, k_in: int,
+                    device="cuda") -> torch.Tensor:
+    b = int(lib().lora_fused_workspace_bytes(n, num_slots, num_slices, max_rank, k_in))
+    return torch.zeros(max(b, 16), dtype=torch.uint8, device=device)
+
+
+def lora_delta_fused(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor,
+                     scale: torch.Tensor, slice_sizes, meta: LoraMeta, y: torch.Tensor,
+                     offset_start: int = 0, ws: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """y[i, window] += (scale[s] * x[i] @ A_s^T) @ B_s^T for active rows, in place."""
+    _pool_dims(a_pool, b_pool)
+    S, Lsl, R, k_in = a_pool.shape
+    if len(slice_sizes) != Lsl or sum(slice_sizes) != b_pool.shape[1]:
+        raise ValueError("slice sizes do not match the pools")
+    xp, ldx = _rows_ld(x, "x")
+    yp, ldy = _rows_ld(y, "y")
+    n = x.shape[0]
+    if y.shape[0] != n:
+        raise ValueError("x and y row counts differ")
+    if ws is None:
+        ws = fused_workspace(n, S, Lsl, R, k_in, x.device)
+    ss = (ctypes.c_int32 * Lsl)(*[int(v) for v in slice_sizes])
+    st = lib().lora_delta_fused(xp, ldx, n, k_in, _dev(a_pool, "a_pool", torch.bfloat16),
+                                _dev(b_pool, "b_pool", torch.bfloat16),
+                                _dev(scale, "scale", torch.float32), S, Lsl, ss, R, meta.struct(),
+                                yp, ldy, int(offset_start), _dev(ws, "ws", torch.uint8),
+                                ws.numel(), _stream(stream))
+    _check("lora_delta_fused", st)
+    return y
+
+
+# ---------------------------------------------------------------- MoE
+def moe_workspace(T: int, top_k: int, num_experts: int, num_loras: int, rank: int, H: int,
+                  device="cuda") -> torch.Tensor:
+    b = int(lib().moe_lora_workspace_bytes(T, top_k, num_experts, num_loras, rank, H))
+    return torch.zeros(max(b, 16), dtype=torch.uint8, device=device)
+
+
+def moe_lora_gemm1_delta(hidden_states: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: int,
+                         w_ptr_b: torch.Tensor, lora_stride_b: int, topk_ids: torch.Tensor,
+                         lora_ids: torch.Tensor, rank: int, intermediate_size: int, *,
+                         num_loras: int, scale: float = 1.0, out: torch.Tensor | None = None,
+                         ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """[T, top_k, 2I] gate/up delta per routed pair.  A 2-D [2, E] pointer
+    table selects the regular form, a 1-D [E] table the shared-A form."""
+    shared = w_ptr_a.dim() == 1
+    if (w_ptr_b.dim() == 1) != shared:
+        raise ValueError("w_ptr_a and w_ptr_b must both be 1-D or both be [2, E]")
+    E = w_ptr_a.shape[-1]
+    if not shared and w_ptr_a.shape[0] != 2:
+        raise ValueError("regular pointer tables are [2, num_experts]")
+    T, H = hidden_states.shape
+    top_k = topk_ids.shape[1]
+    xp, ldx = _rows_ld(hidden_states, "hidden_states")
+    if out is None:
+        out = torch.empty((T, top_k, 2 * intermediate_size), dtype=torch.bfloat16,
+                          device=hidden_states.device)
+    if ws is None:
+        ws = moe_workspace(T, top_k, E, num_loras, rank, H, hidden_states.device)
+    st = lib().moe_lora_gemm1_delta(
+        xp, ldx, T, H, _dev(w_ptr_a, "w_ptr_a", torch.int64), int(lora_stride_a),
+        _dev(w_ptr_b, "w_ptr_b", torch.int64), int(lora_stride_b), 1 if shared else 0,
+        _dev(topk_ids, "topk_ids", torch.int32), top_k, _dev(lora_ids, "lora_ids", torch.int32),
+        E, int(num_loras), int(rank), int(intermediate_size), float(scale),
+        _dev(out, "out", torch.bfloat16), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    _check("moe_lora_gemm1_delta", st)
+    return out
+
+
+def moe_counts(ws: torch.Tensor) -> torch.Tensor:
+    """{n_active_pairs, n_segments, n_invalid_pairs, n_long_segments} of the last MoE call."""
+    return ws[:16].view(torch.int32)

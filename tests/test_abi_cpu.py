@@ -1,0 +1,134 @@
+"""CPU-only checks of the C ABI: the built library loads, exports every
+function include/lora.h declares, and rejects bad arguments on the host with
+the documented status codes before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tenant_lora_serving_amd import lora as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "sizeof", "defined"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("liblora.so is not built (python -m tenant_lora_serving_amd.build)")
+    return B.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    fns = declared_functions()
+    for f in ["lora_meta_build", "lora_shrink", "lora_expand", "lora_delta_fused",
+              "moe_lora_gemm1_delta"]:
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(B.LIB_PATH)
+    missing = [f for f in declared_functions() if not hasattr(raw, f)]
+    assert not missing, missing
+    assert sorted(B.EXPORTED) == declared_functions()
+
+
+def test_tile_bound_and_workspace_sizes(L):
+    assert L.lora_meta_max_tiles(0, 4) == 0
+    assert L.lora_meta_max_tiles(8, 4) == 5          # ceil(8/16) + min(8, 4)
+    assert L.lora_meta_max_tiles(256, 32) == 48
+    assert L.lora_meta_max_tiles(1024, 1024) == 1024  # capped at n
+    assert L.lora_meta_workspace_bytes(1024, 8) == 0  # one chunk needs none
+    assert L.lora_meta_workspace_bytes(1025, 8) > 0
+    assert L.lora_meta_workspace_bytes(5000, 9000) == 0  # unsupported -> 0
+    assert L.lora_fused_workspace_bytes(256, 32, 3, 16, 4096) > 0
+    assert L.lora_fused_workspace_bytes(256, 32, 3, 12, 4096) == 0  # rank not a multiple of 8
+    assert L.moe_lora_workspace_bytes(2048, 8, 64, 8, 16, 4096) > 0
+
+
+def _meta(ptr=0x10000):
+    return B._MetaStruct(ptr, ptr, ptr, ptr, ptr)
+
+
+def test_meta_build_validation(L):
+    m = _meta()
+    assert L.lora_meta_build(0x1000, -1, 4, m, None, 0, None) == EINVAL
+    assert L.lora_meta_build(0x1000, 8, 0, m, None, 0, None) == EINVAL
+    assert L.lora_meta_build(None, 8, 4, m, None, 0, None) == EINVAL
+    assert L.lora_meta_build(0x1000, 8, 4, B._MetaStruct(0, 0, 0, 0, 0), None, 0, None) == EINVAL
+    # two chunks need a workspace
+    assert L.lora_meta_build(0x1000, 2000, 4, m, None, 0, None) == EWS
+    assert L.lora_meta_build(0x1000, 2000, 4, m, 0x2000, 16, None) == EWS
+    # several chunks support at most 8192 slots
+    assert L.lora_meta_build(0x1000, 2000, 9000, m, 0x2000, 1 << 30, None) == EUNSUP
+
+
+def test_shrink_validation(L):
+    m = _meta()
+    a = dict(x=0x1000, ldx=256, n=8, k_in=256, a=0x2000, sc=0x3000, S=4, L=1, R=8, xa=0x4000)
+
+    def call(**kw):
+        v = dict(a, **kw)
+        return L.lora_shrink(v["x"], v["ldx"], v["n"], v["k_in"], v["a"], v["sc"], v["S"], v["L"],
+                             v["R"], m, v["xa"], None)
+    assert call(k_in=260) == EINVAL          # not a multiple of 8
+    assert call(ldx=128) == EINVAL           # ldx < k_in
+    assert call(x=0x1008) == EINVAL          # x not 16-byte aligned
+    assert call(R=12) == EUNSUP
+    assert call(R=136) == EUNSUP
+    assert call(L=9) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(xa=None) == EINVAL
+    assert call(n=0) == OK                   # nothing to do, nothing launched
+
+
+def test_expand_and_fused_validation(L):
+    m = _meta()
+    ss = (ctypes.c_int32 * 2)(256, 128)
+    bad = (ctypes.c_int32 * 2)(256, 100)
+    assert L.lora_expand(0x1000, 0x2000, 4, 2, bad, 8, 8, m, 0x3000, 384, 0, 1, None) == EINVAL
+    assert L.lora_expand(0x1000, 0x2000, 4, 2, ss, 8, 8, m, 0x3000, 376, 0, 1, None) == EINVAL  # ldy < N
+    assert L.lora_expand(0x1000, 0x2000, 4, 2, ss, 8, 8, m, 0x3000, 392, 12, 1, None) == EINVAL
+    assert L.lora_expand(0x1000, 0x2000, 4, 2, ss, 8, 8, m, 0x3000, 392, 16, 1, None) == EINVAL
+    assert L.lora_expand(0x1000, 0x2000, 4, 2, ss, 8, 0, m, 0x3000, 384, 0, 1, None) == OK
+    ws_need = L.lora_fused_workspace_bytes(8, 4, 2, 8, 256)
+    args = [0x1000, 256, 8, 256, 0x2000, 0x3000, 0x4000, 4, 2, ss, 8, m, 0x5000, 384, 0]
+    assert L.lora_delta_fused(*args, 0x6000, ws_need - 1, None) == EWS
+    assert L.lora_delta_fused(*args, None, ws_need, None) == EWS
+    args0 = list(args)
+    args0[2] = 0
+    assert L.lora_delta_fused(*args0, 0x6000, 1 << 20, None) == OK
+
+
+def test_moe_validation(L):
+    base = dict(x=0x1000, ldx=4096, T=16, H=4096, wa=0x2000, lsa=16 * 4096, wb=0x3000, lsb=1408 * 16,
+                shared=0, topk=0x4000, top_k=8, lora=0x5000, E=64, L=8, R=16, I=1408, out=0x6000)
+    need = L.moe_lora_workspace_bytes(16, 8, 64, 8, 16, 4096)
+
+    def call(ws=0x7000, wsb=need, **kw):
+        v = dict(base, **kw)
+        return L.moe_lora_gemm1_delta(v["x"], v["ldx"], v["T"], v["H"], v["wa"], v["lsa"], v["wb"],
+                                      v["lsb"], v["shared"], v["topk"], v["top_k"], v["lora"], v["E"],
+                                      v["L"], v["R"], v["I"], 1.0, v["out"], ws, wsb, None)
+    assert call(I=1404) == EINVAL
+    assert call(R=20) == EUNSUP
+    assert call(H=4100) == EINVAL
+    assert call(lsa=7) == EINVAL
+    assert call(wa=None) == EINVAL
+    assert call(wsb=need - 1) == EWS
+    assert call(top_k=0) == EINVAL
+
+
+def test_status_strings(L):
+    for s in (OK, EINVAL, EUNSUP, EWS, -4, 99):
+        assert isinstance(L.lora_status_string(s), bytes)

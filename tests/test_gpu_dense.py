@@ -1,0 +1,212 @@
+"""GPU parity of lora_shrink, lora_expand and lora_delta_fused against the
+fp64 oracle, on both compute paths (vector ALU for short segments, MFMA for
+segments with at least `mfma_min_rows` rows), plus the bitwise invariants:
+rows without an active slot and columns outside the slice windows untouched,
+zero scale leaves y unchanged, run-to-run bitwise determinism."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tenant_lora_serving_amd import inputs as I
+from tenant_lora_serving_amd import lora as B
+from gpu_util import assert_close, bf64, d16, d32, h16
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"default": 16, "valu": 1 << 30, "mfma": 1}
+
+
+@pytest.fixture(params=list(PATHS))
+def path(request):
+    old = B.mfma_min_rows()
+    B.set_mfma_min_rows(PATHS[request.param])
+    yield request.param
+    B.set_mfma_min_rows(old)
+
+
+class Dev:
+    """Device copies of a DenseCase."""
+
+    def __init__(self, c: I.DenseCase, ldy_pad: int = 0, offset_start: int = 0):
+        self.c = c
+        self.x = d16(c.x)
+        self.a = d16(c.a_pool)
+        self.b = d16(c.b_pool)
+        self.scale = d32(c.scale)
+        self.slot = d32(c.slot)
+        self.offset_start = offset_start
+        ldy = offset_start + c.n_out + ldy_pad
+        if ldy == c.n_out:
+            yh = c.y.copy()
+        else:
+            # finite random filler outside the window, to catch stray writes
+            yh = np.empty((c.n, ldy), dtype=np.uint16)
+            yh[:] = I.f32_to_bf16_bits(
+                np.random.default_rng(99).standard_normal((c.n, ldy), dtype=np.float32) * 100)
+            yh[:, offset_start:offset_start + c.n_out] = c.y
+        self.y_host = yh
+        self.y = d16(yh)
+        self.meta = B.lora_meta_build(self.slot, c.num_slots)
+
+
+def active(c):
+    return (c.slot >= 0) & (c.slot < c.num_slots)
+
+
+def check_y(dv: Dev, y_gpu_bits: np.ndarray, rows: np.ndarray, what: str, add_inputs=True, xa=None):
+    c = dv.c
+    if xa is None:
+        orc = O.fused_rows(c.x, c.k_in, c.a_pool, c.b_pool, c.scale, c.num_slots, c.slice_sizes,
+                           c.max_rank, c.slot, rows, dv.y_host, dv.offset_start)
+    else:
+        orc = O.expand_rows(xa, c.b_pool, c.num_slots, c.slice_sizes, c.max_rank, c.slot, rows,
+                            dv.y_host, dv.offset_start, add_inputs)
+    gpu = bf64(y_gpu_bits[rows])
+    w0, w1 = dv.offset_start, dv.offset_start + c.n_out
+    worst = assert_close(gpu[:, w0:w1], orc[:, w0:w1], what)
+    # outside the window and on inactive rows: bitwise unchanged
+    assert np.array_equal(y_gpu_bits[rows][:, :w0], dv.y_host[rows][:, :w0])
+    assert np.array_equal(y_gpu_bits[rows][:, w1:], dv.y_host[rows][:, w1:])
+    off = ~active(c)[rows]
+    assert np.array_equal(y_gpu_bits[rows][off], dv.y_host[rows][off])
+    return worst
+
+
+def small_case(seed, n=70, k_in=264, slices=(40, 24, 64), S=6, R=16, zipf=False, neg=0.15):
+    rng = np.random.default_rng(seed)
+    if zipf:
+        p = 1.0 / np.arange(1, S + 1)
+        slot = rng.choice(S, size=n, p=p / p.sum())
+    else:
+        slot = rng.integers(0, S, size=n)
+    slot = np.where(rng.random(n) < neg, -1, slot)
+    slot = np.where(rng.random(n) < 0.03, S + 2, slot).astype(np.int32)   # a few invalid slots
+    return I.make_dense(seed, n=n, k_in=k_in, slice_sizes=slices, num_slots=S, max_rank=R,
+                        rank_choices=[R // 2, R], slot=slot, scale_num=2.0 * R)
+
+
+SMALL = [
+    dict(seed=1),
+    dict(seed=2, n=300, S=4, zipf=True),                          # long segments with ragged tails
+    dict(seed=3, n=45, k_in=8, slices=(8,), S=3, R=8),            # smallest shapes
+    dict(seed=4, n=257, k_in=1032, slices=(520, 16), S=40, R=24),  # R not a multiple of 16
+    dict(seed=5, n=33, k_in=512, slices=(1024,), S=2, R=128),     # largest rank
+    dict(seed=6, n=129, k_in=128, slices=(8, 8, 8, 8, 8, 8, 8, 8), S=5, R=8),   # 8 slices
+    dict(seed=7, n=1500, k_in=256, slices=(256,), S=7, R=16, zipf=True),       # several meta chunks
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=[f"s{k['seed']}" for k in SMALL])
+def test_fused_small(kw, path):
+    c = small_case(**kw)
+    print(f"fused small {kw} path={path}", flush=True)
+    dv = Dev(c, ldy_pad=16, offset_start=8)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y,
+                       offset_start=dv.offset_start)
+    torch.cuda.synchronize()
+    check_y(dv, h16(dv.y), np.arange(c.n), f"fused {kw} {path}")
+
+
+@pytest.mark.parametrize("kw", SMALL[:5], ids=[f"s{k['seed']}" for k in SMALL[:5]])
+def test_shrink_then_expand_small(kw, path):
+    c = small_case(**kw)
+    print(f"split small {kw} path={path}", flush=True)
+    dv = Dev(c, ldy_pad=8)
+    xa = torch.full((c.num_slices, c.n, c.max_rank), float("nan"), device="cuda")
+    B.lora_shrink(dv.x, dv.a, dv.scale, dv.meta, xa)
+    torch.cuda.synchronize()
+    xa_h = xa.cpu().numpy()
+    rows = np.arange(c.n)
+    orc = O.shrink_rows(c.x, c.k_in, c.a_pool, c.scale, c.num_slots, c.num_slices, c.max_rank,
+                        c.slot, rows)
+    act = active(c)
+    assert_close(np.transpose(xa_h, (1, 0, 2))[act], orc[act], f"shrink {kw} {path}")
+    assert np.isnan(np.transpose(xa_h, (1, 0, 2))[~act]).all()       # inactive rows untouched
+    # expand from the GPU's own xa (the oracle widens the same fp32 values)
+    xa_rows = np.nan_to_num(np.transpose(xa_h, (1, 0, 2)))
+    for add in (True, False):
+        y = d16(dv.y_host)
+        B.lora_expand(xa.nan_to_num(0.0), dv.b, c.slice_sizes, dv.meta, y, add_inputs=add)
+        torch.cuda.synchronize()
+        check_y(dv, h16(y), rows, f"expand add={add} {kw} {path}", add_inputs=add, xa=xa_rows)
+
+
+def test_fused_tiny_config(path):
+    c = I.tiny_bgmv()
+    dv = Dev(c)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    check_y(dv, h16(dv.y), np.arange(c.n), f"tiny {path}")
+
+
+@pytest.fixture(scope="module")
+def decode_case():
+    return I.decode_bgmv()
+
+
+def test_fused_decode_full(decode_case, path):
+    c = decode_case
+    print(f"decode full path={path}", flush=True)
+    dv = Dev(c)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    check_y(dv, h16(dv.y), np.arange(c.n), f"decode {path}")
+
+
+def test_fused_decode_deterministic_and_ws_clean(decode_case):
+    c = decode_case
+    outs = []
+    for _ in range(3):
+        dv = Dev(c)
+        ws = B.fused_workspace(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in)
+        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y, ws=ws)
+        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(h16(dv.y))
+        tb = B.lib().lora_meta_max_tiles(c.n, c.num_slots)
+        ctl = ws[: 64 + 8 * tb].view(torch.int32).cpu().numpy()
+        assert not ctl.any(), "fused workspace counters/flag not back to zero"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+def test_zero_scale_is_bitwise_noop(decode_case):
+    c = decode_case
+    dv = Dev(c)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale * 0, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    assert np.array_equal(h16(dv.y), dv.y_host)
+
+
+def test_shrink_expand_decode_full(decode_case):
+    c = decode_case
+    dv = Dev(c)
+    xa = torch.zeros((c.num_slices, c.n, c.max_rank), device="cuda")
+    B.lora_shrink(dv.x, dv.a, dv.scale, dv.meta, xa)
+    B.lora_expand(xa, dv.b, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    check_y(dv, h16(dv.y), np.arange(c.n), "decode split")
+
+
+def test_fused_no_reuse_full():
+    c = I.no_reuse()
+    print("no-reuse full", flush=True)
+    dv = Dev(c)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(c.n, size=96, replace=False)
+    check_y(dv, h16(dv.y), rows, "no-reuse")
+
+
+def test_fused_prefill_full():
+    c = I.prefill_sgmv()
+    print(f"prefill full n={c.n}", flush=True)
+    dv = Dev(c)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    y = h16(dv.y)
+    rng = np.random.default_rng(0)
+    # sampled rows: segment boundaries, tile tails and random rows
+    starts = np.concatenate([[0], np.cumsum(c.meta["seq_lens"])])
+    rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1, rng.choice(c.n, 40, replace=False)]))
+    check_y(dv, y, rows, "prefill")
