@@ -154,6 +154,9 @@ __device__ __forceinline__ int atomic_add_acqrel(int *p, int v) {
 __device__ __forceinline__ int load_acquire(const int *p) {
     return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int load_relaxed(const int *p) {
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void store_relaxed(int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -28,11 +28,18 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace tl {
 
 constexpr int kBT = 256;        // threads per compute workgroup
 constexpr int kCW = 512;        // expand columns per unit
-constexpr int kRRChunk = 256;   // shrink rank rows per pass
+constexpr int kRRMfma = 128;    // shrink rank rows per pass on the MFMA path
+constexpr int kRRValu = 64;     // shrink rank rows per pass on the vector ALU
+constexpr int kKC = 512;        // x columns staged in LDS per pass
+constexpr int kXS = kKC + 8;    // padded LDS row stride (elements) of the staged x tile
+constexpr int kXsBytes = kTileRows * kXS * 2;
+constexpr int kMaxPieces = 16;  // k pieces of the fused shrink
 constexpr int kRedStride = 48 * 16;  // per-wave partial block when waves split k
 constexpr int kOutStride = 132;      // padded fp32 row stride of the MFMA output tile
 constexpr int kSpinLimit = 1 << 24;
@@ -130,6 +137,7 @@ __device__ bool load_tile(const Op &op, const int32_t *tiles, int t, UnitHdr &h)
 }
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 
 // How the 4 waves share a unit: GW waves split the rank-row groups, KW = 4/GW
 // split the k range (their partials are summed in wave order).
@@ -138,41 +146,8 @@ __device__ __forceinline__ void wave_split(int groups, int &GW, int &KW) {
     KW = 4 / GW;
 }
 
-// ============================================================ shrink
-// res[rl*16 + j] = sum_{k in [k0,k1)} x[row_j][k] * A[slot][rr0 + rl][k], rl < n_rr.
-template <class Op>
-__device__ void shrink_mfma(const Op &op, const UnitHdr &h, int rr0, int n_rr, int k0, int k1, float *res,
-                            float *red) {
-    const int lane = lane_id(), w = wave_id();
-    const int groups = (n_rr + 15) >> 4;
-    int GW, KW;
-    wave_split(groups, GW, KW);
-    const int gw = w % GW, kw = w / GW;
-    const int per = ((k1 - k0 + KW * 32 - 1) / (KW * 32)) * 32;
-    const int ka = k0 + kw * per, kb = min(k1, ka + per);
-    const int col = lane & 15, kk = (lane >> 4) * 8;
-    const uint16_t *xr = h.xrow[col];  // MFMA-A row = tile row (null past m)
-    float *dst = KW == 1 ? res : red + kw * kRedStride;
-    for (int g = gw; g < groups; g += GW) {
-        const int rl = 16 * g + col;  // MFMA-B column = rank row
-        const uint16_t *ap = rl < n_rr ? op.arow(h.slot, rr0 + rl) : nullptr;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-
-        for (int k = ka; k < kb; k += 32) {
-            const int kx = k + kk;
-            const bool in = kx < kb;
-            const u32x4_t xo = (xr && in) ? ld16(xr + kx) : zero4();
-            const u32x4_t ao = (ap && in) ? ld16_stream(ap + kx) : zero4();
-            acc = mfma_16x16x32(xo, ao, acc);
-        }
-        if (rl < n_rr) {
-            const int j0 = (lane >> 4) * 4;
-            dst[rl * 16 + j0 + 0] = acc[0];
-            dst[rl * 16 + j0 + 1] = acc[1];
-            dst[rl * 16 + j0 + 2] = acc[2];
-            dst[rl * 16 + j0 + 3] = acc[3];
-        }
-    }
+// Sum the KW per-wave partial blocks of `red` into `res` in wave order.
+__device__ __forceinline__ void reduce_waves(int KW, int n_rr, float *res, const float *red) {
     __syncthreads();
     if (KW > 1) {
         for (int idx = threadIdx.x; idx < n_rr * 16; idx += kBT) {
@@ -184,60 +159,157 @@ __device__ void shrink_mfma(const Op &op, const UnitHdr &h, int rr0, int n_rr, i
     }
 }
 
+// ============================================================ shrink
+// Every unit reads its x rows through LDS in chunks of kKC columns (coalesced
+// 16-byte loads, all issued before any is used) and streams the adapter's
+// A rows straight from HBM into registers, eight 16-byte loads per lane in
+// flight before the first is consumed.
+//
+// Stage x rows j < 16 (zero rows past m), columns [kc0, kc1), into xs[j][.].
+__device__ __forceinline__ void stage_x(const UnitHdr &h, int kc0, int kc1, uint16_t *xs) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + kBT * i;
+        const int j = idx >> 6, k = kc0 + 8 * (idx & 63);
+        v[i] = (j < h.m && k < kc1) ? ld16(h.xrow[j] + k) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + kBT * i;
+        *reinterpret_cast<u32x4_t *>(xs + (idx >> 6) * kXS + 8 * (idx & 63)) = v[i];
+    }
+}
+
+// res[rl*16 + j] = sum_{k in [k0,k1)} x[row_j][k] * A[slot][rr0 + rl][k] for
+// rl < n_rr <= kRRMfma, on v_mfma_f32_16x16x32_bf16 (tile rows = MFMA rows,
+// rank rows = MFMA columns).
+template <class Op>
+__device__ void shrink_mfma(const Op &op, const UnitHdr &h, int rr0, int n_rr, int k0, int k1, float *res,
+                            float *red, uint16_t *xs) {
+    const int lane = lane_id(), w = wave_id();
+    const int groups = (n_rr + 15) >> 4;
+    int GW, KW;
+    wave_split(groups, GW, KW);
+    const int gw = w % GW, kw = w / GW;
+    const int col = lane & 15, kk = (lane >> 4) * 8;
+    const bool has0 = gw < groups, has1 = gw + GW < groups;
+    const int rl0 = 16 * gw + col, rl1 = 16 * (gw + GW) + col;
+    const uint16_t *ap0 = (has0 && rl0 < n_rr) ? op.arow(h.slot, rr0 + rl0) : nullptr;
+    const uint16_t *ap1 = (has1 && rl1 < n_rr) ? op.arow(h.slot, rr0 + rl1) : nullptr;
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int kc0 = k0; kc0 < k1; kc0 += kKC) {
+        const int kc1 = min(k1, kc0 + kKC);
+        __syncthreads();
+        stage_x(h, kc0, kc1, xs);
+        __syncthreads();
+        const int per = ((kc1 - kc0 + KW * 32 - 1) / (KW * 32)) * 32;
+        const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
+        for (int kb0 = ka; kb0 < kb; kb0 += 8 * 32) {
+            u32x4_t a0[8], a1[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = kb0 + 32 * u + kk;
+                a0[u] = (ap0 && k < kb) ? ld16_stream(ap0 + k) : zero4();
+                a1[u] = (ap1 && k < kb) ? ld16_stream(ap1 + k) : zero4();
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = kb0 + 32 * u + kk;
+                const u32x4_t xo = k < kb ? lds16(xs + col * kXS + (k - kc0)) : zero4();
+                if (has0) acc0 = mfma_16x16x32(xo, a0[u], acc0);
+                if (has1) acc1 = mfma_16x16x32(xo, a1[u], acc1);
+            }
+        }
+    }
+    // lane holds D[tile row 4*(lane>>4) + i][rank row rl]
+    float *dst = KW == 1 ? res : red + kw * kRedStride;
+    const int j0 = (lane >> 4) * 4;
+    if (has0 && rl0 < n_rr) {
+        dst[rl0 * 16 + j0 + 0] = acc0[0];
+        dst[rl0 * 16 + j0 + 1] = acc0[1];
+        dst[rl0 * 16 + j0 + 2] = acc0[2];
+        dst[rl0 * 16 + j0 + 3] = acc0[3];
+    }
+    if (has1 && rl1 < n_rr) {
+        dst[rl1 * 16 + j0 + 0] = acc1[0];
+        dst[rl1 * 16 + j0 + 1] = acc1[1];
+        dst[rl1 * 16 + j0 + 2] = acc1[2];
+        dst[rl1 * 16 + j0 + 3] = acc1[3];
+    }
+    reduce_waves(KW, n_rr, res, red);
+}
+
+// Same result on the vector ALU (v_dot2c_f32_bf16) for n_rr <= kRRValu:
+// a wave holds 8 rank rows x 8 k lanes; each lane dots 8 k per load and the
+// 8 k lanes of a rank row are summed with xor shuffles at the end.
 template <class Op>
 __device__ void shrink_valu(const Op &op, const UnitHdr &h, int rr0, int n_rr, int k0, int k1, float *res,
-                            float *red) {
+                            float *red, uint16_t *xs) {
     const int lane = lane_id(), w = wave_id();
     const int rsub = lane >> 3, kl = lane & 7;
     const int groups = n_rr >> 3;
     int GW, KW;
     wave_split(groups, GW, KW);
     const int gw = w % GW, kw = w / GW;
-    const int per = ((k1 - k0 + KW * 64 - 1) / (KW * 64)) * 64;
-    const int ka = k0 + kw * per, kb = min(k1, ka + per);
     const int m = h.m;
     float *dst = KW == 1 ? res : red + kw * kRedStride;
-    for (int q = gw; q < groups; q += GW) {
-        const int rl = 8 * q + rsub;
-        const uint16_t *ap = op.arow(h.slot, rr0 + rl);
-        float acc[kTileRows];
+    for (int kc0 = k0; kc0 < k1; kc0 += kKC) {
+        const int kc1 = min(k1, kc0 + kKC);
+        __syncthreads();
+        stage_x(h, kc0, kc1, xs);
+        __syncthreads();
+        const int per = ((kc1 - kc0 + KW * 64 - 1) / (KW * 64)) * 64;
+        const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
+        for (int q = gw; q < groups; q += GW) {
+            const int rl = 8 * q + rsub;
+            const uint16_t *ap = op.arow(h.slot, rr0 + rl);
+            float acc[kTileRows];
 #pragma unroll
-        for (int j = 0; j < kTileRows; ++j) acc[j] = 0.f;
-        for (int k = ka + 8 * kl; k < kb; k += 64) {
-            const u32x4_t av = ld16_stream(ap + k);
+            for (int j = 0; j < kTileRows; ++j) acc[j] = 0.f;
+            for (int kb0 = ka; kb0 < kb; kb0 += 8 * 64) {
+                u32x4_t a[8];
 #pragma unroll
-            for (int j = 0; j < kTileRows; ++j)
-                if (j < m) acc[j] = dot8(av, ld16(h.xrow[j] + k), acc[j]);
-        }
+                for (int u = 0; u < 8; ++u) {
+                    const int k = kb0 + 64 * u + 8 * kl;
+                    a[u] = k < kb ? ld16_stream(ap + k) : zero4();
+                }
 #pragma unroll
-        for (int j = 0; j < kTileRows; ++j) {
-            if (j < m) {
-                float v = acc[j];
-                v += __shfl_xor(v, 1);
-                v += __shfl_xor(v, 2);
-                v += __shfl_xor(v, 4);
-                if (kl == 0) dst[rl * 16 + j] = v;
+                for (int j = 0; j < kTileRows; ++j) {
+                    if (j < m) {
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int k = kb0 + 64 * u + 8 * kl;
+                            if (k < kb) acc[j] = dot8(a[u], lds16(xs + j * kXS + (k - kc0)), acc[j]);
+                        }
+                    }
+                }
+            }
+            // sum the 8 k lanes of each rank row; accumulate over x chunks in dst
+#pragma unroll
+            for (int j = 0; j < kTileRows; ++j) {
+                if (j < m) {
+                    float v = acc[j];
+                    v += __shfl_xor(v, 1);
+                    v += __shfl_xor(v, 2);
+                    v += __shfl_xor(v, 4);
+                    if (kl == 0) dst[rl * 16 + j] = (kc0 == k0 ? 0.f : dst[rl * 16 + j]) + v;
+                }
             }
         }
     }
-    __syncthreads();
-    if (KW > 1) {
-        for (int idx = threadIdx.x; idx < n_rr * 16; idx += kBT) {
-            float s = red[idx];
-            for (int q = 1; q < KW; ++q) s += red[q * kRedStride + idx];
-            res[idx] = s;
-        }
-        __syncthreads();
-    }
+    reduce_waves(KW, n_rr, res, red);
 }
 
+// Rank rows [rr0, rr0 + n_rr) of one tile over k in [k0, k1) into res
+// (n_rr <= kRRMfma on the MFMA path, <= kRRValu on the vector ALU).
 template <class Op>
 __device__ __forceinline__ void shrink_compute(const Op &op, const UnitHdr &h, bool mf, int rr0, int n_rr,
-                                               int k0, int k1, float *res, float *red) {
+                                               int k0, int k1, float *res, float *red, uint16_t *xs) {
     if (mf)
-        shrink_mfma(op, h, rr0, n_rr, k0, k1, res, red);
+        shrink_mfma(op, h, rr0, n_rr, k0, k1, res, red, xs);
     else
-        shrink_valu(op, h, rr0, n_rr, k0, k1, res, red);
+        shrink_valu(op, h, rr0, n_rr, k0, k1, res, red, xs);
 }
 
 // ============================================================ expand
@@ -247,138 +319,245 @@ struct XaDirect {  // caller's xa[slice][n][R], already scaled
     int n, R;
     __device__ float get(int sg, int row, int, int r) const { return xa[((int64_t)sg * n + row) * R + r]; }
 };
-struct XaPartials {  // fused workspace part[p][pos][n_rr], scaled here
+struct XaPartials {  // fused workspace part[pos][n_rr][P] (P a power of two <= 16), scaled here
     const float *part;
-    int n, P, n_rr, R;
+    int P, n_rr, R;
     float scale;
     __device__ float get(int sg, int, int pos, int r) const {
+        const float *q = part + ((int64_t)pos * n_rr + sg * R + r) * P;
         float s = 0.f;
-        for (int p = 0; p < P; ++p) s += part[((int64_t)p * n + pos) * n_rr + sg * R + r];
+        if (P >= 4) {
+            for (int c = 0; c < P; c += 4) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(q + c);
+                s += v[0];
+                s += v[1];
+                s += v[2];
+                s += v[3];
+            }
+        } else {
+            for (int c = 0; c < P; ++c) s += q[c];
+        }
         return scale * s;
     }
 };
 
+struct NoWait {
+    __device__ bool operator()() const { return true; }
+};
+
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
-template <class Op>
-__device__ __forceinline__ void store_row8(const Op &op, uint16_t *yp, const float *v, bool add_inputs) {
-    float o[8];
+// xl[sl][j][0..R) = bf16(xa), xl[sl][j][R..2R) = bf16(xa - bf16(xa)) for the
+// tile rows j (zero past m) and xa slices sg_lo .. sg_lo + ns - 1.
+template <class Xa>
+__device__ void stage_xa(const UnitHdr &h, const Xa &xs, int sg_lo, int ns, int R, uint16_t *xl) {
+    const int total = ns * kTileRows * R;
+    for (int base = 0; base < total; base += 4 * kBT) {
+        float v[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = v[q];
-    if (add_inputs) {
-        const u32x4_t yv = ld16(yp);
-        o[0] += bf_lo(yv.x);
-        o[1] += bf_hi(yv.x);
-        o[2] += bf_lo(yv.y);
-        o[3] += bf_hi(yv.y);
-        o[4] += bf_lo(yv.z);
-        o[5] += bf_hi(yv.z);
-        o[6] += bf_lo(yv.w);
-        o[7] += bf_hi(yv.w);
+        for (int i = 0; i < 4; ++i) {
+            const int idx = base + threadIdx.x + kBT * i;
+            const int r = idx % R, j = (idx / R) % kTileRows, sl = idx / (kTileRows * R);
+            v[i] = (idx < total && j < h.m) ? xs.get(sg_lo + sl, h.rows[j], h.pos0 + j, r) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = base + threadIdx.x + kBT * i;
+            if (idx < total) {
+                const int r = idx % R, j = (idx / R) % kTileRows, sl = idx / (kTileRows * R);
+                const float hi = bf16_round(v[i]);
+                uint16_t *d = xl + (sl * kTileRows + j) * 2 * R;
+                d[r] = bf16_bits(hi);
+                d[R + r] = bf16_bits(v[i] - hi);
+            }
+        }
     }
-    st16(yp, u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                     pack_bf16x2(o[6], o[7])});
 }
 
-template <class Op, class Xa>
-__device__ void expand_unit(const Op &op, const UnitHdr &h, bool mf, int c0, const Xa &xs, bool add_inputs,
-                            char *smem) {
-    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-    const int R = op.R, R2 = 2 * R;
+// Vector-ALU expand of one unit: thread t owns columns c0 + 2t, c0 + 2t + 1 and
+// every row of the tile.  B and y are loaded before `wait` returns.
+template <class Op, class Xa, class Wait>
+__device__ void expand_valu(const Op &op, const UnitHdr &h, int c0, const Xa &xs, bool add_inputs,
+                            const Wait &wait, char *smem) {
+    const int R = op.R, m = h.m;
     const int cend = min(c0 + kCW, op.n_out);
-    const int sg_lo = op.xslice(c0), sg_hi = op.xslice(cend - 1);
-    const int ns = sg_hi - sg_lo + 1;
-    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);  // [ns][16][hi R | lo R]
-    for (int idx = tid; idx < ns * kTileRows * R; idx += kBT) {
-        const int r = idx % R, j = (idx / R) % kTileRows, sl = idx / (kTileRows * R);
-        const float v = j < h.m ? xs.get(sg_lo + sl, h.rows[j], h.pos0 + j, r) : 0.f;
-        const float hi = bf16_round(v);
-        uint16_t *d = xl + (sl * kTileRows + j) * R2;
-        d[r] = bf16_bits(hi);
-        d[R + r] = bf16_bits(v - hi);
+    const int sg_lo = op.xslice(c0), ns = op.xslice(cend - 1) - sg_lo + 1;
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
+    const int c = c0 + 2 * threadIdx.x;
+    const bool cok = c < cend;
+    const int sl = cok ? op.xslice(c) - sg_lo : 0;
+    const uint16_t *b = cok ? op.brow(h.slot, c) : nullptr;  // rows c, c+1: 2R contiguous
+    u32x4_t bv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        bv[q] = (cok && 8 * q < R) ? ld16_stream(b + 8 * q) : zero4();
+        bv[4 + q] = (cok && 8 * q < R) ? ld16_stream(b + R + 8 * q) : zero4();
     }
+    uint32_t yv[kTileRows];
+#pragma unroll
+    for (int j = 0; j < kTileRows; ++j)
+        yv[j] = (cok && add_inputs && j < m) ? *reinterpret_cast<const uint32_t *>(op.yrow(h.rows[j]) + c) : 0u;
+    if (!wait()) return;
+    stage_xa(h, xs, sg_lo, ns, R, xl);
     __syncthreads();
-
-    if (!mf) {
-        // vector ALU: lane -> 8 columns, wave w -> rows w, w+4, w+8, w+12
-        const int c = c0 + 8 * lane;
-        if (c < cend) {
-            const int sl = op.xslice(c) - sg_lo;
-            const uint16_t *b = op.brow(h.slot, c);
-            float acc[4][8];
+    float a0[kTileRows], a1[kTileRows];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < kTileRows; ++j) a0[j] = a1[j] = 0.f;
+    for (int rb = 0; rb < R; rb += 32) {
+        if (rb > 0) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
-            for (int r8 = 0; r8 < R; r8 += 8) {
-                u32x4_t bv[8];
+            for (int q = 0; q < 4; ++q) {
+                bv[q] = (cok && rb + 8 * q < R) ? ld16_stream(b + rb + 8 * q) : zero4();
+                bv[4 + q] = (cok && rb + 8 * q < R) ? ld16_stream(b + R + rb + 8 * q) : zero4();
+            }
+        }
 #pragma unroll
-                for (int q = 0; q < 8; ++q) bv[q] = ld16_stream(b + q * R + r8);
+        for (int j = 0; j < kTileRows; ++j) {
+            if (j < m) {
+                const uint16_t *xr = xl + (sl * kTileRows + j) * 2 * R;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = w + 4 * i;
-                    if (j < h.m) {
-                        const uint16_t *xr = xl + (sl * kTileRows + j) * R2;
-                        const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(xr + r8);
-                        const u32x4_t lv = *reinterpret_cast<const u32x4_t *>(xr + R + r8);
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) acc[i][q] = dot8(bv[q], lv, dot8(bv[q], hv, acc[i][q]));
+                for (int q = 0; q < 4; ++q) {
+                    if (rb + 8 * q < R) {
+                        const u32x4_t hv = lds16(xr + rb + 8 * q);
+                        const u32x4_t lv = lds16(xr + R + rb + 8 * q);
+                        a0[j] = dot8(bv[q], lv, dot8(bv[q], hv, a0[j]));
+                        a1[j] = dot8(bv[4 + q], lv, dot8(bv[4 + q], hv, a1[j]));
                     }
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = w + 4 * i;
-                if (j < h.m) store_row8(op, op.yrow(h.rows[j]) + c, acc[i], add_inputs);
-            }
         }
-        return;
     }
+    if (!cok) return;
+#pragma unroll
+    for (int j = 0; j < kTileRows; ++j) {
+        if (j < m) {
+            float lo = a0[j], hi = a1[j];
+            if (add_inputs) {
+                lo += bf_lo(yv[j]);
+                hi += bf_hi(yv[j]);
+            }
+            *reinterpret_cast<uint32_t *>(op.yrow(h.rows[j]) + c) = pack_bf16x2(lo, hi);
+        }
+    }
+}
 
-    // MFMA: D[col][row] = B[col][hi|lo ranks] . [xa_hi | xa_lo][row]; wave w -> 128 columns
+// MFMA expand of one unit: D[column][tile row] = B[column][ranks] .
+// (xa_hi + xa_lo)[tile row][ranks] as two bf16 MFMAs per 32 ranks; wave w owns
+// columns c0 + 128w .. +128 (8 tiles of 16).  NRS = rank steps of 32.
+template <int NRS, class Op, class Xa, class Wait>
+__device__ void expand_mfma(const Op &op, const UnitHdr &h, int c0, const Xa &xs, bool add_inputs,
+                            const Wait &wait, char *smem) {
+    constexpr int CTB = 8 / NRS;  // column tiles whose B operands are in flight together (8 loads)
+    const int lane = lane_id(), w = wave_id();
+    const int R = op.R, R2 = 2 * R;
+    const int cend = min(c0 + kCW, op.n_out);
+    const int sg_lo = op.xslice(c0), ns = op.xslice(cend - 1) - sg_lo + 1;
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
     const size_t xl_bytes = ((size_t)ns * kTileRows * R2 * 2 + 15) & ~(size_t)15;
     float *ol = reinterpret_cast<float *>(smem + xl_bytes) + w * (kTileRows * kOutStride);
     const int cw0 = c0 + 128 * w;
     const int col_l = lane & 15, kk = (lane >> 4) * 8;
-    for (int ct = 0; ct < 8; ++ct) {
-        const int cb = cw0 + 16 * ct;
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-        if (cb < cend) {
-            const int c = cb + col_l;
-            const bool cok = c < cend;
-            const int sgc = cok ? op.xslice(c) : -1;
-            const int s_first = op.xslice(cb), s_last = op.xslice(min(cb + 15, cend - 1));
+
+    u32x4_t bo[CTB][NRS];
+    // B operands of column tiles ct0 .. ct0+CTB-1; rows of columns outside
+    // xa slice `only` (when >= 0) are zeroed
+    auto load_b = [&](int ct0, int only) {
+#pragma unroll
+        for (int i = 0; i < CTB; ++i) {
+            const int c = cw0 + 16 * (ct0 + i) + col_l;
+            const bool cok = c < cend && (only < 0 || op.xslice(c) == only);
             const uint16_t *b = cok ? op.brow(h.slot, c) : nullptr;
-            for (int sg = s_first; sg <= s_last; ++sg) {
-                const bool use = cok && sgc == sg;
-                const uint16_t *xr = xl + ((sg - sg_lo) * kTileRows + col_l) * R2;  // MFMA-B column = tile row
-                for (int kb = 0; kb < R2; kb += 32) {
-                    const int kap = kb + kk;
-                    const bool kin = kap < R2;
-                    const int r = kap < R ? kap : kap - R;
-                    const u32x4_t ao = (use && kin) ? ld16_stream(b + r) : zero4();
-                    const u32x4_t bo = kin ? *reinterpret_cast<const u32x4_t *>(xr + kap) : zero4();
-                    d = mfma_16x16x32(ao, bo, d);
+#pragma unroll
+            for (int s = 0; s < NRS; ++s) {
+                const int rk = 32 * s + kk;
+                bo[i][s] = (cok && rk < R) ? ld16_stream(b + rk) : zero4();
+            }
+        }
+    };
+    load_b(0, -1);
+    // y for the epilogue: rows 4p + lane/16, columns cw0 + 8*(lane%16)
+    const int cy = cw0 + 8 * (lane & 15);
+    u32x4_t yv[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int j = 4 * p + (lane >> 4);
+        yv[p] = (add_inputs && j < h.m && cy < cend) ? ld16(op.yrow(h.rows[j]) + cy) : zero4();
+    }
+    if (!wait()) return;
+    stage_xa(h, xs, sg_lo, ns, R, xl);
+    __syncthreads();
+
+    f32x4_t d[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int sg_w0 = op.xslice(min(cw0, cend - 1)), sg_w1 = op.xslice(min(cw0 + 127, cend - 1));
+    const bool straddle = sg_w0 != sg_w1;
+    // one pass per xa slice under this wave's columns (almost always one);
+    // when they straddle a slice boundary each pass masks the other slice's rows
+    for (int sg = sg_w0; cw0 < cend && sg <= sg_w1; ++sg) {
+        const uint16_t *xr = xl + ((sg - sg_lo) * kTileRows + col_l) * R2;  // MFMA-B column = tile row
+        u32x4_t hv[NRS], lv[NRS];
+#pragma unroll
+        for (int s = 0; s < NRS; ++s) {
+            const int rk = 32 * s + kk;
+            hv[s] = rk < R ? lds16(xr + rk) : zero4();
+            lv[s] = rk < R ? lds16(xr + R + rk) : zero4();
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; cb += CTB) {
+            if (cb > 0 || straddle) load_b(cb, straddle ? sg : -1);
+#pragma unroll
+            for (int i = 0; i < CTB; ++i) {
+#pragma unroll
+                for (int s = 0; s < NRS; ++s) {
+                    d[cb + i] = mfma_16x16x32(bo[i][s], hv[s], d[cb + i]);
+                    d[cb + i] = mfma_16x16x32(bo[i][s], lv[s], d[cb + i]);
                 }
             }
         }
-        // lane holds D[column cb + 4*(lane>>4) + i][tile row lane & 15]
+    }
+    // lane holds D[column cw0 + 16ct + 4*(lane>>4) + q][tile row lane & 15]
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
         float *o = ol + col_l * kOutStride + 16 * ct + 4 * (lane >> 4);
-        o[0] = d[0];
-        o[1] = d[1];
-        o[2] = d[2];
-        o[3] = d[3];
+        o[0] = d[ct][0];
+        o[1] = d[ct][1];
+        o[2] = d[ct][2];
+        o[3] = d[ct][3];
     }
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int j = 4 * p + (lane >> 4);
-        const int c = cw0 + 8 * (lane & 15);
-        if (j < h.m && c < cend) {
+        if (j < h.m && cy < cend) {
             const float *src = ol + j * kOutStride + 8 * (lane & 15);
-            store_row8(op, op.yrow(h.rows[j]) + c, src, add_inputs);
+            float o[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = src[q];
+            if (add_inputs) {
+                o[0] += bf_lo(yv[p].x);
+                o[1] += bf_hi(yv[p].x);
+                o[2] += bf_lo(yv[p].y);
+                o[3] += bf_hi(yv[p].y);
+                o[4] += bf_lo(yv[p].z);
+                o[5] += bf_hi(yv[p].z);
+                o[6] += bf_lo(yv[p].w);
+                o[7] += bf_hi(yv[p].w);
+            }
+            st16(op.yrow(h.rows[j]) + cy,
+                 u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                         pack_bf16x2(o[6], o[7])});
         }
     }
+}
+
+template <int NRS, class Op, class Xa, class Wait>
+__device__ __forceinline__ void expand_unit(const Op &op, const UnitHdr &h, bool mf, int c0, const Xa &xs,
+                                            bool add_inputs, const Wait &wait, char *smem) {
+    if (mf)
+        expand_mfma<NRS>(op, h, c0, xs, add_inputs, wait, smem);
+    else
+        expand_valu(op, h, c0, xs, add_inputs, wait, smem);
 }
 
 // ============================================================ kernels
@@ -390,18 +569,24 @@ __global__ __launch_bounds__(kBT) void shrink_kernel(Op op, const int32_t *tiles
     const int t = blockIdx.x / n_sl, sl = blockIdx.x % n_sl;
     if (!load_tile(op, tiles, t, h)) return;
     const bool mf = h.mseg >= mfma_min;
-    float *res = reinterpret_cast<float *>(smem);
-    float *red = res + kRRChunk * 16;
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+    float *res = reinterpret_cast<float *>(smem + kXsBytes);
+    float *red = res + kRRMfma * 16;
     const int R = op.R;
-    shrink_compute(op, h, mf, sl * R, R, 0, op.k_in, res, red);
     const float sc = op.scale_of(h.slot);
-    for (int idx = threadIdx.x; idx < h.m * R; idx += kBT) {
-        const int j = idx / R, r = idx % R;
-        xa[((int64_t)sl * n + h.rows[j]) * R + r] = sc * res[r * 16 + j];
+    const int chunk = mf ? kRRMfma : kRRValu;
+    for (int r0 = 0; r0 < R; r0 += chunk) {
+        const int cnt = min(chunk, R - r0);
+        shrink_compute(op, h, mf, sl * R + r0, cnt, 0, op.k_in, res, red, xs);
+        for (int idx = threadIdx.x; idx < h.m * cnt; idx += kBT) {
+            const int j = idx / cnt, r = idx % cnt;
+            xa[((int64_t)sl * n + h.rows[j]) * R + r0 + r] = sc * res[r * 16 + j];
+        }
+        __syncthreads();
     }
 }
 
-template <class Op>
+template <int NRS, class Op>
 __global__ __launch_bounds__(kBT) void expand_kernel(Op op, const int32_t *tiles, const float *xa, int n, int C,
                                                      int add_inputs, int mfma_min) {
     extern __shared__ __align__(16) char smem[];
@@ -409,7 +594,7 @@ __global__ __launch_bounds__(kBT) void expand_kernel(Op op, const int32_t *tiles
     const int t = blockIdx.x / C, cc = blockIdx.x % C;
     if (!load_tile(op, tiles, t, h)) return;
     const bool mf = h.mseg >= mfma_min;
-    expand_unit(op, h, mf, cc * kCW, XaDirect{xa, n, op.R}, add_inputs != 0, smem);
+    expand_unit<NRS>(op, h, mf, cc * kCW, XaDirect{xa, n, op.R}, add_inputs != 0, NoWait{}, smem);
 }
 
 struct ZeroFill {  // MoE: rows of pairs without a valid (adapter, expert) are zeroed
@@ -418,7 +603,39 @@ struct ZeroFill {  // MoE: rows of pairs without a valid (adapter, expert) are z
     int top_k, E, L, n_pairs;
 };
 
-template <class Op>
+// Expand-unit wait of the fused kernel: thread 0 polls the tile's counter
+// until all P shrink pieces have been published, then acquires once.
+struct TileWait {
+    int *ctl, *ctr, *done;
+    int t, P, C;
+    UnitHdr *h;
+    __device__ bool operator()() const {
+        if (threadIdx.x == 0) {
+            // poll without acquire semantics (an acquire load would invalidate
+            // the L2 on every poll), then acquire once
+            int spins = 0;
+            while (load_relaxed(&ctr[t]) < P) {
+                __builtin_amdgcn_s_sleep(1);
+                if (++spins > kSpinLimit) {
+                    atomicExch(&ctl[0], 1);
+                    h->flag = 1;
+                    break;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (!h->flag && atomicAdd(&done[t], 1) == C - 1) {
+                store_relaxed(&ctr[t], 0);
+                store_relaxed(&done[t], 0);
+            }
+        }
+        // thread 0's agent-scope acquire is ordered before the other threads'
+        // loads of the partials by the workgroup barrier
+        __syncthreads();
+        return h->flag == 0;
+    }
+};
+
+template <int NRS, class Op>
 __global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles, int tile_bound, int P, int C,
                                                     int n_pos, float *part, int *ctl, int *ctr, int *done,
                                                     int mfma_min, int add_inputs, ZeroFill zf) {
@@ -434,19 +651,21 @@ __global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles,
         const bool mf = h.mseg >= mfma_min;
         const int KP = (((op.k_in + P - 1) / P + 63) / 64) * 64;
         const int k0 = min(op.k_in, p * KP), k1 = min(op.k_in, k0 + KP);
-        float *res = reinterpret_cast<float *>(smem);
-        float *red = res + kRRChunk * 16;
-        for (int rr0 = 0; rr0 < n_rr; rr0 += kRRChunk) {
-            const int cnt = min(kRRChunk, n_rr - rr0);
-            shrink_compute(op, h, mf, rr0, cnt, k0, k1, res, red);
+        uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+        float *res = reinterpret_cast<float *>(smem + kXsBytes);
+        float *red = res + kRRMfma * 16;
+        const int chunk = mf ? kRRMfma : kRRValu;
+        for (int rr0 = 0; rr0 < n_rr; rr0 += chunk) {
+            const int cnt = min(chunk, n_rr - rr0);
+            shrink_compute(op, h, mf, rr0, cnt, k0, k1, res, red, xs);
             for (int idx = tid; idx < h.m * cnt; idx += kBT) {
                 const int j = idx / cnt, rl = idx % cnt;
-                part[((int64_t)p * n_pos + h.pos0 + j) * n_rr + rr0 + rl] = res[rl * 16 + j];
+                part[((int64_t)(h.pos0 + j) * n_rr + rr0 + rl) * P + p] = res[rl * 16 + j];
             }
             __syncthreads();
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
+        // every thread's partial stores are ordered before thread 0's
+        // agent-scope release by the workgroup barrier above
         if (tid == 0) atomic_add_release(&ctr[t], 1);
         return;
     }
@@ -454,27 +673,9 @@ __global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles,
         const int e = bid - n_shr;
         const int t = e / C, cc = e % C;
         if (!load_tile(op, tiles, t, h)) return;
-        if (tid == 0) {
-            int spins = 0;
-            while (load_acquire(&ctr[t]) < P) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kSpinLimit) {
-                    atomicExch(&ctl[0], 1);
-                    h.flag = 1;
-                    break;
-                }
-            }
-            if (!h.flag && atomicAdd(&done[t], 1) == C - 1) {
-                store_relaxed(&ctr[t], 0);
-                store_relaxed(&done[t], 0);
-            }
-        }
-        __syncthreads();
-        if (h.flag) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const bool mf = h.mseg >= mfma_min;
-        expand_unit(op, h, mf, cc * kCW, XaPartials{part, n_pos, P, n_rr, op.R, op.scale_of(h.slot)},
-                    add_inputs != 0, smem);
+        expand_unit<NRS>(op, h, mf, cc * kCW, XaPartials{part, P, n_rr, op.R, op.scale_of(h.slot)},
+                         add_inputs != 0, TileWait{ctl, ctr, done, t, P, C, &h}, smem);
         return;
     }
     // zero rows of pairs that get no delta (MoE only)
@@ -490,12 +691,17 @@ __global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles,
 // ============================================================ host side
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-static size_t shrink_lds() { return (size_t)(kRRChunk * 16 + 4 * kRedStride) * sizeof(float); }
+static size_t shrink_lds() {
+    return (size_t)kXsBytes + (size_t)(kRRMfma * 16 + 4 * kRedStride) * sizeof(float);
+}
 
 static size_t expand_lds(int n_xa_slices, int R) {
     return align_up((size_t)n_xa_slices * kTileRows * 2 * R * 2, 16) +
            (size_t)4 * kTileRows * kOutStride * sizeof(float);
 }
+
+// rank steps of 32 of the MFMA expand
+static int nrs_of(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }
 
 static int tile_bound_of(int n, int S) {
     if (n <= 0) return 0;
@@ -508,7 +714,8 @@ FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out)
     p.tile_bound = tile_bound_of(n, num_slots);
     p.P = 1;
     const int target_units = 512;  // about two units per CU of the shrink over the k dimension
-    while (p.tile_bound > 0 && (long long)p.P * 2 * p.tile_bound <= target_units && p.P * 2 <= k_in / 256)
+    while (p.tile_bound > 0 && (long long)p.P * 2 * p.tile_bound <= target_units && p.P * 2 <= k_in / 256 &&
+           p.P * 2 <= kMaxPieces)
         p.P *= 2;
     p.C = (n_out + kCW - 1) / kCW;
     p.ctr_bytes = align_up(64 + (size_t)2 * p.tile_bound * sizeof(int), 256);
@@ -553,15 +760,43 @@ hipError_t launch_shrink(const DenseShape &d, const int32_t *tiles, int tile_bou
     return hipGetLastError();
 }
 
+template <int NRS>
+static hipError_t launch_expand_nrs(const DenseOp &op, const float *xa, const int32_t *tiles, int tile_bound,
+                                    int n, int add_inputs, int mfma_min, size_t lds, hipStream_t st) {
+    const int C = (op.n_out + kCW - 1) / kCW;
+    allow_lds(expand_kernel<NRS, DenseOp>, lds);
+    hipLaunchKernelGGL((expand_kernel<NRS, DenseOp>), dim3(tile_bound * C), dim3(kBT), lds, st, op, tiles, xa, n,
+                       C, add_inputs, mfma_min);
+    return hipGetLastError();
+}
+
 hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *tiles, int tile_bound,
                          int add_inputs, int mfma_min, hipStream_t st) {
     if (tile_bound == 0) return hipSuccess;
     const DenseOp op = dense_op(d);
-    const int C = (op.n_out + kCW - 1) / kCW;
     const size_t lds = expand_lds(d.num_slices, d.R);
-    allow_lds(expand_kernel<DenseOp>, lds);
-    hipLaunchKernelGGL(expand_kernel<DenseOp>, dim3(tile_bound * C), dim3(kBT), lds, st, op, tiles, xa, d.n, C,
-                       add_inputs, mfma_min);
+    switch (nrs_of(d.R)) {
+    case 1: return launch_expand_nrs<1>(op, xa, tiles, tile_bound, d.n, add_inputs, mfma_min, lds, st);
+    case 2: return launch_expand_nrs<2>(op, xa, tiles, tile_bound, d.n, add_inputs, mfma_min, lds, st);
+    default: return launch_expand_nrs<4>(op, xa, tiles, tile_bound, d.n, add_inputs, mfma_min, lds, st);
+    }
+}
+
+template <int NRS, class Op>
+static hipError_t launch_fused_nrs(const Op &op, int n_pos, int n_xa_slices, const int32_t *tiles,
+                                   const FusedPlan &plan, void *ws, int mfma_min, int add_inputs, ZeroFill zf,
+                                   int zero_units, hipStream_t st) {
+    char *w = static_cast<char *>(ws);
+    int *ctl = reinterpret_cast<int *>(w);
+    int *ctr = ctl + 16;
+    int *done = ctr + plan.tile_bound;
+    float *part = reinterpret_cast<float *>(w + plan.ctr_bytes);
+    const size_t lds = std::max(shrink_lds(), expand_lds(n_xa_slices, op.R));
+    allow_lds(fused_kernel<NRS, Op>, lds);
+    const long long grid = (long long)plan.tile_bound * (plan.P + plan.C) + zero_units;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((fused_kernel<NRS, Op>), dim3((unsigned)grid), dim3(kBT), lds, st, op, tiles,
+                       plan.tile_bound, plan.P, plan.C, n_pos, part, ctl, ctr, done, mfma_min, add_inputs, zf);
     return hipGetLastError();
 }
 
@@ -569,18 +804,11 @@ template <class Op>
 static hipError_t launch_fused_op(const Op &op, int n_pos, int n_xa_slices, const int32_t *tiles,
                                   const FusedPlan &plan, void *ws, int mfma_min, int add_inputs, ZeroFill zf,
                                   int zero_units, hipStream_t st) {
-    char *w = static_cast<char *>(ws);
-    int *ctl = reinterpret_cast<int *>(w);
-    int *ctr = ctl + 16;
-    int *done = ctr + plan.tile_bound;
-    float *part = reinterpret_cast<float *>(w + plan.ctr_bytes);
-    const size_t lds = shrink_lds() > expand_lds(n_xa_slices, op.R) ? shrink_lds() : expand_lds(n_xa_slices, op.R);
-    allow_lds(fused_kernel<Op>, lds);
-    const long long grid = (long long)plan.tile_bound * (plan.P + plan.C) + zero_units;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(fused_kernel<Op>, dim3((unsigned)grid), dim3(kBT), lds, st, op, tiles, plan.tile_bound,
-                       plan.P, plan.C, n_pos, part, ctl, ctr, done, mfma_min, add_inputs, zf);
-    return hipGetLastError();
+    switch (nrs_of(op.R)) {
+    case 1: return launch_fused_nrs<1>(op, n_pos, n_xa_slices, tiles, plan, ws, mfma_min, add_inputs, zf, zero_units, st);
+    case 2: return launch_fused_nrs<2>(op, n_pos, n_xa_slices, tiles, plan, ws, mfma_min, add_inputs, zf, zero_units, st);
+    default: return launch_fused_nrs<4>(op, n_pos, n_xa_slices, tiles, plan, ws, mfma_min, add_inputs, zf, zero_units, st);
+    }
 }
 
 hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const FusedPlan &plan, void *ws, int mfma_min,
