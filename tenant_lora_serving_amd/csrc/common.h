@@ -69,6 +69,23 @@ __device__ __forceinline__ u32x4_t ld16_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
 }
 
+// ---------------------------------------------------------------- DPP lane sums
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Sum over aligned groups of 2^lg lanes (lg <= 4); every lane of a group gets
+// the group's total.  quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at xor 1
+// and xor 2; row_half_mirror (i <-> 7-i) and row_mirror (i <-> 15-i) then
+// join quads into 8 and 16 lanes.
+__device__ __forceinline__ float group_sum(float v, int lg) {
+    if (lg >= 1) v += dpp_mov<0xB1>(v);
+    if (lg >= 2) v += dpp_mov<0x4E>(v);
+    if (lg >= 3) v += dpp_mov<0x141>(v);
+    if (lg >= 4) v += dpp_mov<0x140>(v);
+    return v;
+}
+
 // ---------------------------------------------------------------- wave/block scans
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int lane = lane_id();

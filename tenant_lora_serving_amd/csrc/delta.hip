@@ -43,6 +43,8 @@ constexpr int kMaxPieces = 16;  // k pieces of the fused shrink
 constexpr int kRedStride = 48 * 16;  // per-wave partial block when waves split k
 constexpr int kOutStride = 132;      // padded fp32 row stride of the MFMA output tile
 constexpr int kSpinLimit = 1 << 24;
+constexpr int kCtrStride = 64;  // ints between tile counters: one 256-byte line each, so
+                                // pollers and publishers of different tiles never share a line
 
 // ============================================================ addressing
 struct DenseOp {
@@ -61,9 +63,12 @@ struct DenseOp {
     __device__ const uint16_t *arow(int slot, int rr) const {
         return a_pool + ((int64_t)slot * n_sh * R + rr) * k_in;
     }
+    // slice of output column c; unrolled so off[] is only read at constant
+    // indices (a runtime index would move the kernel argument to scratch)
     __device__ int xslice(int c) const {
         int l = 0;
-        while (l + 1 < n_sl && c >= off[l + 1]) ++l;
+#pragma unroll
+        for (int i = 1; i < kMaxSlices; ++i) l += (i < n_sl && c >= off[i]) ? 1 : 0;
         return l;
     }
     __device__ const uint16_t *brow(int slot, int c) const {
@@ -107,30 +112,40 @@ struct MoeOp {
 };
 
 // ============================================================ tile header
-struct UnitHdr {
-    int m, slot, pos0, mseg, flag;
+// The scalar fields of a tile record live in SGPRs (read through
+// readfirstlane), so every branch on them is uniform; the row ids and x row
+// pointers live in LDS.
+struct TileLds {
+    int hdr[4];
+    int flag;
     int rows[kTileRows];
     const uint16_t *xrow[kTileRows];
 };
 
+struct Tile {
+    int m, slot, pos0, mseg;
+    const int *rows;               // LDS
+    const uint16_t *const *xrow;   // LDS (null past m)
+};
+
 template <class Op>
-__device__ bool load_tile(const Op &op, const int32_t *tiles, int t, UnitHdr &h) {
+__device__ __forceinline__ bool load_tile(const Op &op, const int32_t *tiles, int t, TileLds &sh, Tile &h) {
     const int tid = threadIdx.x;
     const int32_t *rec = tiles + (int64_t)t * kTileWords;
-    if (tid == 0) {
-        h.m = rec[kRecRows];
-        h.slot = rec[kRecSlot];
-        h.pos0 = rec[kRecPos];
-        h.mseg = rec[kRecSegRows];
-        h.flag = 0;
-    }
+    if (tid < 4) sh.hdr[tid] = rec[tid == 0 ? kRecRows : tid == 1 ? kRecSlot : tid == 2 ? kRecPos : kRecSegRows];
+    if (tid == 0) sh.flag = 0;
     __syncthreads();
-    const int m = h.m;
-    if (m == 0) return false;
+    h.m = __builtin_amdgcn_readfirstlane(sh.hdr[0]);
+    h.slot = __builtin_amdgcn_readfirstlane(sh.hdr[1]);
+    h.pos0 = __builtin_amdgcn_readfirstlane(sh.hdr[2]);
+    h.mseg = __builtin_amdgcn_readfirstlane(sh.hdr[3]);
+    h.rows = sh.rows;
+    h.xrow = sh.xrow;
+    if (h.m == 0) return false;
     if (tid < kTileRows) {
-        const int row = tid < m ? rec[kRecRowIds + tid] : 0;
-        h.rows[tid] = row;
-        h.xrow[tid] = tid < m ? op.xrow(row) : nullptr;
+        const int row = tid < h.m ? rec[kRecRowIds + tid] : 0;
+        sh.rows[tid] = row;
+        sh.xrow[tid] = tid < h.m ? op.xrow(row) : nullptr;
     }
     __syncthreads();
     return true;
@@ -166,7 +181,7 @@ __device__ __forceinline__ void reduce_waves(int KW, int n_rr, float *res, const
 // flight before the first is consumed.
 //
 // Stage x rows j < 16 (zero rows past m), columns [kc0, kc1), into xs[j][.].
-__device__ __forceinline__ void stage_x(const UnitHdr &h, int kc0, int kc1, uint16_t *xs) {
+__device__ __forceinline__ void stage_x(const Tile &h, int kc0, int kc1, uint16_t *xs) {
     u32x4_t v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -185,8 +200,8 @@ __device__ __forceinline__ void stage_x(const UnitHdr &h, int kc0, int kc1, uint
 // rl < n_rr <= kRRMfma, on v_mfma_f32_16x16x32_bf16 (tile rows = MFMA rows,
 // rank rows = MFMA columns).
 template <class Op>
-__device__ void shrink_mfma(const Op &op, const UnitHdr &h, int rr0, int n_rr, int k0, int k1, float *res,
-                            float *red, uint16_t *xs) {
+__device__ __forceinline__ void shrink_mfma(const Op &op, const Tile &h, int rr0, int n_rr, int k0, int k1,
+                                            float *res, float *red, uint16_t *xs) {
     const int lane = lane_id(), w = wave_id();
     const int groups = (n_rr + 15) >> 4;
     int GW, KW;
@@ -198,27 +213,31 @@ __device__ void shrink_mfma(const Op &op, const UnitHdr &h, int rr0, int n_rr, i
     const uint16_t *ap0 = (has0 && rl0 < n_rr) ? op.arow(h.slot, rr0 + rl0) : nullptr;
     const uint16_t *ap1 = (has1 && rl1 < n_rr) ? op.arow(h.slot, rr0 + rl1) : nullptr;
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t a0[8], a1[8];
+    auto load_a = [&](int kb0, int kb) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = kb0 + 32 * u + kk;
+            a0[u] = (ap0 && k < kb) ? ld16(ap0 + k) : zero4();
+            a1[u] = (ap1 && k < kb) ? ld16(ap1 + k) : zero4();
+        }
+    };
     for (int kc0 = k0; kc0 < k1; kc0 += kKC) {
         const int kc1 = min(k1, kc0 + kKC);
+        const int per = ((kc1 - kc0 + KW * 32 - 1) / (KW * 32)) * 32;
+        const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
+        load_a(ka, kb);  // first A batch in flight while x is staged
         __syncthreads();
         stage_x(h, kc0, kc1, xs);
         __syncthreads();
-        const int per = ((kc1 - kc0 + KW * 32 - 1) / (KW * 32)) * 32;
-        const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
         for (int kb0 = ka; kb0 < kb; kb0 += 8 * 32) {
-            u32x4_t a0[8], a1[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int k = kb0 + 32 * u + kk;
-                a0[u] = (ap0 && k < kb) ? ld16_stream(ap0 + k) : zero4();
-                a1[u] = (ap1 && k < kb) ? ld16_stream(ap1 + k) : zero4();
-            }
+            if (kb0 > ka) load_a(kb0, kb);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int k = kb0 + 32 * u + kk;
                 const u32x4_t xo = k < kb ? lds16(xs + col * kXS + (k - kc0)) : zero4();
-                if (has0) acc0 = mfma_16x16x32(xo, a0[u], acc0);
-                if (has1) acc1 = mfma_16x16x32(xo, a1[u], acc1);
+                acc0 = mfma_16x16x32(xo, a0[u], acc0);  // absent groups multiply zeros
+                acc1 = mfma_16x16x32(xo, a1[u], acc1);
             }
         }
     }
@@ -244,8 +263,8 @@ __device__ void shrink_mfma(const Op &op, const UnitHdr &h, int rr0, int n_rr, i
 // a wave holds 8 rank rows x 8 k lanes; each lane dots 8 k per load and the
 // 8 k lanes of a rank row are summed with xor shuffles at the end.
 template <class Op>
-__device__ void shrink_valu(const Op &op, const UnitHdr &h, int rr0, int n_rr, int k0, int k1, float *res,
-                            float *red, uint16_t *xs) {
+__device__ __forceinline__ void shrink_valu(const Op &op, const Tile &h, int rr0, int n_rr, int k0, int k1,
+                                            float *res, float *red, uint16_t *xs) {
     const int lane = lane_id(), w = wave_id();
     const int rsub = lane >> 3, kl = lane & 7;
     const int groups = n_rr >> 3;
@@ -254,13 +273,21 @@ __device__ void shrink_valu(const Op &op, const UnitHdr &h, int rr0, int n_rr, i
     const int gw = w % GW, kw = w / GW;
     const int m = h.m;
     float *dst = KW == 1 ? res : red + kw * kRedStride;
+    u32x4_t a[8];
     for (int kc0 = k0; kc0 < k1; kc0 += kKC) {
         const int kc1 = min(k1, kc0 + kKC);
+        const int per = ((kc1 - kc0 + KW * 64 - 1) / (KW * 64)) * 64;
+        const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
+        // first A batch of this wave's first group in flight while x is staged
+        const uint16_t *ap_first = gw < groups ? op.arow(h.slot, rr0 + 8 * gw + rsub) : nullptr;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = ka + 64 * u + 8 * kl;
+            a[u] = (ap_first && k < kb) ? ld16_stream(ap_first + k) : zero4();
+        }
         __syncthreads();
         stage_x(h, kc0, kc1, xs);
         __syncthreads();
-        const int per = ((kc1 - kc0 + KW * 64 - 1) / (KW * 64)) * 64;
-        const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
         for (int q = gw; q < groups; q += GW) {
             const int rl = 8 * q + rsub;
             const uint16_t *ap = op.arow(h.slot, rr0 + rl);
@@ -268,32 +295,39 @@ __device__ void shrink_valu(const Op &op, const UnitHdr &h, int rr0, int n_rr, i
 #pragma unroll
             for (int j = 0; j < kTileRows; ++j) acc[j] = 0.f;
             for (int kb0 = ka; kb0 < kb; kb0 += 8 * 64) {
-                u32x4_t a[8];
+                if (q != gw || kb0 != ka) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int k = kb0 + 64 * u + 8 * kl;
-                    a[u] = k < kb ? ld16_stream(ap + k) : zero4();
+                    for (int u = 0; u < 8; ++u) {
+                        const int k = kb0 + 64 * u + 8 * kl;
+                        a[u] = k < kb ? ld16_stream(ap + k) : zero4();
+                    }
                 }
+                // x rows past m are zero in LDS, so whole 4-row blocks run
+                // without per-row branches; lanes past kb read chunk 0 and
+                // multiply a zero A chunk
 #pragma unroll
-                for (int j = 0; j < kTileRows; ++j) {
-                    if (j < m) {
+                for (int jb = 0; jb < kTileRows; jb += 4) {
+                    if (jb < m) {
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
                             const int k = kb0 + 64 * u + 8 * kl;
-                            if (k < kb) acc[j] = dot8(a[u], lds16(xs + j * kXS + (k - kc0)), acc[j]);
+                            const uint16_t *xp = xs + (k < kb ? k - kc0 : 0) + jb * kXS;
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) acc[jb + jj] = dot8(a[u], lds16(xp + jj * kXS), acc[jb + jj]);
                         }
                     }
                 }
             }
             // sum the 8 k lanes of each rank row; accumulate over x chunks in dst
 #pragma unroll
-            for (int j = 0; j < kTileRows; ++j) {
-                if (j < m) {
-                    float v = acc[j];
-                    v += __shfl_xor(v, 1);
-                    v += __shfl_xor(v, 2);
-                    v += __shfl_xor(v, 4);
-                    if (kl == 0) dst[rl * 16 + j] = (kc0 == k0 ? 0.f : dst[rl * 16 + j]) + v;
+            for (int jb = 0; jb < kTileRows; jb += 4) {
+                if (jb < m) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float v = group_sum(acc[jb + jj], 3);
+                        if (kl == 0 && jb + jj < m)
+                            dst[rl * 16 + jb + jj] = (kc0 == k0 ? 0.f : dst[rl * 16 + jb + jj]) + v;
+                    }
                 }
             }
         }
@@ -304,7 +338,7 @@ __device__ void shrink_valu(const Op &op, const UnitHdr &h, int rr0, int n_rr, i
 // Rank rows [rr0, rr0 + n_rr) of one tile over k in [k0, k1) into res
 // (n_rr <= kRRMfma on the MFMA path, <= kRRValu on the vector ALU).
 template <class Op>
-__device__ __forceinline__ void shrink_compute(const Op &op, const UnitHdr &h, bool mf, int rr0, int n_rr,
+__device__ __forceinline__ void shrink_compute(const Op &op, const Tile &h, bool mf, int rr0, int n_rr,
                                                int k0, int k1, float *res, float *red, uint16_t *xs) {
     if (mf)
         shrink_mfma(op, h, rr0, n_rr, k0, k1, res, red, xs);
@@ -350,7 +384,7 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_ca
 // xl[sl][j][0..R) = bf16(xa), xl[sl][j][R..2R) = bf16(xa - bf16(xa)) for the
 // tile rows j (zero past m) and xa slices sg_lo .. sg_lo + ns - 1.
 template <class Xa>
-__device__ void stage_xa(const UnitHdr &h, const Xa &xs, int sg_lo, int ns, int R, uint16_t *xl) {
+__device__ __forceinline__ void stage_xa(const Tile &h, const Xa &xs, int sg_lo, int ns, int R, uint16_t *xl) {
     const int total = ns * kTileRows * R;
     for (int base = 0; base < total; base += 4 * kBT) {
         float v[4];
@@ -374,158 +408,27 @@ __device__ void stage_xa(const UnitHdr &h, const Xa &xs, int sg_lo, int ns, int 
     }
 }
 
-// Vector-ALU expand of one unit: thread t owns columns c0 + 2t, c0 + 2t + 1 and
-// every row of the tile.  B and y are loaded before `wait` returns.
-template <class Op, class Xa, class Wait>
-__device__ void expand_valu(const Op &op, const UnitHdr &h, int c0, const Xa &xs, bool add_inputs,
-                            const Wait &wait, char *smem) {
-    const int R = op.R, m = h.m;
-    const int cend = min(c0 + kCW, op.n_out);
-    const int sg_lo = op.xslice(c0), ns = op.xslice(cend - 1) - sg_lo + 1;
-    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
-    const int c = c0 + 2 * threadIdx.x;
-    const bool cok = c < cend;
-    const int sl = cok ? op.xslice(c) - sg_lo : 0;
-    const uint16_t *b = cok ? op.brow(h.slot, c) : nullptr;  // rows c, c+1: 2R contiguous
-    u32x4_t bv[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        bv[q] = (cok && 8 * q < R) ? ld16_stream(b + 8 * q) : zero4();
-        bv[4 + q] = (cok && 8 * q < R) ? ld16_stream(b + R + 8 * q) : zero4();
-    }
-    uint32_t yv[kTileRows];
-#pragma unroll
-    for (int j = 0; j < kTileRows; ++j)
-        yv[j] = (cok && add_inputs && j < m) ? *reinterpret_cast<const uint32_t *>(op.yrow(h.rows[j]) + c) : 0u;
-    if (!wait()) return;
-    stage_xa(h, xs, sg_lo, ns, R, xl);
-    __syncthreads();
-    float a0[kTileRows], a1[kTileRows];
-#pragma unroll
-    for (int j = 0; j < kTileRows; ++j) a0[j] = a1[j] = 0.f;
-    for (int rb = 0; rb < R; rb += 32) {
-        if (rb > 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                bv[q] = (cok && rb + 8 * q < R) ? ld16_stream(b + rb + 8 * q) : zero4();
-                bv[4 + q] = (cok && rb + 8 * q < R) ? ld16_stream(b + R + rb + 8 * q) : zero4();
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kTileRows; ++j) {
-            if (j < m) {
-                const uint16_t *xr = xl + (sl * kTileRows + j) * 2 * R;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (rb + 8 * q < R) {
-                        const u32x4_t hv = lds16(xr + rb + 8 * q);
-                        const u32x4_t lv = lds16(xr + R + rb + 8 * q);
-                        a0[j] = dot8(bv[q], lv, dot8(bv[q], hv, a0[j]));
-                        a1[j] = dot8(bv[4 + q], lv, dot8(bv[4 + q], hv, a1[j]));
-                    }
-                }
-            }
-        }
-    }
-    if (!cok) return;
-#pragma unroll
-    for (int j = 0; j < kTileRows; ++j) {
-        if (j < m) {
-            float lo = a0[j], hi = a1[j];
-            if (add_inputs) {
-                lo += bf_lo(yv[j]);
-                hi += bf_hi(yv[j]);
-            }
-            *reinterpret_cast<uint32_t *>(op.yrow(h.rows[j]) + c) = pack_bf16x2(lo, hi);
-        }
-    }
-}
-
-// MFMA expand of one unit: D[column][tile row] = B[column][ranks] .
-// (xa_hi + xa_lo)[tile row][ranks] as two bf16 MFMAs per 32 ranks; wave w owns
-// columns c0 + 128w .. +128 (8 tiles of 16).  NRS = rank steps of 32.
-template <int NRS, class Op, class Xa, class Wait>
-__device__ void expand_mfma(const Op &op, const UnitHdr &h, int c0, const Xa &xs, bool add_inputs,
-                            const Wait &wait, char *smem) {
-    constexpr int CTB = 8 / NRS;  // column tiles whose B operands are in flight together (8 loads)
-    const int lane = lane_id(), w = wave_id();
-    const int R = op.R, R2 = 2 * R;
-    const int cend = min(c0 + kCW, op.n_out);
-    const int sg_lo = op.xslice(c0), ns = op.xslice(cend - 1) - sg_lo + 1;
-    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
-    const size_t xl_bytes = ((size_t)ns * kTileRows * R2 * 2 + 15) & ~(size_t)15;
-    float *ol = reinterpret_cast<float *>(smem + xl_bytes) + w * (kTileRows * kOutStride);
-    const int cw0 = c0 + 128 * w;
-    const int col_l = lane & 15, kk = (lane >> 4) * 8;
-
-    u32x4_t bo[CTB][NRS];
-    // B operands of column tiles ct0 .. ct0+CTB-1; rows of columns outside
-    // xa slice `only` (when >= 0) are zeroed
-    auto load_b = [&](int ct0, int only) {
-#pragma unroll
-        for (int i = 0; i < CTB; ++i) {
-            const int c = cw0 + 16 * (ct0 + i) + col_l;
-            const bool cok = c < cend && (only < 0 || op.xslice(c) == only);
-            const uint16_t *b = cok ? op.brow(h.slot, c) : nullptr;
-#pragma unroll
-            for (int s = 0; s < NRS; ++s) {
-                const int rk = 32 * s + kk;
-                bo[i][s] = (cok && rk < R) ? ld16_stream(b + rk) : zero4();
-            }
-        }
-    };
-    load_b(0, -1);
-    // y for the epilogue: rows 4p + lane/16, columns cw0 + 8*(lane%16)
+// y of the 16 x 128 output tile of wave w: lane reads rows 4p + lane/16 (p < 4),
+// columns cw0 + 8*(lane%16) .. +8, as 16-byte loads (issued early).
+template <class Op>
+__device__ __forceinline__ void prefetch_y(const Op &op, const Tile &h, int cw0, int cend, bool add_inputs,
+                                           u32x4_t (&yv)[4]) {
+    const int lane = lane_id();
     const int cy = cw0 + 8 * (lane & 15);
-    u32x4_t yv[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int j = 4 * p + (lane >> 4);
         yv[p] = (add_inputs && j < h.m && cy < cend) ? ld16(op.yrow(h.rows[j]) + cy) : zero4();
     }
-    if (!wait()) return;
-    stage_xa(h, xs, sg_lo, ns, R, xl);
-    __syncthreads();
+}
 
-    f32x4_t d[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int sg_w0 = op.xslice(min(cw0, cend - 1)), sg_w1 = op.xslice(min(cw0 + 127, cend - 1));
-    const bool straddle = sg_w0 != sg_w1;
-    // one pass per xa slice under this wave's columns (almost always one);
-    // when they straddle a slice boundary each pass masks the other slice's rows
-    for (int sg = sg_w0; cw0 < cend && sg <= sg_w1; ++sg) {
-        const uint16_t *xr = xl + ((sg - sg_lo) * kTileRows + col_l) * R2;  // MFMA-B column = tile row
-        u32x4_t hv[NRS], lv[NRS];
-#pragma unroll
-        for (int s = 0; s < NRS; ++s) {
-            const int rk = 32 * s + kk;
-            hv[s] = rk < R ? lds16(xr + rk) : zero4();
-            lv[s] = rk < R ? lds16(xr + R + rk) : zero4();
-        }
-#pragma unroll
-        for (int cb = 0; cb < 8; cb += CTB) {
-            if (cb > 0 || straddle) load_b(cb, straddle ? sg : -1);
-#pragma unroll
-            for (int i = 0; i < CTB; ++i) {
-#pragma unroll
-                for (int s = 0; s < NRS; ++s) {
-                    d[cb + i] = mfma_16x16x32(bo[i][s], hv[s], d[cb + i]);
-                    d[cb + i] = mfma_16x16x32(bo[i][s], lv[s], d[cb + i]);
-                }
-            }
-        }
-    }
-    // lane holds D[column cw0 + 16ct + 4*(lane>>4) + q][tile row lane & 15]
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        float *o = ol + col_l * kOutStride + 16 * ct + 4 * (lane >> 4);
-        o[0] = d[ct][0];
-        o[1] = d[ct][1];
-        o[2] = d[ct][2];
-        o[3] = d[ct][3];
-    }
-    __syncthreads();
+// y[row j][cw0 + c] = (add_inputs ? y : 0) + ol[j][c], rounded once to bf16, for
+// the wave's 16 x 128 tile held in LDS (fp32, row stride kOutStride).
+template <class Op>
+__device__ __forceinline__ void store_tile(const Op &op, const Tile &h, const float *ol, int cw0, int cend,
+                                           bool add_inputs, const u32x4_t (&yv)[4]) {
+    const int lane = lane_id();
+    const int cy = cw0 + 8 * (lane & 15);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int j = 4 * p + (lane >> 4);
@@ -551,8 +454,193 @@ __device__ void expand_mfma(const Op &op, const UnitHdr &h, int c0, const Xa &xs
     }
 }
 
+// B chunks of instructions i0 .. i0+7 of a wave's vector-ALU expand.
+template <class Op>
+__device__ __forceinline__ void valu_load_b(const Op &op, const Tile &h, u32x4_t (&bv)[8], int i0, int cw0,
+                                            int cpi, int lg, int n_ins, int cend, int q, int nq) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = cw0 + (i0 + i) * cpi + (lane >> lg);
+        const bool ok = i0 + i < n_ins && c < cend && q < nq;
+        bv[i] = ok ? ld16(op.brow(h.slot, c) + 8 * q) : zero4();
+    }
+}
+
+// Vector-ALU expand of one unit.  Each B row (one output column, R ranks)
+// is split over 2^lg lanes holding 8 ranks each, so every load instruction of
+// a wave reads 1 KB of consecutive B rows; the per-lane partial dots are
+// summed over those lanes with xor shuffles and land in the wave's 16 x 128
+// fp32 tile in LDS, which is added to y with 16-byte accesses.  Wave w owns
+// columns c0 + 128w .. +128, in n_ins = 128 / (64 >> lg) load instructions.
+template <class Op, class Xa, class Wait>
+__device__ __forceinline__ void expand_valu(const Op &op, const Tile &h, int c0, const Xa &xs, bool add_inputs,
+                                            const Wait &wait, char *smem) {
+    const int lane = lane_id(), w = wave_id();
+    const int R = op.R, m = h.m;
+    const int cend = min(c0 + kCW, op.n_out);
+    const int sg_lo = op.xslice(c0), ns = op.xslice(cend - 1) - sg_lo + 1;
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
+    const size_t xl_bytes = ((size_t)ns * kTileRows * 2 * R * 2 + 15) & ~(size_t)15;
+    float *ol = reinterpret_cast<float *>(smem + xl_bytes) + w * (kTileRows * kOutStride);
+    const int nq = R >> 3;  // 16-byte chunks per B row
+    int lg = 0;
+    while ((1 << lg) < nq) ++lg;
+    const int q = lane & ((1 << lg) - 1);
+    const int cpi = 64 >> lg;         // columns per instruction
+    const int n_ins = 128 / cpi;      // 2 .. 32
+    const int cw0 = c0 + 128 * w;
+    const int sg_w0 = op.xslice(min(cw0, cend - 1)), sg_w1 = op.xslice(min(cw0 + 127, cend - 1));
+    const bool straddle = sg_w0 != sg_w1;
+    u32x4_t bv[8];
+    valu_load_b(op, h, bv, 0, cw0, cpi, lg, n_ins, cend, q, nq);
+    u32x4_t yv[4];
+    prefetch_y(op, h, cw0, cend, add_inputs, yv);
+    if (!wait()) return;
+    stage_xa(h, xs, sg_lo, ns, R, xl);
+    __syncthreads();
+    for (int i0 = 0; i0 < n_ins; i0 += 8) {
+        if (i0 > 0) valu_load_b(op, h, bv, i0, cw0, cpi, lg, n_ins, cend, q, nq);
+        if (!straddle) {
+            // one xa slice under the wave's columns: each xa row chunk is read
+            // once and multiplies all 8 B chunks; xa rows past m are zero in
+            // LDS, so 4-row blocks run without per-row branches
+            const uint16_t *xr = xl + (sg_w0 - sg_lo) * kTileRows * 2 * R + 8 * (q < nq ? q : 0);
+#pragma unroll
+            for (int jb = 0; jb < kTileRows; jb += 4) {
+                if (jb < m) {
+                    u32x4_t hv[4], lv[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        hv[jj] = lds16(xr + (jb + jj) * 2 * R);
+                        lv[jj] = lds16(xr + (jb + jj) * 2 * R + R);
+                    }
+                    float v[8][4];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            v[i][jj] = group_sum(dot8(bv[i], lv[jj], dot8(bv[i], hv[jj], 0.f)), lg);
+                    if (q == 0) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int cl = (i0 + i) * cpi + (lane >> lg);
+                            if (i0 + i < n_ins)
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj) ol[(jb + jj) * kOutStride + cl] = v[i][jj];
+                        }
+                    }
+                }
+            }
+        } else {
+            // columns straddle a slice boundary: per-instruction slice lookup
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int cl = (i0 + i) * cpi + (lane >> lg);
+                const int c = cw0 + cl;
+                const int sg = c < cend ? op.xslice(c) : sg_lo;
+                const uint16_t *xr = xl + (sg - sg_lo) * kTileRows * 2 * R + 8 * (q < nq ? q : 0);
+                for (int j = 0; j < m; ++j) {
+                    const float v = group_sum(
+                        dot8(bv[i], lds16(xr + j * 2 * R + R), dot8(bv[i], lds16(xr + j * 2 * R), 0.f)), lg);
+                    if (q == 0 && i0 + i < n_ins) ol[j * kOutStride + cl] = v;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    store_tile(op, h, ol, cw0, cend, add_inputs, yv);
+}
+
+// B operands of column tiles ct0 .. ct0+CTB-1 of a wave's MFMA expand; rows
+// of columns outside xa slice `only` (when >= 0) are zeroed.
+template <int NRS, int CTB, class Op>
+__device__ __forceinline__ void mfma_load_b(const Op &op, const Tile &h, u32x4_t (&bo)[CTB][NRS], int ct0,
+                                            int only, int cw0, int cend, int R) {
+    const int lane = lane_id();
+    const int col_l = lane & 15, kk = (lane >> 4) * 8;
+#pragma unroll
+    for (int i = 0; i < CTB; ++i) {
+        const int c = cw0 + 16 * (ct0 + i) + col_l;
+        const bool cok = c < cend && (only < 0 || op.xslice(c) == only);
+        const uint16_t *b = cok ? op.brow(h.slot, c) : nullptr;
+#pragma unroll
+        for (int s = 0; s < NRS; ++s) {
+            const int rk = 32 * s + kk;
+            bo[i][s] = (cok && rk < R) ? ld16(b + rk) : zero4();
+        }
+    }
+}
+
+// MFMA expand of one unit: D[column][tile row] = B[column][ranks] .
+// (xa_hi + xa_lo)[tile row][ranks] as two bf16 MFMAs per 32 ranks; wave w owns
+// columns c0 + 128w .. +128 (8 tiles of 16).  NRS = rank steps of 32.
 template <int NRS, class Op, class Xa, class Wait>
-__device__ __forceinline__ void expand_unit(const Op &op, const UnitHdr &h, bool mf, int c0, const Xa &xs,
+__device__ __forceinline__ void expand_mfma(const Op &op, const Tile &h, int c0, const Xa &xs, bool add_inputs,
+                            const Wait &wait, char *smem) {
+    constexpr int CTB = 8 / NRS;  // column tiles whose B operands are in flight together (8 loads)
+    const int lane = lane_id(), w = wave_id();
+    const int R = op.R, R2 = 2 * R;
+    const int cend = min(c0 + kCW, op.n_out);
+    const int sg_lo = op.xslice(c0), ns = op.xslice(cend - 1) - sg_lo + 1;
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
+    const size_t xl_bytes = ((size_t)ns * kTileRows * R2 * 2 + 15) & ~(size_t)15;
+    float *ol = reinterpret_cast<float *>(smem + xl_bytes) + w * (kTileRows * kOutStride);
+    const int cw0 = c0 + 128 * w;
+    const int col_l = lane & 15, kk = (lane >> 4) * 8;
+
+    u32x4_t bo[CTB][NRS];
+    mfma_load_b<NRS, CTB>(op, h, bo, 0, -1, cw0, cend, R);
+    u32x4_t yv[4];
+    prefetch_y(op, h, cw0, cend, add_inputs, yv);
+    if (!wait()) return;
+    stage_xa(h, xs, sg_lo, ns, R, xl);
+    __syncthreads();
+
+    f32x4_t d[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int sg_w0 = op.xslice(min(cw0, cend - 1)), sg_w1 = op.xslice(min(cw0 + 127, cend - 1));
+    const bool straddle = sg_w0 != sg_w1;
+    // one pass per xa slice under this wave's columns (almost always one);
+    // when they straddle a slice boundary each pass masks the other slice's rows
+    for (int sg = sg_w0; cw0 < cend && sg <= sg_w1; ++sg) {
+        const uint16_t *xr = xl + ((sg - sg_lo) * kTileRows + col_l) * R2;  // MFMA-B column = tile row
+        u32x4_t hv[NRS], lv[NRS];
+#pragma unroll
+        for (int s = 0; s < NRS; ++s) {
+            const int rk = 32 * s + kk;
+            hv[s] = rk < R ? lds16(xr + rk) : zero4();
+            lv[s] = rk < R ? lds16(xr + R + rk) : zero4();
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; cb += CTB) {
+            if (cb > 0 || straddle) mfma_load_b<NRS, CTB>(op, h, bo, cb, straddle ? sg : -1, cw0, cend, R);
+#pragma unroll
+            for (int i = 0; i < CTB; ++i) {
+#pragma unroll
+                for (int s = 0; s < NRS; ++s) {
+                    d[cb + i] = mfma_16x16x32(bo[i][s], hv[s], d[cb + i]);
+                    d[cb + i] = mfma_16x16x32(bo[i][s], lv[s], d[cb + i]);
+                }
+            }
+        }
+    }
+    // lane holds D[column cw0 + 16ct + 4*(lane>>4) + q][tile row lane & 15]
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        float *o = ol + col_l * kOutStride + 16 * ct + 4 * (lane >> 4);
+        o[0] = d[ct][0];
+        o[1] = d[ct][1];
+        o[2] = d[ct][2];
+        o[3] = d[ct][3];
+    }
+    __syncthreads();
+    store_tile(op, h, ol, cw0, cend, add_inputs, yv);
+}
+
+template <int NRS, class Op, class Xa, class Wait>
+__device__ __forceinline__ void expand_unit(const Op &op, const Tile &h, bool mf, int c0, const Xa &xs,
                                             bool add_inputs, const Wait &wait, char *smem) {
     if (mf)
         expand_mfma<NRS>(op, h, c0, xs, add_inputs, wait, smem);
@@ -564,10 +652,11 @@ __device__ __forceinline__ void expand_unit(const Op &op, const UnitHdr &h, bool
 template <class Op>
 __global__ __launch_bounds__(kBT) void shrink_kernel(Op op, const int32_t *tiles, float *xa, int n, int mfma_min) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ UnitHdr h;
+    __shared__ TileLds tl_sh;
+    Tile h;
     const int n_sl = op.n_sh;
     const int t = blockIdx.x / n_sl, sl = blockIdx.x % n_sl;
-    if (!load_tile(op, tiles, t, h)) return;
+    if (!load_tile(op, tiles, t, tl_sh, h)) return;
     const bool mf = h.mseg >= mfma_min;
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
     float *res = reinterpret_cast<float *>(smem + kXsBytes);
@@ -590,9 +679,10 @@ template <int NRS, class Op>
 __global__ __launch_bounds__(kBT) void expand_kernel(Op op, const int32_t *tiles, const float *xa, int n, int C,
                                                      int add_inputs, int mfma_min) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ UnitHdr h;
+    __shared__ TileLds tl_sh;
+    Tile h;
     const int t = blockIdx.x / C, cc = blockIdx.x % C;
-    if (!load_tile(op, tiles, t, h)) return;
+    if (!load_tile(op, tiles, t, tl_sh, h)) return;
     const bool mf = h.mseg >= mfma_min;
     expand_unit<NRS>(op, h, mf, cc * kCW, XaDirect{xa, n, op.R}, add_inputs != 0, NoWait{}, smem);
 }
@@ -608,30 +698,30 @@ struct ZeroFill {  // MoE: rows of pairs without a valid (adapter, expert) are z
 struct TileWait {
     int *ctl, *ctr, *done;
     int t, P, C;
-    UnitHdr *h;
+    int *flag;  // LDS
     __device__ bool operator()() const {
         if (threadIdx.x == 0) {
             // poll without acquire semantics (an acquire load would invalidate
             // the L2 on every poll), then acquire once
             int spins = 0;
-            while (load_relaxed(&ctr[t]) < P) {
+            while (load_relaxed(&ctr[t * kCtrStride]) < P) {
                 __builtin_amdgcn_s_sleep(1);
                 if (++spins > kSpinLimit) {
                     atomicExch(&ctl[0], 1);
-                    h->flag = 1;
+                    *flag = 1;
                     break;
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (!h->flag && atomicAdd(&done[t], 1) == C - 1) {
-                store_relaxed(&ctr[t], 0);
-                store_relaxed(&done[t], 0);
+            if (*flag == 0 && atomicAdd(&done[t * kCtrStride], 1) == C - 1) {
+                store_relaxed(&ctr[t * kCtrStride], 0);
+                store_relaxed(&done[t * kCtrStride], 0);
             }
         }
         // thread 0's agent-scope acquire is ordered before the other threads'
         // loads of the partials by the workgroup barrier
         __syncthreads();
-        return h->flag == 0;
+        return __builtin_amdgcn_readfirstlane(*flag) == 0;
     }
 };
 
@@ -640,14 +730,15 @@ __global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles,
                                                     int n_pos, float *part, int *ctl, int *ctr, int *done,
                                                     int mfma_min, int add_inputs, ZeroFill zf) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ UnitHdr h;
+    __shared__ TileLds tl_sh;
+    Tile h;
     const int tid = threadIdx.x;
     const int bid = blockIdx.x;
     const int n_shr = tile_bound * P, n_exp = tile_bound * C;
     const int n_rr = op.n_sh * op.R;
     if (bid < n_shr) {
         const int t = bid / P, p = bid % P;
-        if (!load_tile(op, tiles, t, h)) return;
+        if (!load_tile(op, tiles, t, tl_sh, h)) return;
         const bool mf = h.mseg >= mfma_min;
         const int KP = (((op.k_in + P - 1) / P + 63) / 64) * 64;
         const int k0 = min(op.k_in, p * KP), k1 = min(op.k_in, k0 + KP);
@@ -666,16 +757,16 @@ __global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles,
         }
         // every thread's partial stores are ordered before thread 0's
         // agent-scope release by the workgroup barrier above
-        if (tid == 0) atomic_add_release(&ctr[t], 1);
+        if (tid == 0) atomic_add_release(&ctr[t * kCtrStride], 1);
         return;
     }
     if (bid < n_shr + n_exp) {
         const int e = bid - n_shr;
         const int t = e / C, cc = e % C;
-        if (!load_tile(op, tiles, t, h)) return;
+        if (!load_tile(op, tiles, t, tl_sh, h)) return;
         const bool mf = h.mseg >= mfma_min;
         expand_unit<NRS>(op, h, mf, cc * kCW, XaPartials{part, P, n_rr, op.R, op.scale_of(h.slot)},
-                         add_inputs != 0, TileWait{ctl, ctr, done, t, P, C, &h}, smem);
+                         add_inputs != 0, TileWait{ctl, ctr, done, t, P, C, &tl_sh.flag}, smem);
         return;
     }
     // zero rows of pairs that get no delta (MoE only)
@@ -718,7 +809,7 @@ FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out)
            p.P * 2 <= kMaxPieces)
         p.P *= 2;
     p.C = (n_out + kCW - 1) / kCW;
-    p.ctr_bytes = align_up(64 + (size_t)2 * p.tile_bound * sizeof(int), 256);
+    p.ctr_bytes = align_up(256 + (size_t)p.tile_bound * kCtrStride * sizeof(int), 256);
     p.part_bytes = align_up((size_t)p.P * n * n_sh * R * sizeof(float), 256);
     p.total_bytes = p.ctr_bytes + p.part_bytes;
     return p;
@@ -788,8 +879,8 @@ static hipError_t launch_fused_nrs(const Op &op, int n_pos, int n_xa_slices, con
                                    int zero_units, hipStream_t st) {
     char *w = static_cast<char *>(ws);
     int *ctl = reinterpret_cast<int *>(w);
-    int *ctr = ctl + 16;
-    int *done = ctr + plan.tile_bound;
+    int *ctr = ctl + 64;
+    int *done = ctr + 1;  // same line as the tile counter
     float *part = reinterpret_cast<float *>(w + plan.ctr_bytes);
     const size_t lds = std::max(shrink_lds(), expand_lds(n_xa_slices, op.R));
     allow_lds(fused_kernel<NRS, Op>, lds);
