@@ -19,10 +19,17 @@ eager launches; it gives the roofline fraction against 8 TB/s.  The fp64 CPU
 oracle is timed on the same batch on the host cores (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --calibrate-copy   # a plain 512 MiB device copy, for counter scaling
+
+HBM traffic of the fused kernel (roofline.traffic) comes from rocprofv3
+FETCH_SIZE / WRITE_SIZE runs recorded in profiles/fused_decode_traffic.txt,
+scaled by what the same counters read for the plain copy; it is reported only
+while the kernel sources still hash to the recorded value, else null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +41,42 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "effective HBM GB/s and tokens/sec of routed LoRA delta (% of peak), 1 MI355X"
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_traffic.txt")
+KERNEL_SOURCES = ["common.h", "kernels.h", "delta.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tenant_lora_serving_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(bytes_step: int):
+    """HBM bytes per fused launch from the recorded counter runs, or None when
+    missing or taken on other kernel sources."""
+    try:
+        kv = dict(ln.strip().split("=", 1) for ln in open(TRAFFIC_FILE) if "=" in ln and not ln.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def calibrate_copy():
+    import torch
+    torch.cuda.set_device(0)
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "reps": 3}), flush=True)
 
 
 def algorithmic_bytes(case) -> int:
@@ -71,7 +114,11 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="independent input copies (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the routed LoRA delta on a single "
               "MI355X (no multi-GPU path); run it with --gpus 1.", file=sys.stderr)
@@ -151,6 +198,7 @@ def main():
 
     value = bytes_step * K / wall / 1e9
     fused_gbs = bytes_step / (fused_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(bytes_step)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -168,11 +216,12 @@ def main():
                    "k_in": case.k_in, "slices": list(case.slice_sizes), "num_slots": case.num_slots,
                    "max_rank": case.max_rank, "active_rows": int(act.sum()),
                    "active_slots": int(len(np.unique(case.slot[act]))),
-                   "bytes_per_step": bytes_step, "input_copies": copies},
+                   "bytes_per_step": bytes_step, "input_copies": copies,
+                   "mfma_min_rows": B.mfma_min_rows(), "kernel_sources": kernel_source_hash()},
         "tokens_per_s": round(case.n * K / wall, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "fused_kernel<DenseOp>", "kernel_us": round(fused_ms * 1e3, 3)},
         "meta_kernel_us": round(meta_ms * 1e3, 3),
     }
