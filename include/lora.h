@@ -25,9 +25,12 @@
  *    besides the MFMA row threshold (lora_set_mfma_min_rows).
  *  - Every check that can run on the host runs before any launch and
  *    returns an error code; nothing is enqueued then.
- *  - Workspaces hold counters that must be zero before their first use
- *    (allocate them zero-filled); every call leaves them zero again.
- *    Calls that share a workspace must be ordered (same stream).
+ *  - Workspaces must be zero-filled before their first use.  The meta
+ *    workspace's counters return to zero after every call; the fused and
+ *    MoE workspaces keep a count of the calls completed on them (a control
+ *    word at a library-defined offset), which tags the partial results of
+ *    the next call, and stay valid for calls of any shape that fits them.  Calls that share a
+ *    workspace must be ordered (same stream).
  *
  * Layouts (metrale docs, LoraPair and LoraRoute; the slices follow vLLM's
  * add_shrink / add_expand, one A and one block of B rows per output slice):

@@ -199,7 +199,7 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, co
     d.ldy = ldy;
     d.offset_start = offset_start;
     return launched(
-        tl::launch_fused(d, meta.tiles, plan, ws, mfma_min_rows(), static_cast<hipStream_t>(stream)));
+        tl::launch_fused(d, meta.tiles, meta.counts, plan, ws, mfma_min_rows(), static_cast<hipStream_t>(stream)));
 }
 
 // MoE workspace: [counts 8 | sorted_rows n | seg_offsets cap+1 | seg_slot cap | tiles] [meta ws] [fused ws]
@@ -270,7 +270,7 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
     if (n == 0) return LORA_OK;
     tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
                    lora_ids, num_experts, num_loras, rank, inter, scale, out};
-    return launched(tl::launch_moe_delta(m, mo.tiles, lay.plan, b + lay.fused, mfma_min_rows(), st));
+    return launched(tl::launch_moe_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused, mfma_min_rows(), st));
 }
 
 int32_t lora_mfma_min_rows(void) { return mfma_min_rows(); }

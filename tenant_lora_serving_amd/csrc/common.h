@@ -64,6 +64,7 @@ __device__ __forceinline__ u32x4_t ld16(const void *p) {
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 __device__ __forceinline__ void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 // Streamed once: keep it out of the caches' way.
 __device__ __forceinline__ u32x4_t ld16_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
@@ -176,6 +177,21 @@ __device__ __forceinline__ int load_relaxed(const int *p) {
 }
 __device__ __forceinline__ void store_relaxed(int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int atomic_add_relaxed(int *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 64-bit words read and written as single atomic units: a value with the
+// tag of the call that wrote it travels in one word, so a reader that sees
+// the tag also sees the value, with no fence on either side.
+__device__ __forceinline__ void store_word64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_word64(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
+    return ((uint64_t)tag << 32) | __float_as_uint(v);
 }
 
 }  // namespace tl

@@ -1,15 +1,15 @@
-// delta.hip -- shrink, expand and fused routed LoRA delta for gfx950.
+// delta.hip -- standalone shrink and expand kernels (lora_shrink,
+// lora_expand) for gfx950.  The one-launch fused delta lives in fused.hip.
 //
-// Semantics (vLLM punica_base.py, add_shrink / add_expand / add_lora_linear;
-// metrale lora_delta docs, apply_lora_bgmv and LoraPair; FlashInfer
-// bgmv_moe_gemm1_lora_delta): rows of one adapter slot form a segment; the
-// shrink gives xa = scale * x @ A^T in fp32, the expand adds xa @ B^T to the
-// output window and rounds once to bf16.
+// Semantics (vLLM punica_base.py, add_shrink / add_expand; metrale
+// lora_delta docs, apply_lora_bgmv and LoraPair): rows of one adapter slot
+// form a segment; the shrink gives xa = scale * x @ A^T in fp32, the expand
+// adds xa @ B^T to the output window and rounds once to bf16.
 //
 // Work units.  The metadata cuts every segment into tiles of at most 16 rows
 // (one 128-byte record each: slot, first sorted position, row count, segment
 // size, row ids).  A workgroup (4 waves) takes one unit:
-//   shrink unit  (tile, k piece): every rank row of the adapter over a k range
+//   shrink unit  (tile, shrink slice): every rank row of the slice over all of k
 //   expand unit  (tile, 512-column chunk): every row of the tile
 // Segments with at least `mfma_min` rows (16 by default) run on
 // v_mfma_f32_16x16x32_bf16; shorter ones on the vector ALU with
@@ -17,16 +17,9 @@
 // expand keeps xa's precision by splitting it into two bf16 terms
 // (hi = bf16(xa), lo = bf16(xa - hi)) that both multiply B, so no bf16
 // rounding of xa reaches the result beyond ~2^-16 relative.
-//
-// The fused kernel runs all shrink units (lower workgroup ids) and all expand
-// units in one launch.  A shrink unit stores an fp32 partial for its k piece
-// and bumps its tile's counter (agent-scope release); an expand unit waits on
-// that counter (agent-scope acquire) and sums the P partials in a fixed
-// order, so results are bitwise reproducible.  Workgroups are dispatched in
-// id order, so every awaited shrink unit is already running or done; the wait
-// is bounded anyway and reports a flag instead of hanging.
 #include "common.h"
 #include "kernels.h"
+#include "ops.h"
 
 #include <algorithm>
 
@@ -39,77 +32,8 @@ constexpr int kRRValu = 64;     // shrink rank rows per pass on the vector ALU
 constexpr int kKC = 512;        // x columns staged in LDS per pass
 constexpr int kXS = kKC + 8;    // padded LDS row stride (elements) of the staged x tile
 constexpr int kXsBytes = kTileRows * kXS * 2;
-constexpr int kMaxPieces = 16;  // k pieces of the fused shrink
 constexpr int kRedStride = 48 * 16;  // per-wave partial block when waves split k
 constexpr int kOutStride = 132;      // padded fp32 row stride of the MFMA output tile
-constexpr int kSpinLimit = 1 << 24;
-constexpr int kCtrStride = 64;  // ints between tile counters: one 256-byte line each, so
-                                // pollers and publishers of different tiles never share a line
-
-// ============================================================ addressing
-struct DenseOp {
-    const uint16_t *x;
-    int64_t ldx;
-    const uint16_t *a_pool;
-    const uint16_t *b_pool;
-    const float *scale;
-    uint16_t *y;
-    int64_t ldy;
-    int k_in, R, n_sh, n_out, col0, n_sl;
-    int off[kMaxSlices + 1];
-
-    __device__ const uint16_t *xrow(int row) const { return x + (int64_t)row * ldx; }
-    // rank row rr = l*R + r of slot s: a_pool[s][l][r][:]
-    __device__ const uint16_t *arow(int slot, int rr) const {
-        return a_pool + ((int64_t)slot * n_sh * R + rr) * k_in;
-    }
-    // slice of output column c; unrolled so off[] is only read at constant
-    // indices (a runtime index would move the kernel argument to scratch)
-    __device__ int xslice(int c) const {
-        int l = 0;
-#pragma unroll
-        for (int i = 1; i < kMaxSlices; ++i) l += (i < n_sl && c >= off[i]) ? 1 : 0;
-        return l;
-    }
-    __device__ const uint16_t *brow(int slot, int c) const {
-        return b_pool + ((int64_t)slot * n_out + c) * R;
-    }
-    __device__ uint16_t *yrow(int row) const { return y + (int64_t)row * ldy + col0; }
-    __device__ float scale_of(int slot) const { return scale[slot]; }
-};
-
-// Routed MoE gemm1: key = l*E + e, rows are (token, slot) pairs.
-struct MoeOp {
-    const uint16_t *x;
-    int64_t ldx;
-    int top_k;
-    const int64_t *wa;
-    int64_t lsa;
-    const int64_t *wb;
-    int64_t lsb;
-    uint16_t *out;
-    float sc;
-    int k_in, R, n_sh, n_out, E, inter, shared;
-
-    __device__ const uint16_t *xrow(int pair) const { return x + (int64_t)(pair / top_k) * ldx; }
-    __device__ const uint16_t *arow(int key, int rr) const {
-        const int l = key / E, e = key - l * E;
-        const int sg = rr / R, r = rr - sg * R;
-        const uint16_t *base = reinterpret_cast<const uint16_t *>(wa[shared ? e : sg * E + e]);
-        return base + (int64_t)l * lsa + (int64_t)r * k_in;
-    }
-    __device__ int xslice(int c) const { return shared ? 0 : (c >= inter ? 1 : 0); }
-    __device__ const uint16_t *brow(int key, int c) const {
-        const int l = key / E, e = key - l * E;
-        if (shared)
-            return reinterpret_cast<const uint16_t *>(wb[e]) + (int64_t)l * lsb + (int64_t)c * R;
-        const int sg = c >= inter ? 1 : 0;
-        return reinterpret_cast<const uint16_t *>(wb[sg * E + e]) + (int64_t)l * lsb +
-               (int64_t)(c - sg * inter) * R;
-    }
-    __device__ uint16_t *yrow(int pair) const { return out + (int64_t)pair * n_out; }
-    __device__ float scale_of(int) const { return sc; }
-};
 
 // ============================================================ tile header
 // The scalar fields of a tile record live in SGPRs (read through
@@ -151,7 +75,6 @@ __device__ __forceinline__ bool load_tile(const Op &op, const int32_t *tiles, in
     return true;
 }
 
-__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 
 // How the 4 waves share a unit: GW waves split the rank-row groups, KW = 4/GW
@@ -353,28 +276,6 @@ struct XaDirect {  // caller's xa[slice][n][R], already scaled
     int n, R;
     __device__ float get(int sg, int row, int, int r) const { return xa[((int64_t)sg * n + row) * R + r]; }
 };
-struct XaPartials {  // fused workspace part[pos][n_rr][P] (P a power of two <= 16), scaled here
-    const float *part;
-    int P, n_rr, R;
-    float scale;
-    __device__ float get(int sg, int, int pos, int r) const {
-        const float *q = part + ((int64_t)pos * n_rr + sg * R + r) * P;
-        float s = 0.f;
-        if (P >= 4) {
-            for (int c = 0; c < P; c += 4) {
-                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(q + c);
-                s += v[0];
-                s += v[1];
-                s += v[2];
-                s += v[3];
-            }
-        } else {
-            for (int c = 0; c < P; ++c) s += q[c];
-        }
-        return scale * s;
-    }
-};
-
 struct NoWait {
     __device__ bool operator()() const { return true; }
 };
@@ -687,98 +588,6 @@ __global__ __launch_bounds__(kBT) void expand_kernel(Op op, const int32_t *tiles
     expand_unit<NRS>(op, h, mf, cc * kCW, XaDirect{xa, n, op.R}, add_inputs != 0, NoWait{}, smem);
 }
 
-struct ZeroFill {  // MoE: rows of pairs without a valid (adapter, expert) are zeroed
-    const int32_t *topk;
-    const int32_t *lora;
-    int top_k, E, L, n_pairs;
-};
-
-// Expand-unit wait of the fused kernel: thread 0 polls the tile's counter
-// until all P shrink pieces have been published, then acquires once.
-struct TileWait {
-    int *ctl, *ctr, *done;
-    int t, P, C;
-    int *flag;  // LDS
-    __device__ bool operator()() const {
-        if (threadIdx.x == 0) {
-            // poll without acquire semantics (an acquire load would invalidate
-            // the L2 on every poll), then acquire once
-            int spins = 0;
-            while (load_relaxed(&ctr[t * kCtrStride]) < P) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) {
-                    atomicExch(&ctl[0], 1);
-                    *flag = 1;
-                    break;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (*flag == 0 && atomicAdd(&done[t * kCtrStride], 1) == C - 1) {
-                store_relaxed(&ctr[t * kCtrStride], 0);
-                store_relaxed(&done[t * kCtrStride], 0);
-            }
-        }
-        // thread 0's agent-scope acquire is ordered before the other threads'
-        // loads of the partials by the workgroup barrier
-        __syncthreads();
-        return __builtin_amdgcn_readfirstlane(*flag) == 0;
-    }
-};
-
-template <int NRS, class Op>
-__global__ __launch_bounds__(kBT) void fused_kernel(Op op, const int32_t *tiles, int tile_bound, int P, int C,
-                                                    int n_pos, float *part, int *ctl, int *ctr, int *done,
-                                                    int mfma_min, int add_inputs, ZeroFill zf) {
-    extern __shared__ __align__(16) char smem[];
-    __shared__ TileLds tl_sh;
-    Tile h;
-    const int tid = threadIdx.x;
-    const int bid = blockIdx.x;
-    const int n_shr = tile_bound * P, n_exp = tile_bound * C;
-    const int n_rr = op.n_sh * op.R;
-    if (bid < n_shr) {
-        const int t = bid / P, p = bid % P;
-        if (!load_tile(op, tiles, t, tl_sh, h)) return;
-        const bool mf = h.mseg >= mfma_min;
-        const int KP = (((op.k_in + P - 1) / P + 63) / 64) * 64;
-        const int k0 = min(op.k_in, p * KP), k1 = min(op.k_in, k0 + KP);
-        uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-        float *res = reinterpret_cast<float *>(smem + kXsBytes);
-        float *red = res + kRRMfma * 16;
-        const int chunk = mf ? kRRMfma : kRRValu;
-        for (int rr0 = 0; rr0 < n_rr; rr0 += chunk) {
-            const int cnt = min(chunk, n_rr - rr0);
-            shrink_compute(op, h, mf, rr0, cnt, k0, k1, res, red, xs);
-            for (int idx = tid; idx < h.m * cnt; idx += kBT) {
-                const int j = idx / cnt, rl = idx % cnt;
-                part[((int64_t)(h.pos0 + j) * n_rr + rr0 + rl) * P + p] = res[rl * 16 + j];
-            }
-            __syncthreads();
-        }
-        // every thread's partial stores are ordered before thread 0's
-        // agent-scope release by the workgroup barrier above
-        if (tid == 0) atomic_add_release(&ctr[t * kCtrStride], 1);
-        return;
-    }
-    if (bid < n_shr + n_exp) {
-        const int e = bid - n_shr;
-        const int t = e / C, cc = e % C;
-        if (!load_tile(op, tiles, t, tl_sh, h)) return;
-        const bool mf = h.mseg >= mfma_min;
-        expand_unit<NRS>(op, h, mf, cc * kCW, XaPartials{part, P, n_rr, op.R, op.scale_of(h.slot)},
-                         add_inputs != 0, TileWait{ctl, ctr, done, t, P, C, &tl_sh.flag}, smem);
-        return;
-    }
-    // zero rows of pairs that get no delta (MoE only)
-    const int u = bid - n_shr - n_exp;
-    const int pair = u * 16 + (tid >> 4);
-    if (pair >= zf.n_pairs) return;
-    const int l = zf.lora[pair / zf.top_k], ex = zf.topk[pair];
-    if (l >= 0 && l < zf.L && ex >= 0 && ex < zf.E) return;
-    uint16_t *o = op.yrow(pair);
-    for (int c = (tid & 15) * 8; c < op.n_out; c += 128) st16(o + c, zero4());
-}
-
 // ============================================================ host side
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -793,27 +602,6 @@ static size_t expand_lds(int n_xa_slices, int R) {
 
 // rank steps of 32 of the MFMA expand
 static int nrs_of(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }
-
-static int tile_bound_of(int n, int S) {
-    if (n <= 0) return 0;
-    const long long a = (n + kTileRows - 1) / kTileRows + (long long)(n < S ? n : S);
-    return (int)(a < n ? a : n);
-}
-
-FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out) {
-    FusedPlan p{};
-    p.tile_bound = tile_bound_of(n, num_slots);
-    p.P = 1;
-    const int target_units = 512;  // about two units per CU of the shrink over the k dimension
-    while (p.tile_bound > 0 && (long long)p.P * 2 * p.tile_bound <= target_units && p.P * 2 <= k_in / 256 &&
-           p.P * 2 <= kMaxPieces)
-        p.P *= 2;
-    p.C = (n_out + kCW - 1) / kCW;
-    p.ctr_bytes = align_up(256 + (size_t)p.tile_bound * kCtrStride * sizeof(int), 256);
-    p.part_bytes = align_up((size_t)p.P * n * n_sh * R * sizeof(float), 256);
-    p.total_bytes = p.ctr_bytes + p.part_bytes;
-    return p;
-}
 
 template <class K>
 static void allow_lds(K kernel, size_t bytes) {
@@ -871,67 +659,6 @@ hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *ti
     case 2: return launch_expand_nrs<2>(op, xa, tiles, tile_bound, d.n, add_inputs, mfma_min, lds, st);
     default: return launch_expand_nrs<4>(op, xa, tiles, tile_bound, d.n, add_inputs, mfma_min, lds, st);
     }
-}
-
-template <int NRS, class Op>
-static hipError_t launch_fused_nrs(const Op &op, int n_pos, int n_xa_slices, const int32_t *tiles,
-                                   const FusedPlan &plan, void *ws, int mfma_min, int add_inputs, ZeroFill zf,
-                                   int zero_units, hipStream_t st) {
-    char *w = static_cast<char *>(ws);
-    int *ctl = reinterpret_cast<int *>(w);
-    int *ctr = ctl + 64;
-    int *done = ctr + 1;  // same line as the tile counter
-    float *part = reinterpret_cast<float *>(w + plan.ctr_bytes);
-    const size_t lds = std::max(shrink_lds(), expand_lds(n_xa_slices, op.R));
-    allow_lds(fused_kernel<NRS, Op>, lds);
-    const long long grid = (long long)plan.tile_bound * (plan.P + plan.C) + zero_units;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fused_kernel<NRS, Op>), dim3((unsigned)grid), dim3(kBT), lds, st, op, tiles,
-                       plan.tile_bound, plan.P, plan.C, n_pos, part, ctl, ctr, done, mfma_min, add_inputs, zf);
-    return hipGetLastError();
-}
-
-template <class Op>
-static hipError_t launch_fused_op(const Op &op, int n_pos, int n_xa_slices, const int32_t *tiles,
-                                  const FusedPlan &plan, void *ws, int mfma_min, int add_inputs, ZeroFill zf,
-                                  int zero_units, hipStream_t st) {
-    switch (nrs_of(op.R)) {
-    case 1: return launch_fused_nrs<1>(op, n_pos, n_xa_slices, tiles, plan, ws, mfma_min, add_inputs, zf, zero_units, st);
-    case 2: return launch_fused_nrs<2>(op, n_pos, n_xa_slices, tiles, plan, ws, mfma_min, add_inputs, zf, zero_units, st);
-    default: return launch_fused_nrs<4>(op, n_pos, n_xa_slices, tiles, plan, ws, mfma_min, add_inputs, zf, zero_units, st);
-    }
-}
-
-hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const FusedPlan &plan, void *ws, int mfma_min,
-                        hipStream_t st) {
-    const DenseOp op = dense_op(d);
-    return launch_fused_op(op, d.n, d.num_slices, tiles, plan, ws, mfma_min, 1, ZeroFill{nullptr, nullptr, 1, 1, 1, 0},
-                           0, st);
-}
-
-hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const FusedPlan &plan, void *ws,
-                            int mfma_min, hipStream_t st) {
-    MoeOp op{};
-    op.x = m.x;
-    op.ldx = m.ldx;
-    op.top_k = m.top_k;
-    op.wa = m.w_ptr_a;
-    op.lsa = m.lora_stride_a;
-    op.wb = m.w_ptr_b;
-    op.lsb = m.lora_stride_b;
-    op.out = m.out;
-    op.sc = m.scale;
-    op.k_in = m.H;
-    op.R = m.R;
-    op.n_sh = m.shared_a ? 1 : 2;
-    op.n_out = 2 * m.inter;
-    op.E = m.E;
-    op.inter = m.inter;
-    op.shared = m.shared_a ? 1 : 0;
-    const int n_pairs = m.T * m.top_k;
-    const ZeroFill zf{m.topk_ids, m.lora_ids, m.top_k, m.E, m.L, n_pairs};
-    const int zero_units = (n_pairs + 15) / 16;
-    return launch_fused_op(op, n_pairs, op.n_sh, tiles, plan, ws, mfma_min, 0, zf, zero_units, st);
 }
 
 }  // namespace tl

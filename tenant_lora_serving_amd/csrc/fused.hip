@@ -1,0 +1,670 @@
+// fused.hip -- the routed LoRA delta in one launch (shrink, then expand) for
+// gfx950, dense and routed-MoE gemm1.
+//
+// Semantics (vLLM punica_base.py, add_lora_linear = add_shrink then
+// add_expand; metrale lora_delta docs, apply_lora_bgmv; FlashInfer
+// bgmv_moe_gemm1_lora_delta): rows of one adapter slot form a segment; the
+// shrink gives xa = scale * x @ A^T in fp32, the expand adds xa @ B^T to the
+// row's output window and rounds once to bf16.
+//
+// Work units (a workgroup of 4 waves each), all shrink units first:
+//   shrink unit (tile t, k piece p): every rank row of the tile's adapter over
+//     k in [512p, 512p + 512); writes an fp32 partial block part[t][p][rr][16]
+//     and raises the piece's flag.
+//   expand unit (tile t, column chunk): at most 512 columns of one output
+//     window.  It issues its B and y loads, waits for the tile's P flags, sums
+//     the P partials in piece order (bitwise reproducible), scales, and adds
+//     xa @ B^T to y.
+// A consumer only waits on producers with lower workgroup ids, which never
+// wait themselves; workgroups are dispatched in id order, so every awaited
+// producer is running or done and the wait always ends.  It is still bounded
+// and reports a flag instead of spinning forever.
+//
+// Hand-off without fences.  Every partial is a 64-bit word {fp32 value, tag}
+// written and read as one agent-scope atomic, and the tag names the call
+// (tag = generation + 1, the generation being the number of completed calls
+// on this workspace).  A reader that sees the current tag therefore sees the
+// value, so the producer needs no release (an L2 write-back) and the consumer
+// no acquire (an L2 invalidate).  The piece flags carry the same tag and only
+// tell the consumer when to start reading; a word that still shows an old tag
+// is read again.  The last consumer of a tile counts the tile as finished,
+// and the last finished tile of the call advances the generation.  Tags only grow, so data left by an
+// earlier call, of any shape, is never taken for the current one.
+//
+// The latency chain (tile record -> A/x loads -> reduce -> publish -> poll ->
+// partial loads -> expand -> y store) is what bounds a decode-sized call, so
+// every wave reads its tile record itself (scalar fields through readlane),
+// every unit issues all of its first-pass loads before it waits for any, and
+// the x tile is staged once in LDS for all four waves.
+//
+// Segments with at least mfma_min rows run on v_mfma_f32_16x16x32_bf16
+// (tile rows are the MFMA rows; the expand feeds xa as bf16 hi + lo terms,
+// hi = bf16(xa), lo = bf16(xa - hi)).  Shorter ones run on the vector ALU:
+//   shrink: a wave is 4 DPP rows of 16 lanes; the 16 lanes of a row split the
+//     unit's k range (8 k each, 4 steps of 128), each row of lanes owns
+//     RPL rank rows, and the 16 per-lane dot products of a (row, rank row)
+//     are summed with DPP row moves.
+//   expand: a lane owns two adjacent output columns (their B rows are 2R
+//     consecutive bf16) and multiplies them by fp32 xa read from LDS with
+//     uniform addresses; y is read and written 4 bytes per lane, so a wave's
+//     access to one row is 256 contiguous bytes.
+#include "common.h"
+#include "kernels.h"
+#include "ops.h"
+
+namespace tl {
+
+constexpr int kFT = 256;      // threads per workgroup
+constexpr int kKP = 512;      // k per shrink unit
+constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x tile
+constexpr int kEC = 512;      // output columns per expand unit (128 per wave)
+constexpr int kSpinLimit = 1 << 22;
+// control line of the workspace
+constexpr int kCtlError = 0;  // set when a bounded wait gave up
+constexpr int kCtlGen = 1;    // completed calls on this workspace
+constexpr int kCtlDone = 2;   // finished tiles of the running call
+
+// ============================================================ tile record, per wave
+// Lane i holds word (i mod 32) of the record; the scalar fields are read
+// with readlane, so every branch on them is uniform.
+struct Hdr {
+    int rec;
+    int slot, pos0, m, mseg;
+};
+
+__device__ __forceinline__ Hdr load_hdr(const int32_t *tiles, int t) {
+    Hdr h;
+    h.rec = tiles[(int64_t)t * kTileWords + (lane_id() & 31)];
+    h.slot = __builtin_amdgcn_readlane(h.rec, kRecSlot);
+    h.pos0 = __builtin_amdgcn_readlane(h.rec, kRecPos);
+    h.m = __builtin_amdgcn_readlane(h.rec, kRecRows);
+    h.mseg = __builtin_amdgcn_readlane(h.rec, kRecSegRows);
+    return h;
+}
+// original row id of tile row j; j must be wave-uniform
+__device__ __forceinline__ int hdr_row(const Hdr &h, int j) {
+    return __builtin_amdgcn_readlane(h.rec, kRecRowIds + j);
+}
+
+// ============================================================ shrink units
+// x rows 0..15 (zero past m), k in [k0, k1), into xs[j * kXS + k - k0]: wave w
+// loads rows w, w+4, w+8, w+12, one coalesced 1 KB row segment each.
+template <class Op>
+__device__ __forceinline__ void load_x(const Op &op, const Hdr &h, int k0, int k1, u32x4_t (&xv)[4]) {
+    const int lane = lane_id(), w = wave_id();
+    const int k = k0 + 8 * lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = w + 4 * u;
+        const uint16_t *xp = j < h.m ? op.xrow(hdr_row(h, j)) : nullptr;
+        xv[u] = (xp && k < k1) ? ld16(xp + k) : zero4();
+    }
+}
+__device__ __forceinline__ void store_x(const u32x4_t (&xv)[4], uint16_t *xs) {
+    const int lane = lane_id(), w = wave_id();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(xs + (w + 4 * u) * kXS + 8 * lane) = xv[u];
+}
+__device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+
+// Vector-ALU shrink of one unit into pu[rr * 16 + j] (rr < n_rr, j < m).
+// Lane (rl = lane / 16, kl = lane % 16) of wave w holds rank rows
+// rb + 4w + rl + 16i (i < RPL) at k = k0 + 128s + 8kl (s < 4).
+template <int RPL, class Op>
+__device__ __forceinline__ void shrink_valu(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
+                                            uint64_t *pu, uint32_t tag) {
+    const int lane = lane_id(), w = wave_id();
+    const int rl = lane >> 4, kl = lane & 15;
+    const int n_rr = op.n_rr(), m = h.m;
+    u32x4_t a[RPL][4];
+    auto load_a = [&](int rb) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int rr = rb + 4 * w + rl + 16 * i;
+            const uint16_t *ap = rr < n_rr ? op.arow(h.slot, rr) : nullptr;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = k0 + 128 * s + 8 * kl;
+                a[i][s] = (ap && k < k1) ? ld16_stream(ap + k) : zero4();
+            }
+        }
+    };
+    {
+        u32x4_t xv[4];
+        load_x(op, h, k0, k1, xv);  // x first: the LDS store below waits only for these
+        load_a(0);
+        store_x(xv, xs);
+        __syncthreads();
+    }
+    for (int rb = 0; rb < n_rr; rb += 16 * RPL) {
+        if (rb > 0) load_a(rb);
+        float sv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (4 * b < m) {
+                float acc[RPL][4];
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    u32x4_t xv[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) xv[jj] = lds16(xs + (4 * b + jj) * kXS + 128 * s + 8 * kl);
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = dot8(a[i][s], xv[jj], acc[i][jj]);
+                }
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = group_sum(acc[i][jj], 4);
+                // lane kl keeps value kl = 4i + jj of its row of lanes
+                float v = acc[0][0];
+#pragma unroll
+                for (int q = 1; q < 4 * RPL; ++q) v = kl == q ? acc[q >> 2][q & 3] : v;
+                sv[b] = v;
+            }
+        }
+        const int i = kl >> 2, jj = kl & 3;
+        const int rr = rb + 4 * w + rl + 16 * i;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = 4 * b + jj;
+            if (kl < 4 * RPL && rr < n_rr && j < m) store_word64(pu + rr * 16 + j, tagged(sv[b], tag));
+        }
+    }
+}
+
+// MFMA shrink of one unit: wave w takes rank-row groups g = w, w+4, ... of 16;
+// D[tile row][rank row] = x[16 x 32k] . A^T over 16 steps of 32 k.
+template <class Op>
+__device__ __forceinline__ void shrink_mfma(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
+                                            uint64_t *pu, uint32_t tag) {
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 15, kq = lane >> 4;
+    const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
+    u32x4_t av[16];
+    auto load_a = [&](int g) {
+        const int rr = 16 * g + col;
+        const uint16_t *ap = (g < G && rr < n_rr) ? op.arow(h.slot, rr) : nullptr;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int k = k0 + 32 * s + 8 * kq;
+            av[s] = (ap && k < k1) ? ld16_stream(ap + k) : zero4();
+        }
+    };
+    {
+        u32x4_t xv[4];
+        load_x(op, h, k0, k1, xv);
+        load_a(w);
+        store_x(xv, xs);
+        __syncthreads();
+    }
+    for (int g = w; g < G; g += 4) {
+        if (g != w) load_a(g);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 16; ++s) acc = mfma_16x16x32(lds16(xs + col * kXS + 32 * s + 8 * kq), av[s], acc);
+        // lane holds D[4kq + i][col]: tile rows 4kq..4kq+3 of rank row rr
+        const int rr = 16 * g + col;
+        if (rr < n_rr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kq + i < h.m) store_word64(pu + rr * 16 + 4 * kq + i, tagged(acc[i], tag));
+        }
+    }
+}
+
+// ============================================================ expand units
+// Wait until the tile's P pieces carry this call's tag (threads p < P poll
+// flag p with relaxed loads); false if a bounded wait gave up.
+__device__ __forceinline__ bool wait_pieces(const int *flags, int P, uint32_t tag, int *ctl, int *ok_lds) {
+    if (threadIdx.x == 0) *ok_lds = 1;
+    __syncthreads();
+    for (int p = threadIdx.x; p < P; p += kFT) {
+        int spins = 0;
+        while ((uint32_t)load_relaxed(flags + p) != tag) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kSpinLimit) {
+                atomicExch(ctl + kCtlError, 1);
+                *ok_lds = 0;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*ok_lds) != 0;
+}
+
+// xa of tile rows j < 16 for the R rank rows of block xb: the P partials
+// summed in piece order, times the slot's scale (rows j >= m are zero).
+// MF: bf16 hi/lo pairs xl[j][0..R) = hi, xl[j][R..2R) = lo; else fp32 xf[j][R].
+template <bool MF>
+__device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, int xb, int R, int m, float sc,
+                                         uint32_t tag, int *ctl, char *lds) {
+    const int64_t pstride = (int64_t)n_rr * 16;
+    for (int idx = threadIdx.x; idx < R * 16; idx += kFT) {
+        const int r = idx >> 4, j = idx & 15;
+        float s = 0.f;
+        if (j < m) {
+            const uint64_t *q = pt + (int64_t)(xb * R + r) * 16 + j;
+            for (int p0 = 0; p0 < P; p0 += 8) {
+                uint64_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = p0 + u < P ? load_word64(q + (p0 + u) * pstride) : 0;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (p0 + u < P) {
+                        // a flag can become visible before the data it announces
+                        int spins = 0;
+                        while ((uint32_t)(v[u] >> 32) != tag && spins++ < kSpinLimit)
+                            v[u] = load_word64(q + (p0 + u) * pstride);
+                        if ((uint32_t)(v[u] >> 32) != tag) atomicExch(ctl + kCtlError, 1);
+                        s += __uint_as_float((uint32_t)v[u]);
+                    }
+                }
+            }
+            s *= sc;
+        }
+        if (MF) {
+            uint16_t *xl = reinterpret_cast<uint16_t *>(lds);
+            const float hi = bf16_round(s);
+            xl[j * 2 * R + r] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+            xl[j * 2 * R + R + r] = __builtin_bit_cast(uint16_t, (__bf16)(s - hi));
+        } else {
+            reinterpret_cast<float *>(lds)[j * R + r] = s;
+        }
+    }
+}
+
+// What an expand unit needs to find its xa.
+struct XaSrc {
+    const uint64_t *pt;  // the tile's partial blocks
+    const int *flags;    // the tile's piece flags
+    int P, xb;
+    float sc;
+    uint32_t tag;
+    int *ctl;
+    int *ok;  // LDS
+};
+
+// Vector-ALU expand: lane owns columns c, c+1 of [c0, c1) (c = c0 + 128w + 2 lane).
+template <class Op>
+__device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
+                                            const XaSrc &xs, char *lds) {
+    const int lane = lane_id(), w = wave_id();
+    const int R = op.R, m = h.m;
+    const int c = c0 + 128 * w + 2 * lane;
+    const bool cok = c < c1;
+    const uint16_t *bp = cok ? op.brow(h.slot, c) : nullptr;  // rows c and c+1 are adjacent
+    u32x4_t bq[2][4];  // ranks 0..31 of both columns, in flight during the wait
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bq[cc][q] = (bp && 8 * q < R) ? ld16(bp + cc * R + 8 * q) : zero4();
+    uint32_t yv[kTileRows];
+#pragma unroll
+    for (int j = 0; j < kTileRows; ++j)
+        yv[j] = (add_inputs && cok && j < m)
+                    ? *reinterpret_cast<const uint32_t *>(op.yrow(hdr_row(h, j)) + c)
+                    : 0u;
+    if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
+    stage_xa<false>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.tag, xs.ctl, lds);
+    __syncthreads();
+    const float *xf = reinterpret_cast<const float *>(lds);
+    // rows in two blocks of 8, ranks in blocks of 32 held as packed bf16 (bq)
+    // and widened 16 at a time
+#pragma unroll
+    for (int jb = 0; jb < kTileRows; jb += 8) {
+        if (jb >= m) break;
+        float o0[8], o1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o0[j] = o1[j] = 0.f;
+        for (int r0 = 0; r0 < R; r0 += 32) {
+            if (r0 > 0 || (jb > 0 && R > 32)) {
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        bq[cc][q] = (bp && r0 + 8 * q < R) ? ld16(bp + cc * R + r0 + 8 * q) : zero4();
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int rh = r0 + 16 * half;
+                if (rh < R) {
+                    float b0[16], b1[16];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const u32x4_t u0 = bq[0][2 * half + q], u1 = bq[1][2 * half + q];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            b0[8 * q + 2 * e] = bf_lo(u0[e]);
+                            b0[8 * q + 2 * e + 1] = bf_hi(u0[e]);
+                            b1[8 * q + 2 * e] = bf_lo(u1[e]);
+                            b1[8 * q + 2 * e + 1] = bf_hi(u1[e]);
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (jb + j < m) {
+#pragma unroll
+                            for (int q4 = 0; q4 < 4; ++q4) {
+                                if (rh + 4 * q4 >= R) break;  // R is a multiple of 8, not always of 16
+                                const f32x4_t xa4 =
+                                    *reinterpret_cast<const f32x4_t *>(xf + (jb + j) * R + rh + 4 * q4);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    o0[j] = __builtin_fmaf(xa4[e], b0[4 * q4 + e], o0[j]);
+                                    o1[j] = __builtin_fmaf(xa4[e], b1[4 * q4 + e], o1[j]);
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (cok) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (jb + j < m) {
+                    float v0 = o0[j], v1 = o1[j];
+                    if (add_inputs) {
+                        v0 += bf_lo(yv[jb + j]);
+                        v1 += bf_hi(yv[jb + j]);
+                    }
+                    *reinterpret_cast<uint32_t *>(op.yrow(hdr_row(h, jb + j)) + c) = pack_bf16x2(v0, v1);
+                }
+            }
+        }
+    }
+}
+
+// MFMA expand: wave w owns columns c0 + 128w .. +128 as 8 tiles of 16;
+// D[column][tile row] = B[column][ranks] . (xa_hi + xa_lo)[tile row][ranks]
+// as two bf16 MFMAs per 32 ranks (NRS rank steps).
+template <int NRS, class Op>
+__device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
+                                            const XaSrc &xs, char *lds) {
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 15, kq = lane >> 4;
+    const int R = op.R, cw0 = c0 + 128 * w;
+    u32x4_t bo[8][NRS];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        const int cc = cw0 + 16 * ct + col;
+        const uint16_t *bp = cc < c1 ? op.brow(h.slot, cc) : nullptr;
+#pragma unroll
+        for (int s = 0; s < NRS; ++s) {
+            const int rk = 32 * s + 8 * kq;
+            bo[ct][s] = (bp && rk < R) ? ld16(bp + rk) : zero4();
+        }
+    }
+    // output row = col, columns cw0 + 16ct + 4kq .. +4 (8 bytes)
+    const int rid = __shfl(h.rec, kRecRowIds + col, kWave);
+    uint16_t *yp = col < h.m ? op.yrow(rid) : nullptr;
+    uint2 yv[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        const int cy = cw0 + 16 * ct + 4 * kq;
+        yv[ct] = (add_inputs && yp && cy < c1) ? *reinterpret_cast<const uint2 *>(yp + cy) : make_uint2(0u, 0u);
+    }
+    if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
+    stage_xa<true>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.tag, xs.ctl, lds);
+    __syncthreads();
+    const uint16_t *xl = reinterpret_cast<const uint16_t *>(lds) + col * 2 * R;
+    u32x4_t hv[NRS], lv[NRS];
+#pragma unroll
+    for (int s = 0; s < NRS; ++s) {
+        const int rk = 32 * s + 8 * kq;
+        hv[s] = rk < R ? lds16(xl + rk) : zero4();
+        lv[s] = rk < R ? lds16(xl + R + rk) : zero4();
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NRS; ++s) {
+            d = mfma_16x16x32(bo[ct][s], hv[s], d);
+            d = mfma_16x16x32(bo[ct][s], lv[s], d);
+        }
+        const int cy = cw0 + 16 * ct + 4 * kq;
+        if (yp && cy < c1) {
+            float v[4] = {d[0], d[1], d[2], d[3]};
+            if (add_inputs) {
+                v[0] += bf_lo(yv[ct].x);
+                v[1] += bf_hi(yv[ct].x);
+                v[2] += bf_lo(yv[ct].y);
+                v[3] += bf_hi(yv[ct].y);
+            }
+            *reinterpret_cast<uint2 *>(yp + cy) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+    }
+}
+
+// Expand chunk cc -> output window l and columns [c0, c1) (chunks of kEC
+// columns, window by window); slice offsets are read at constant indices.
+template <class Op>
+__device__ __forceinline__ void chunk_of(const Op &op, int cc, int &l, int &c0, int &c1) {
+    int base = 0;
+    l = -1;
+    c0 = c1 = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s) {
+        if (s < op.n_xs() && l < 0) {
+            const int a = op.xoff(s), b = op.xoff(s + 1);
+            const int n = (b - a + kEC - 1) / kEC;
+            if (cc < base + n) {
+                l = s;
+                c0 = a + (cc - base) * kEC;
+                c1 = min(b, c0 + kEC);
+            }
+            base += n;
+        }
+    }
+}
+
+// ============================================================ kernel
+struct FusedArgs {
+    const int32_t *tiles;
+    const int32_t *counts;  // counts[4] = tiles in use
+    int tile_bound, P, FP, C;
+    uint64_t *part;  // [tile_bound][P][n_rr][16] tagged partials
+    int *ctl;        // control line
+    int *flags;      // [tile_bound][FP]: piece flags, then the tile's finished consumers at FP - 1
+    int mfma_min, add_inputs;
+};
+
+template <int RPL, int NRS, class Op>
+__global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
+    __shared__ __align__(16) char lds[kTileRows * kXS * 2 > kTileRows * kMaxRank * 4 ? kTileRows * kXS * 2
+                                                                                    : kTileRows * kMaxRank * 4];
+    __shared__ int ok;
+    const int bid = blockIdx.x;
+    const int P = fa.P, C = fa.C;
+    const int n_shr = fa.tile_bound * P, n_exp = fa.tile_bound * C;
+    const int n_rr = op.n_rr();
+    if (bid < n_shr + n_exp) {
+        const uint32_t tag = (uint32_t)load_relaxed(fa.ctl + kCtlGen) + 1u;
+        if (bid < n_shr) {
+            const int t = bid / P, p = bid - t * P;
+            const Hdr h = load_hdr(fa.tiles, t);
+            if (h.m == 0) return;
+            const int k0 = p * kKP, k1 = min(op.k_in, k0 + kKP);
+            uint64_t *pu = fa.part + ((int64_t)t * P + p) * n_rr * 16;
+            uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
+            if (h.mseg >= fa.mfma_min)
+                shrink_mfma(op, h, k0, k1, xs, pu, tag);
+            else
+                shrink_valu<RPL>(op, h, k0, k1, xs, pu, tag);
+            // raise the flag after every wave has issued its stores (the tags,
+            // not this order, are what make the hand-off correct)
+            __syncthreads();
+            if (threadIdx.x == 0) store_relaxed(fa.flags + (int64_t)t * fa.FP + p, (int)tag);
+            return;
+        }
+        const int e = bid - n_shr;
+        const int t = e / C, cc = e - t * C;
+        const int n_tiles = fa.counts[4];
+        const Hdr h = load_hdr(fa.tiles, t);
+        if (h.m == 0) return;
+        int l, c0, c1;
+        chunk_of(op, cc, l, c0, c1);
+        const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
+                       op.scale_of(h.slot), tag, fa.ctl, &ok};
+        if (h.mseg >= fa.mfma_min)
+            expand_mfma<NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+        else
+            expand_valu(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+        // the last consumer of a tile counts the tile as finished; the last
+        // finished tile of the call advances the generation (two levels, so
+        // no single address takes one atomic per consumer)
+        if (threadIdx.x == 0) {
+            int *tile_done = fa.flags + (int64_t)t * fa.FP + fa.FP - 1;
+            if (atomic_add_relaxed(tile_done, 1) == C - 1) {
+                store_relaxed(tile_done, 0);
+                if (atomic_add_relaxed(fa.ctl + kCtlDone, 1) == n_tiles - 1) {
+                    store_relaxed(fa.ctl + kCtlDone, 0);
+                    store_relaxed(fa.ctl + kCtlGen, (int)tag);
+                }
+            }
+        }
+        return;
+    }
+    // zero rows of pairs that get no delta (MoE only)
+    const int u = bid - n_shr - n_exp;
+    const int tid = threadIdx.x;
+    const int pair = u * 16 + (tid >> 4);
+    if (pair >= zf.n_pairs) return;
+    const int l = zf.lora[pair / zf.top_k], ex = zf.topk[pair];
+    if (l >= 0 && l < zf.L && ex >= 0 && ex < zf.E) return;
+    uint16_t *o = op.yrow(pair);
+    for (int c = (tid & 15) * 8; c < op.n_out; c += 128) st16(o + c, zero4());
+}
+
+// ============================================================ host side
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static int tile_bound_of(int n, int S) {
+    if (n <= 0) return 0;
+    const long long a = (n + kTileRows - 1) / kTileRows + (long long)(n < S ? n : S);
+    return (int)(a < n ? a : n);
+}
+
+// Workspace: [control line, 256 B] [per tile: P piece flags .. finished consumers, FP int]
+// [tagged partials: tile_bound x P x n_rr x 16 uint64].
+FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out) {
+    (void)n_out;
+    FusedPlan p{};
+    p.tile_bound = tile_bound_of(n, num_slots);
+    p.P = (k_in + kKP - 1) / kKP;
+    p.FP = (int)align_up((size_t)p.P + 1, 64);
+    p.flag_bytes = align_up(256 + (size_t)p.tile_bound * p.FP * sizeof(int), 256);
+    p.part_bytes = align_up((size_t)p.tile_bound * p.P * n_sh * R * kTileRows * sizeof(uint64_t), 256);
+    p.total_bytes = p.flag_bytes + p.part_bytes;
+    return p;
+}
+
+static int rpl_of(int n_rr) { return n_rr >= 64 ? 4 : (n_rr + 15) / 16; }
+static int nrs_of(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }
+
+template <int RPL, int NRS, class Op>
+static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, long long grid, ZeroFill zf, hipStream_t st) {
+    hipLaunchKernelGGL((fused_kernel<RPL, NRS, Op>), dim3((unsigned)grid), dim3(kFT), 0, st, op, fa, zf);
+    return hipGetLastError();
+}
+
+template <int RPL, class Op>
+static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, long long grid, ZeroFill zf, hipStream_t st) {
+    switch (nrs_of(op.R)) {
+    case 1: return launch_fused_t<RPL, 1>(op, fa, grid, zf, st);
+    case 2: return launch_fused_t<RPL, 2>(op, fa, grid, zf, st);
+    default: return launch_fused_t<RPL, 4>(op, fa, grid, zf, st);
+    }
+}
+
+template <class Op>
+static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
+                                  int C, void *ws, int mfma_min, int add_inputs, ZeroFill zf, int zero_units,
+                                  hipStream_t st) {
+    char *w = static_cast<char *>(ws);
+    FusedArgs fa{};
+    fa.tiles = tiles;
+    fa.counts = counts;
+    fa.tile_bound = plan.tile_bound;
+    fa.P = plan.P;
+    fa.FP = plan.FP;
+    fa.C = C;
+    fa.ctl = reinterpret_cast<int *>(w);
+    fa.flags = fa.ctl + 64;
+    fa.part = reinterpret_cast<uint64_t *>(w + plan.flag_bytes);
+    fa.mfma_min = mfma_min;
+    fa.add_inputs = add_inputs;
+    const long long grid = (long long)plan.tile_bound * (plan.P + C) + zero_units;
+    if (grid == 0) return hipSuccess;
+    switch (rpl_of(op.n_sh * op.R)) {
+    case 1: return launch_fused_r<1>(op, fa, grid, zf, st);
+    case 2: return launch_fused_r<2>(op, fa, grid, zf, st);
+    case 3: return launch_fused_r<3>(op, fa, grid, zf, st);
+    default: return launch_fused_r<4>(op, fa, grid, zf, st);
+    }
+}
+
+static int chunks_of(const int *off, int n_windows) {
+    int c = 0;
+    for (int l = 0; l < n_windows; ++l) c += (off[l + 1] - off[l] + kEC - 1) / kEC;
+    return c;
+}
+
+hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
+                        void *ws, int mfma_min, hipStream_t st) {
+    DenseOp op{};
+    op.x = d.x;
+    op.ldx = d.ldx;
+    op.a_pool = d.a_pool;
+    op.b_pool = d.b_pool;
+    op.scale = d.scale;
+    op.y = d.y;
+    op.ldy = d.ldy;
+    op.k_in = d.k_in;
+    op.R = d.R;
+    op.n_sh = d.num_slices;
+    op.n_sl = d.num_slices;
+    op.n_out = d.slice_off[d.num_slices];
+    op.col0 = d.offset_start;
+    for (int l = 0; l <= kMaxSlices; ++l) op.off[l] = d.slice_off[l < d.num_slices ? l : d.num_slices];
+    const int C = chunks_of(d.slice_off, d.num_slices);
+    return launch_fused_op(op, tiles, counts, plan, C, ws, mfma_min, 1, ZeroFill{nullptr, nullptr, 1, 1, 1, 0}, 0,
+                           st);
+}
+
+hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
+                            void *ws, int mfma_min, hipStream_t st) {
+    MoeOp op{};
+    op.x = m.x;
+    op.ldx = m.ldx;
+    op.top_k = m.top_k;
+    op.wa = m.w_ptr_a;
+    op.lsa = m.lora_stride_a;
+    op.wb = m.w_ptr_b;
+    op.lsb = m.lora_stride_b;
+    op.out = m.out;
+    op.sc = m.scale;
+    op.k_in = m.H;
+    op.R = m.R;
+    op.n_sh = m.shared_a ? 1 : 2;
+    op.n_out = 2 * m.inter;
+    op.E = m.E;
+    op.inter = m.inter;
+    op.shared = m.shared_a ? 1 : 0;
+    const int n_pairs = m.T * m.top_k;
+    const ZeroFill zf{m.topk_ids, m.lora_ids, m.top_k, m.E, m.L, n_pairs};
+    const int zero_units = (n_pairs + 15) / 16;
+    const int off[3] = {0, m.inter, 2 * m.inter};
+    const int C = chunks_of(off, 2);
+    return launch_fused_op(op, tiles, counts, plan, C, ws, mfma_min, 0, zf, zero_units, st);
+}
+
+}  // namespace tl

@@ -55,8 +55,8 @@ struct DenseShape {
 struct FusedPlan {
     int tile_bound;  // tile records the meta build wrote
     int P;           // k pieces of the shrink
-    int C;           // 512-column chunks of the expand
-    size_t part_bytes, ctr_bytes, total_bytes;
+    int FP;          // ints per tile: P piece flags and a consumer count (P + 1 rounded up to 64)
+    size_t flag_bytes, part_bytes, total_bytes;
 };
 FusedPlan fused_plan(int n, int num_slots, int num_slices, int R, int k_in, int n_out);
 
@@ -64,8 +64,15 @@ hipError_t launch_shrink(const DenseShape &d, const int32_t *tiles, int tile_bou
                          hipStream_t st);
 hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *tiles, int tile_bound,
                          int add_inputs, int mfma_min, hipStream_t st);
-hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const FusedPlan &plan, void *ws,
-                        int mfma_min, hipStream_t st);
+hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
+                        void *ws, int mfma_min, hipStream_t st);
+
+// MoE pairs whose (adapter, expert) is not valid get a zero output row.
+struct ZeroFill {
+    const int32_t *topk;
+    const int32_t *lora;
+    int top_k, E, L, n_pairs;
+};
 
 struct MoeShape {
     const uint16_t *x;
@@ -83,7 +90,7 @@ struct MoeShape {
     float scale;
     uint16_t *out;
 };
-hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const FusedPlan &plan, void *ws,
-                            int mfma_min, hipStream_t st);
+hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
+                            void *ws, int mfma_min, hipStream_t st);
 
 }  // namespace tl

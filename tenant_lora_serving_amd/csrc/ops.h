@@ -1,0 +1,92 @@
+// ops.h -- addressing policies of the routed LoRA delta kernels: where a row's
+// input, an adapter's A and B rows and a row's output live.  Internal to the
+// library; the kernels are written once against this interface.
+//
+// Rank rows: the shrink computes n_rr = n_sh * R values per row, rank row
+// rr = l * R + r belonging to shrink slice l.  Output slices: the expand
+// writes n_xs column windows [xoff(l), xoff(l + 1)), each fed by the R rank
+// rows of xa block xblk(l).
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tl {
+
+// Dense delta (vLLM punica_base.py, add_shrink / add_expand: one A and one
+// block of B rows per output slice; metrale lora_delta, LoraPair layout).
+struct DenseOp {
+    const uint16_t *x;
+    int64_t ldx;
+    const uint16_t *a_pool;
+    const uint16_t *b_pool;
+    const float *scale;
+    uint16_t *y;
+    int64_t ldy;
+    int k_in, R, n_sh, n_out, col0, n_sl;
+    int off[kMaxSlices + 1];
+
+    __device__ int n_rr() const { return n_sh * R; }
+    __device__ int n_xs() const { return n_sl; }
+    __device__ const uint16_t *xrow(int row) const { return x + (int64_t)row * ldx; }
+    // rank row rr = l*R + r of slot s: a_pool[s][l][r][:]
+    __device__ const uint16_t *arow(int slot, int rr) const {
+        return a_pool + ((int64_t)slot * n_sh * R + rr) * k_in;
+    }
+    // slice of output column c; unrolled so off[] is only read at constant
+    // indices (a runtime index would move the kernel argument to scratch)
+    __device__ int xslice(int c) const {
+        int l = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSlices; ++i) l += (i < n_sl && c >= off[i]) ? 1 : 0;
+        return l;
+    }
+    // output window of slice l (l a compile-time constant at every call)
+    __device__ int xoff(int l) const { return off[l]; }
+    __device__ int xblk(int l) const { return l; }
+    __device__ const uint16_t *brow(int slot, int c) const {
+        return b_pool + ((int64_t)slot * n_out + c) * R;
+    }
+    __device__ uint16_t *yrow(int row) const { return y + (int64_t)row * ldy + col0; }
+    __device__ float scale_of(int slot) const { return scale[slot]; }
+};
+
+// Routed MoE gemm1 (FlashInfer bgmv_moe_gemm1_lora_delta): key = l*E + e,
+// rows are (token, slot) pairs; output window 0 is gate, window 1 is up.
+struct MoeOp {
+    const uint16_t *x;
+    int64_t ldx;
+    int top_k;
+    const int64_t *wa;
+    int64_t lsa;
+    const int64_t *wb;
+    int64_t lsb;
+    uint16_t *out;
+    float sc;
+    int k_in, R, n_sh, n_out, E, inter, shared;
+
+    __device__ int n_rr() const { return n_sh * R; }
+    __device__ int n_xs() const { return 2; }
+    __device__ const uint16_t *xrow(int pair) const { return x + (int64_t)(pair / top_k) * ldx; }
+    __device__ const uint16_t *arow(int key, int rr) const {
+        const int l = key / E, e = key - l * E;
+        const int sg = rr / R, r = rr - sg * R;
+        const uint16_t *base = reinterpret_cast<const uint16_t *>(wa[shared ? e : sg * E + e]);
+        return base + (int64_t)l * lsa + (int64_t)r * k_in;
+    }
+    __device__ int xslice(int c) const { return shared ? 0 : (c >= inter ? 1 : 0); }
+    __device__ int xoff(int l) const { return l * inter; }
+    __device__ int xblk(int l) const { return shared ? 0 : l; }
+    __device__ const uint16_t *brow(int key, int c) const {
+        const int l = key / E, e = key - l * E;
+        if (shared)
+            return reinterpret_cast<const uint16_t *>(wb[e]) + (int64_t)l * lsb + (int64_t)c * R;
+        const int sg = c >= inter ? 1 : 0;
+        return reinterpret_cast<const uint16_t *>(wb[sg * E + e]) + (int64_t)l * lsb +
+               (int64_t)(c - sg * inter) * R;
+    }
+    __device__ uint16_t *yrow(int pair) const { return out + (int64_t)pair * n_out; }
+    __device__ float scale_of(int) const { return sc; }
+};
+
+}  // namespace tl
