@@ -219,8 +219,8 @@ __device__ __forceinline__ void shrink_mfma(const Op &op, const Hdr &h, int k0, 
 }
 
 // ============================================================ expand units
-// Wait until the tile's P pieces carry this call's tag (threads p < P poll
-// flag p with relaxed loads); false if a bounded wait gave up.
+// Wait until pieces [0, P) of the tile carry this call's tag (threads p < P
+// poll flag p with relaxed loads); false if a bounded wait gave up.
 __device__ __forceinline__ bool wait_pieces(const int *flags, int P, uint32_t tag, int *ctl, int *ok_lds) {
     if (threadIdx.x == 0) *ok_lds = 1;
     __syncthreads();
@@ -252,9 +252,10 @@ __device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, in
         if (j < m) {
             const uint64_t *q = pt + (int64_t)(xb * R + r) * 16 + j;
             for (int p0 = 0; p0 < P; p0 += 8) {
+                // eight loads in flight (indices past P repeat piece P - 1 and are not summed)
                 uint64_t v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = p0 + u < P ? load_word64(q + (p0 + u) * pstride) : 0;
+                for (int u = 0; u < 8; ++u) v[u] = load_word64(q + min(p0 + u, P - 1) * pstride);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     if (p0 + u < P) {
@@ -348,17 +349,21 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
                         }
                     }
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        if (jb + j < m) {
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if (rh + 4 * q4 >= R) break;  // R is a multiple of 8, not always of 16
+                        // the 8 rows' xa of this rank quad in one batch of LDS reads
+                        // (rows past m read row m - 1 and are not used)
+                        f32x4_t xa4[8];
 #pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4) {
-                                if (rh + 4 * q4 >= R) break;  // R is a multiple of 8, not always of 16
-                                const f32x4_t xa4 =
-                                    *reinterpret_cast<const f32x4_t *>(xf + (jb + j) * R + rh + 4 * q4);
+                        for (int j = 0; j < 8; ++j)
+                            xa4[j] = *reinterpret_cast<const f32x4_t *>(xf + min(jb + j, m - 1) * R + rh + 4 * q4);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            if (jb + j < m) {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
-                                    o0[j] = __builtin_fmaf(xa4[e], b0[4 * q4 + e], o0[j]);
-                                    o1[j] = __builtin_fmaf(xa4[e], b1[4 * q4 + e], o1[j]);
+                                    o0[j] = __builtin_fmaf(xa4[j][e], b0[4 * q4 + e], o0[j]);
+                                    o1[j] = __builtin_fmaf(xa4[j][e], b1[4 * q4 + e], o1[j]);
                                 }
                             }
                         }
