@@ -254,12 +254,148 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
     }
 }
 
+// ------------------------------------------------------------ small batches
+// n <= 1024 rows and a slot table that fits LDS: one workgroup of NT >= n
+// threads, one row per thread.  Each wave ranks its rows among equal slots
+// with one ballot per distinct slot present in the wave and records how many
+// rows of each slot it holds in a [slot][wave] table; one block scan over
+// the slots turns the table into every (slot, wave)'s first sorted position
+// and gives each slot its segment index and first tile.  Since waves hold
+// rows in order, rows stay in ascending order within a slot.
+constexpr int kSmallTable = 16384;  // slots x waves entries of the count table
+constexpr int kSmallMaxSlots = 4096;
+constexpr int kSmallBallotSlots = 64;  // up to this many slots: one ballot per slot value
+
+template <int NT, class Src>
+__global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, MetaOut out) {
+    constexpr int W = NT / kWave;
+    extern __shared__ int dyn[];
+    int *tab = dyn;                        // [S][W]: counts, then first sorted positions
+    int *seg_idx = tab + (size_t)S * W;    // [S]
+    int *tile_off = seg_idx + S;           // [S]
+    int *start = tile_off + S;             // [S]
+    __shared__ Int3 scan3[W + 1];
+    __shared__ int n_long, n_invalid;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int raw = tid < n ? src.key(tid) : -1;
+    const bool active = tid < n && raw >= 0 && raw < S;
+    const int key = active ? raw : -1;
+    for (int i = tid; i < S * W; i += NT) tab[i] = 0;
+    if (tid == 0) n_long = n_invalid = 0;
+    __syncthreads();
+    if (tid < n && raw >= S) atomicAdd(&n_invalid, 1);
+    // rank among the wave's rows of the same slot: with few slots one ballot
+    // per slot value (no scalar round trips), else one per distinct slot
+    int rank = 0;
+    if (S <= kSmallBallotSlots) {
+        for (int k = 0; k < S; ++k) {
+            const uint64_t same = __ballot(key == k);
+            if (key == k) rank = __popcll(same & lanemask_lt());
+            if (lane == 0) tab[k * W + w] = __popcll(same);
+        }
+    } else {
+        uint64_t pending = __ballot(active);
+        while (pending) {
+            const int leader = __builtin_ctzll(pending);
+            const int k = __builtin_amdgcn_readlane(key, leader);
+            const uint64_t same = __ballot(key == k);
+            if (key == k) rank = __popcll(same & lanemask_lt());
+            if (lane == leader) tab[k * W + w] = __popcll(same);
+            pending &= ~same;
+        }
+    }
+    __syncthreads();
+    // per-slot totals: {rows, segments, tiles}, scanned over the slots
+    const int per = (S + NT - 1) / NT;
+    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+    Int3 loc = {0, 0, 0};
+    for (int k = s0; k < s1; ++k) {
+        int t = 0;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
+        loc = loc + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+        if (t >= kTileRows) atomicAdd(&n_long, 1);
+    }
+    Int3 tot;
+    Int3 run = block_excl_scan3<NT>(loc, scan3, tot);
+    for (int k = s0; k < s1; ++k) {
+        int t = 0;
+        int base = run.a;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) {
+            const int c = tab[k * W + ww];
+            tab[k * W + ww] = base;
+            base += c;
+            t += c;
+        }
+        seg_idx[k] = run.b;
+        tile_off[k] = run.c;
+        start[k] = run.a;
+        if (t > 0) {
+            out.seg_offsets[run.b] = run.a;
+            out.seg_slot[run.b] = k;
+        }
+        run = run + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+    }
+    __syncthreads();
+    if (active) {
+        const int pos = tab[key * W + w] + rank;
+        const int st = start[key];
+        const int len = (key + 1 < S ? start[key + 1] : tot.a) - st;
+        const int q = pos - st;
+        out.sorted_rows[pos] = tid;
+        const int t = tile_off[key] + q / kTileRows, j = q % kTileRows;
+        int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+        rec[kRecRowIds + j] = tid;
+        if (j == 0) write_tile_header(rec, key, pos, min(kTileRows, len - q), len, seg_idx[key]);
+    }
+    if (tid == 0) {
+        out.seg_offsets[tot.b] = tot.a;
+        out.counts[0] = tot.a;
+        out.counts[1] = tot.b;
+        out.counts[2] = n_invalid;
+        out.counts[3] = n_long;
+        out.counts[4] = tot.c;
+        out.counts[5] = out.counts[6] = out.counts[7] = 0;
+    }
+    for (int t = tot.c + tid; t < out.tile_bound; t += NT)
+        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0);
+}
+
+static int small_threads(int n) { return n <= 64 ? 64 : (n <= 256 ? 256 : 1024); }
+
+// Past 256 rows with many slots, up to 64 distinct slots per wave make the
+// per-wave ranking slower than the radix path.
+static bool small_fits(int n, int S) {
+    return n <= kMT && S <= kSmallMaxSlots && (long long)(small_threads(n) / kWave) * S <= kSmallTable &&
+           (n <= 256 || S <= kSmallBallotSlots);
+}
+
+static size_t small_lds(int n, int S) { return ((size_t)S * (small_threads(n) / kWave) + 3 * (size_t)S) * sizeof(int); }
+
 int meta_chunks(int n) { return n <= 0 ? 1 : (n + kMT - 1) / kMT; }
 
 size_t meta_dyn_lds(int n, int S) { return meta_chunks(n) > 1 ? (size_t)4 * S * sizeof(int) : 0; }
 
+template <int NT, class Src>
+static hipError_t launch_small(Src src, int n, int S, MetaOut out, hipStream_t st) {
+    const size_t dyn = small_lds(n, S);
+    if (dyn > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_small_kernel<NT, Src>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    hipLaunchKernelGGL((meta_small_kernel<NT, Src>), dim3(1), dim3(NT), dyn, st, src, n, S, out);
+    return hipGetLastError();
+}
+
 template <class Src>
 static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hipStream_t st) {
+    if (small_fits(n, S)) {
+        switch (small_threads(n)) {
+        case 64: return launch_small<64>(src, n, S, out, st);
+        case 256: return launch_small<256>(src, n, S, out, st);
+        default: return launch_small<1024>(src, n, S, out, st);
+        }
+    }
     const int chunks = meta_chunks(n);
     const size_t dyn = meta_dyn_lds(n, S);
     if (dyn > 64 * 1024)
