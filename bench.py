@@ -44,7 +44,7 @@ METRIC = "effective HBM GB/s and tokens/sec of routed LoRA delta (% of peak), 1 
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_traffic.txt")
-KERNEL_SOURCES = ["common.h", "kernels.h", "delta.hip"]
+KERNEL_SOURCES = ["common.h", "kernels.h", "ops.h", "fused.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -143,10 +143,14 @@ def main():
     sets = []
     base = dict(x=d16(case.x), a=d16(case.a_pool), b=d16(case.b_pool), y=d16(case.y),
                 scale=torch.from_numpy(case.scale).cuda(), slot=torch.from_numpy(case.slot).cuda())
+    # the data rotates over independent copies; the metadata buffers and the
+    # workspace are one set reused by every step, as a serving loop reuses them
+    meta = B.LoraMeta.allocate(case.n, case.num_slots)
+    ws = B.fused_workspace(case.n, case.num_slots, case.num_slices, case.max_rank, case.k_in)
     for _ in range(copies):
         s = {k: v.clone() for k, v in base.items()}
-        s["meta"] = B.LoraMeta.allocate(case.n, case.num_slots)
-        s["ws"] = B.fused_workspace(case.n, case.num_slots, case.num_slices, case.max_rank, case.k_in)
+        s["meta"] = meta
+        s["ws"] = ws
         sets.append(s)
     del base
 
