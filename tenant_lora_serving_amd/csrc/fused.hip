@@ -292,6 +292,71 @@ struct XaSrc {
     int *ok;  // LDS
 };
 
+// Rows jb .. jb+3 of a vector-ALU expand (jb a compile-time multiple of 4;
+// rows past m are computed from row m - 1's xa and not stored): both of the
+// lane's columns over all R ranks.  Ranks 0..31 are already in bq; later
+// blocks are loaded here, as are ranks 0..31 again for jb > 0 when R > 32.
+template <int JB, class Op>
+__device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, int c, bool cok, bool add_inputs,
+                                           const uint16_t *bp, int R, u32x4_t (&bq)[2][4],
+                                           const uint32_t (&yv)[kTileRows], const float *xf) {
+    float o0[4] = {0.f, 0.f, 0.f, 0.f}, o1[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < R; r0 += 32) {
+        if (r0 > 0 || (JB > 0 && R > 32)) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    bq[cc][q] = (bp && r0 + 8 * q < R) ? ld16(bp + cc * R + r0 + 8 * q) : zero4();
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int rh = r0 + 16 * half;
+            if (rh < R) {
+                float b0[16], b1[16];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const u32x4_t u0 = bq[0][2 * half + q], u1 = bq[1][2 * half + q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        b0[8 * q + 2 * e] = bf_lo(u0[e]);
+                        b0[8 * q + 2 * e + 1] = bf_hi(u0[e]);
+                        b1[8 * q + 2 * e] = bf_lo(u1[e]);
+                        b1[8 * q + 2 * e + 1] = bf_hi(u1[e]);
+                    }
+                }
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    if (rh + 4 * q4 >= R) break;  // R is a multiple of 8, not always of 16
+                    f32x4_t xa4[4];              // one batch of uniform-address LDS reads
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xa4[j] = *reinterpret_cast<const f32x4_t *>(xf + min(JB + j, m - 1) * R + rh + 4 * q4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            o0[j] = __builtin_fmaf(xa4[j][e], b0[4 * q4 + e], o0[j]);
+                            o1[j] = __builtin_fmaf(xa4[j][e], b1[4 * q4 + e], o1[j]);
+                        }
+                }
+            }
+        }
+    }
+    if (!cok) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (JB + j < m) {
+            float v0 = o0[j], v1 = o1[j];
+            if (add_inputs) {
+                v0 += bf_lo(yv[JB + j]);
+                v1 += bf_hi(yv[JB + j]);
+            }
+            *reinterpret_cast<uint32_t *>(op.yrow(hdr_row(h, JB + j)) + c) = pack_bf16x2(v0, v1);
+        }
+    }
+}
+
 // Vector-ALU expand: lane owns columns c, c+1 of [c0, c1) (c = c0 + 128w + 2 lane).
 template <class Op>
 __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
@@ -316,75 +381,11 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
     stage_xa<false>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.tag, xs.ctl, lds);
     __syncthreads();
     const float *xf = reinterpret_cast<const float *>(lds);
-    // rows in two blocks of 8, ranks in blocks of 32 held as packed bf16 (bq)
-    // and widened 16 at a time
-#pragma unroll
-    for (int jb = 0; jb < kTileRows; jb += 8) {
-        if (jb >= m) break;
-        float o0[8], o1[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o0[j] = o1[j] = 0.f;
-        for (int r0 = 0; r0 < R; r0 += 32) {
-            if (r0 > 0 || (jb > 0 && R > 32)) {
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        bq[cc][q] = (bp && r0 + 8 * q < R) ? ld16(bp + cc * R + r0 + 8 * q) : zero4();
-            }
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int rh = r0 + 16 * half;
-                if (rh < R) {
-                    float b0[16], b1[16];
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const u32x4_t u0 = bq[0][2 * half + q], u1 = bq[1][2 * half + q];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            b0[8 * q + 2 * e] = bf_lo(u0[e]);
-                            b0[8 * q + 2 * e + 1] = bf_hi(u0[e]);
-                            b1[8 * q + 2 * e] = bf_lo(u1[e]);
-                            b1[8 * q + 2 * e + 1] = bf_hi(u1[e]);
-                        }
-                    }
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        if (rh + 4 * q4 >= R) break;  // R is a multiple of 8, not always of 16
-                        // the 8 rows' xa of this rank quad in one batch of LDS reads
-                        // (rows past m read row m - 1 and are not used)
-                        f32x4_t xa4[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            xa4[j] = *reinterpret_cast<const f32x4_t *>(xf + min(jb + j, m - 1) * R + rh + 4 * q4);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            if (jb + j < m) {
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    o0[j] = __builtin_fmaf(xa4[j][e], b0[4 * q4 + e], o0[j]);
-                                    o1[j] = __builtin_fmaf(xa4[j][e], b1[4 * q4 + e], o1[j]);
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        if (cok) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (jb + j < m) {
-                    float v0 = o0[j], v1 = o1[j];
-                    if (add_inputs) {
-                        v0 += bf_lo(yv[jb + j]);
-                        v1 += bf_hi(yv[jb + j]);
-                    }
-                    *reinterpret_cast<uint32_t *>(op.yrow(hdr_row(h, jb + j)) + c) = pack_bf16x2(v0, v1);
-                }
-            }
-        }
-    }
+    // rows in blocks of 4, no per-row branch inside a block
+    if (m > 0) valu_rows4<0>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+    if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+    if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+    if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
 }
 
 // MFMA expand: wave w owns columns c0 + 128w .. +128 as 8 tiles of 16;
@@ -427,17 +428,22 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
         hv[s] = rk < R ? lds16(xl + rk) : zero4();
         lv[s] = rk < R ? lds16(xl + R + rk) : zero4();
     }
+    // all eight column tiles first, so the MFMAs overlap; then the stores
+    f32x4_t d[8];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+        d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NRS; ++s) {
-            d = mfma_16x16x32(bo[ct][s], hv[s], d);
-            d = mfma_16x16x32(bo[ct][s], lv[s], d);
+            d[ct] = mfma_16x16x32(bo[ct][s], hv[s], d[ct]);
+            d[ct] = mfma_16x16x32(bo[ct][s], lv[s], d[ct]);
         }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
         const int cy = cw0 + 16 * ct + 4 * kq;
         if (yp && cy < c1) {
-            float v[4] = {d[0], d[1], d[2], d[3]};
+            float v[4] = {d[ct][0], d[ct][1], d[ct][2], d[ct][3]};
             if (add_inputs) {
                 v[0] += bf_lo(yv[ct].x);
                 v[1] += bf_hi(yv[ct].x);
