@@ -9,10 +9,10 @@
 //
 // Work units (a workgroup of 4 waves each), all shrink units first:
 //   shrink unit (tile t, k piece p): every rank row of the tile's adapter over
-//     k in [512p, 512p + 512); writes an fp32 partial block part[t][p][rr][16]
+//     k in [512p, 512p + 512); writes an fp32 partial block part[t][p][16][rr]
 //     and raises the piece's flag.
-//   expand unit (tile t, column chunk): at most 512 columns of one output
-//     window.  It issues its B and y loads, waits for the tile's P flags, sums
+//   expand unit (tile t, column chunk): at most 512, 1024 or 2048 columns of
+//     one output window (more for larger calls), in batches of 512.  It issues its B and y loads, waits for the tile's P flags, sums
 //     the P partials in piece order (bitwise reproducible), scales, and adds
 //     xa @ B^T to y.
 // A consumer only waits on producers with lower workgroup ids, which never
@@ -52,12 +52,14 @@
 #include "kernels.h"
 #include "ops.h"
 
+#include <algorithm>
+
 namespace tl {
 
 constexpr int kFT = 256;      // threads per workgroup
 constexpr int kKP = 512;      // k per shrink unit
 constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x tile
-constexpr int kEC = 512;      // output columns per expand unit (128 per wave)
+constexpr int kEB = 512;      // output columns per expand batch (128 per wave); a unit has 1, 2 or 4
 constexpr int kSpinLimit = 1 << 22;
 // control line of the workspace
 constexpr int kCtlError = 0;  // set when a bounded wait gave up
@@ -107,7 +109,7 @@ __device__ __forceinline__ void store_x(const u32x4_t (&xv)[4], uint16_t *xs) {
 }
 __device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 
-// Vector-ALU shrink of one unit into pu[rr * 16 + j] (rr < n_rr, j < m).
+// Vector-ALU shrink of one unit into pu[j * n_rr + rr] (rr < n_rr, j < m).
 // Lane (rl = lane / 16, kl = lane % 16) of wave w holds rank rows
 // rb + 4w + rl + 16i (i < RPL) at k = k0 + 128s + 8kl (s < 4).
 template <int RPL, class Op>
@@ -173,7 +175,7 @@ __device__ __forceinline__ void shrink_valu(const Op &op, const Hdr &h, int k0, 
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int j = 4 * b + jj;
-            if (kl < 4 * RPL && rr < n_rr && j < m) store_word64(pu + rr * 16 + j, tagged(sv[b], tag));
+            if (kl < 4 * RPL && rr < n_rr && j < m) store_word64(pu + j * n_rr + rr, tagged(sv[b], tag));
         }
     }
 }
@@ -213,7 +215,7 @@ __device__ __forceinline__ void shrink_mfma(const Op &op, const Hdr &h, int k0, 
         if (rr < n_rr) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (4 * kq + i < h.m) store_word64(pu + rr * 16 + 4 * kq + i, tagged(acc[i], tag));
+                if (4 * kq + i < h.m) store_word64(pu + (4 * kq + i) * n_rr + rr, tagged(acc[i], tag));
         }
     }
 }
@@ -246,11 +248,13 @@ template <bool MF>
 __device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, int xb, int R, int m, float sc,
                                          uint32_t tag, int *ctl, char *lds) {
     const int64_t pstride = (int64_t)n_rr * 16;
+    // thread -> (row j, rank r) with r fastest: one pass covers 256 / R rows,
+    // and a wave's loads of one piece are contiguous words
     for (int idx = threadIdx.x; idx < R * 16; idx += kFT) {
-        const int r = idx >> 4, j = idx & 15;
+        const int j = idx / R, r = idx - j * R;
         float s = 0.f;
         if (j < m) {
-            const uint64_t *q = pt + (int64_t)(xb * R + r) * 16 + j;
+            const uint64_t *q = pt + (int64_t)j * n_rr + xb * R + r;
             for (int p0 = 0; p0 < P; p0 += 8) {
                 // eight loads in flight (indices past P repeat piece P - 1 and are not summed)
                 uint64_t v[8];
@@ -357,47 +361,73 @@ __device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, in
     }
 }
 
-// Vector-ALU expand: lane owns columns c, c+1 of [c0, c1) (c = c0 + 128w + 2 lane).
+// Vector-ALU expand of columns [c0, c1) in batches of kEB: in a batch, lane
+// owns columns c, c+1 (c = batch start + 128w + 2 lane).  The first batch's B
+// and y are loaded before the wait; each later batch's are loaded while the
+// previous batch computes.
+template <class Op>
+__device__ __forceinline__ void valu_load(const Op &op, const Hdr &h, int c, int c1, int R, bool add_inputs,
+                                          const uint16_t *&bp, u32x4_t (&bq)[2][4], uint32_t (&yv)[kTileRows]) {
+    const bool cok = c < c1;
+    bp = cok ? op.brow(h.slot, c) : nullptr;  // rows c and c+1 are adjacent
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bq[cc][q] = (bp && 8 * q < R) ? ld16(bp + cc * R + 8 * q) : zero4();
+#pragma unroll
+    for (int j = 0; j < kTileRows; ++j)
+        yv[j] = (add_inputs && cok && j < h.m) ? *reinterpret_cast<const uint32_t *>(op.yrow(hdr_row(h, j)) + c)
+                                                : 0u;
+}
+
 template <class Op>
 __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                             const XaSrc &xs, char *lds) {
     const int lane = lane_id(), w = wave_id();
     const int R = op.R, m = h.m;
-    const int c = c0 + 128 * w + 2 * lane;
-    const bool cok = c < c1;
-    const uint16_t *bp = cok ? op.brow(h.slot, c) : nullptr;  // rows c and c+1 are adjacent
-    u32x4_t bq[2][4];  // ranks 0..31 of both columns, in flight during the wait
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bq[cc][q] = (bp && 8 * q < R) ? ld16(bp + cc * R + 8 * q) : zero4();
+    const int nb = (c1 - c0 + kEB - 1) / kEB;
+    const uint16_t *bp;
+    u32x4_t bq[2][4];  // ranks 0..31 of both columns
     uint32_t yv[kTileRows];
-#pragma unroll
-    for (int j = 0; j < kTileRows; ++j)
-        yv[j] = (add_inputs && cok && j < m)
-                    ? *reinterpret_cast<const uint32_t *>(op.yrow(hdr_row(h, j)) + c)
-                    : 0u;
+    valu_load(op, h, c0 + 128 * w + 2 * lane, c1, R, add_inputs, bp, bq, yv);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
     stage_xa<false>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.tag, xs.ctl, lds);
     __syncthreads();
     const float *xf = reinterpret_cast<const float *>(lds);
-    // rows in blocks of 4, no per-row branch inside a block
-    if (m > 0) valu_rows4<0>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-    if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-    if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-    if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+    for (int b = 0; b < nb; ++b) {
+        const int c = c0 + kEB * b + 128 * w + 2 * lane;
+        const bool cok = c < c1;
+        const uint16_t *bp_n = nullptr;
+        u32x4_t bq_n[2][4];
+        uint32_t yv_n[kTileRows];
+        if (b + 1 < nb) valu_load(op, h, c + kEB, c1, R, add_inputs, bp_n, bq_n, yv_n);
+        // rows in blocks of 4, no per-row branch inside a block
+        if (m > 0) valu_rows4<0>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (b + 1 < nb) {
+            bp = bp_n;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bq[cc][q] = bq_n[cc][q];
+#pragma unroll
+            for (int j = 0; j < kTileRows; ++j) yv[j] = yv_n[j];
+        }
+    }
 }
 
-// MFMA expand: wave w owns columns c0 + 128w .. +128 as 8 tiles of 16;
+// MFMA expand of columns [c0, c1) in batches of kEB: in a batch, wave w owns
+// columns start + 128w .. +128 as 8 tiles of 16;
 // D[column][tile row] = B[column][ranks] . (xa_hi + xa_lo)[tile row][ranks]
-// as two bf16 MFMAs per 32 ranks (NRS rank steps).
+// as two bf16 MFMAs per 32 ranks (NRS rank steps).  A later batch's B and y
+// are loaded once the MFMAs have consumed the previous batch's B.
 template <int NRS, class Op>
-__device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
-                                            const XaSrc &xs, char *lds) {
-    const int lane = lane_id(), w = wave_id();
+__device__ __forceinline__ void mfma_load_b(const Op &op, const Hdr &h, int cw0, int c1, int R,
+                                            u32x4_t (&bo)[8][NRS]) {
+    const int lane = lane_id();
     const int col = lane & 15, kq = lane >> 4;
-    const int R = op.R, cw0 = c0 + 128 * w;
-    u32x4_t bo[8][NRS];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
         const int cc = cw0 + 16 * ct + col;
@@ -408,15 +438,30 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
             bo[ct][s] = (bp && rk < R) ? ld16(bp + rk) : zero4();
         }
     }
-    // output row = col, columns cw0 + 16ct + 4kq .. +4 (8 bytes)
-    const int rid = __shfl(h.rec, kRecRowIds + col, kWave);
-    uint16_t *yp = col < h.m ? op.yrow(rid) : nullptr;
-    uint2 yv[8];
+}
+__device__ __forceinline__ void mfma_load_y(const uint16_t *yp, int cw0, int c1, bool add_inputs, uint2 (&yv)[8]) {
+    const int kq = lane_id() >> 4;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
         const int cy = cw0 + 16 * ct + 4 * kq;
         yv[ct] = (add_inputs && yp && cy < c1) ? *reinterpret_cast<const uint2 *>(yp + cy) : make_uint2(0u, 0u);
     }
+}
+
+template <int NRS, class Op>
+__device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
+                                            const XaSrc &xs, char *lds) {
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 15, kq = lane >> 4;
+    const int R = op.R;
+    const int nb = (c1 - c0 + kEB - 1) / kEB;
+    // output row = col, columns cw0 + 16ct + 4kq .. +4 (8 bytes)
+    const int rid = __shfl(h.rec, kRecRowIds + col, kWave);
+    uint16_t *yp = col < h.m ? op.yrow(rid) : nullptr;
+    u32x4_t bo[8][NRS];
+    uint2 yv[8];
+    mfma_load_b<NRS>(op, h, c0 + 128 * w, c1, R, bo);
+    mfma_load_y(yp, c0 + 128 * w, c1, add_inputs, yv);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
     stage_xa<true>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.tag, xs.ctl, lds);
     __syncthreads();
@@ -428,37 +473,50 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
         hv[s] = rk < R ? lds16(xl + rk) : zero4();
         lv[s] = rk < R ? lds16(xl + R + rk) : zero4();
     }
-    // all eight column tiles first, so the MFMAs overlap; then the stores
-    f32x4_t d[8];
+    for (int b = 0; b < nb; ++b) {
+        const int cw0 = c0 + kEB * b + 128 * w;
+        // all eight column tiles first, so the MFMAs overlap; then the stores
+        f32x4_t d[8];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < 8; ++ct) {
+            d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NRS; ++s) {
-            d[ct] = mfma_16x16x32(bo[ct][s], hv[s], d[ct]);
-            d[ct] = mfma_16x16x32(bo[ct][s], lv[s], d[ct]);
-        }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        const int cy = cw0 + 16 * ct + 4 * kq;
-        if (yp && cy < c1) {
-            float v[4] = {d[ct][0], d[ct][1], d[ct][2], d[ct][3]};
-            if (add_inputs) {
-                v[0] += bf_lo(yv[ct].x);
-                v[1] += bf_hi(yv[ct].x);
-                v[2] += bf_lo(yv[ct].y);
-                v[3] += bf_hi(yv[ct].y);
+            for (int s = 0; s < NRS; ++s) {
+                d[ct] = mfma_16x16x32(bo[ct][s], hv[s], d[ct]);
+                d[ct] = mfma_16x16x32(bo[ct][s], lv[s], d[ct]);
             }
-            *reinterpret_cast<uint2 *>(yp + cy) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+        uint2 yv_n[8];
+        if (b + 1 < nb) {
+            mfma_load_b<NRS>(op, h, cw0 + kEB, c1, R, bo);
+            mfma_load_y(yp, cw0 + kEB, c1, add_inputs, yv_n);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int cy = cw0 + 16 * ct + 4 * kq;
+            if (yp && cy < c1) {
+                float v[4] = {d[ct][0], d[ct][1], d[ct][2], d[ct][3]};
+                if (add_inputs) {
+                    v[0] += bf_lo(yv[ct].x);
+                    v[1] += bf_hi(yv[ct].x);
+                    v[2] += bf_lo(yv[ct].y);
+                    v[3] += bf_hi(yv[ct].y);
+                }
+                *reinterpret_cast<uint2 *>(yp + cy) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+        }
+        if (b + 1 < nb) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) yv[ct] = yv_n[ct];
         }
     }
 }
 
-// Expand chunk cc -> output window l and columns [c0, c1) (chunks of kEC
+// Expand chunk cc -> output window l and columns [c0, c1) (chunks of EC
 // columns, window by window); slice offsets are read at constant indices.
 template <class Op>
-__device__ __forceinline__ void chunk_of(const Op &op, int cc, int &l, int &c0, int &c1) {
+__device__ __forceinline__ void chunk_of(const Op &op, int cc, int EC, int &l, int &c0, int &c1) {
     int base = 0;
     l = -1;
     c0 = c1 = 0;
@@ -466,15 +524,47 @@ __device__ __forceinline__ void chunk_of(const Op &op, int cc, int &l, int &c0, 
     for (int s = 0; s < kMaxSlices; ++s) {
         if (s < op.n_xs() && l < 0) {
             const int a = op.xoff(s), b = op.xoff(s + 1);
-            const int n = (b - a + kEC - 1) / kEC;
+            const int n = (b - a + EC - 1) / EC;
             if (cc < base + n) {
                 l = s;
-                c0 = a + (cc - base) * kEC;
-                c1 = min(b, c0 + kEC);
+                c0 = a + (cc - base) * EC;
+                c1 = min(b, c0 + EC);
             }
             base += n;
         }
     }
+}
+
+// ============================================================ unit order
+// Tiles are taken in groups of GT.  Workgroups run the units in the order
+//   S_0, S_1, E_0, S_2, E_1, ..., S_{G-1}, E_{G-2}, E_{G-1}, then MoE zero rows
+// (S_g: the shrink units of group g, P per tile; E_g: its expand units, C per
+// tile), so a group's consumers start while the next group's producers run
+// and the two phases of a large call overlap.  E_g only waits on S_g, which
+// precedes it.
+constexpr int kUnitShrink = 0, kUnitExpand = 1, kUnitZero = 2;
+struct Unit {
+    int kind, t, sub;
+};
+__device__ __forceinline__ Unit unit_of(int bid, int tile_bound, int P, int C, int GT) {
+    const int G = (tile_bound + GT - 1) / GT;
+    const int nS = GT * P, nE = GT * C;
+    const int n_main = G * (nS + nE);
+    if (bid >= n_main) return Unit{kUnitZero, 0, bid - n_main};
+    int g, local, kind;
+    if (bid < nS) {
+        kind = kUnitShrink, g = 0, local = bid;
+    } else {
+        const int r = bid - nS, q = r / (nS + nE), off = r - q * (nS + nE);
+        if (q < G - 1 && off < nS)
+            kind = kUnitShrink, g = q + 1, local = off;
+        else if (q < G - 1)
+            kind = kUnitExpand, g = q, local = off - nS;
+        else
+            kind = kUnitExpand, g = G - 1, local = off;
+    }
+    const int per = kind == kUnitShrink ? P : C;
+    return Unit{kind, g * GT + local / per, local % per};
 }
 
 // ============================================================ kernel
@@ -482,6 +572,8 @@ struct FusedArgs {
     const int32_t *tiles;
     const int32_t *counts;  // counts[4] = tiles in use
     int tile_bound, P, FP, C;
+    int GT;          // tiles per group of the unit order
+    int EC;          // output columns per expand unit (a multiple of kEB)
     uint64_t *part;  // [tile_bound][P][n_rr][16] tagged partials
     int *ctl;        // control line
     int *flags;      // [tile_bound][FP]: piece flags, then the tile's finished consumers at FP - 1
@@ -493,14 +585,15 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
     __shared__ __align__(16) char lds[kTileRows * kXS * 2 > kTileRows * kMaxRank * 4 ? kTileRows * kXS * 2
                                                                                     : kTileRows * kMaxRank * 4];
     __shared__ int ok;
-    const int bid = blockIdx.x;
     const int P = fa.P, C = fa.C;
-    const int n_shr = fa.tile_bound * P, n_exp = fa.tile_bound * C;
     const int n_rr = op.n_rr();
-    if (bid < n_shr + n_exp) {
+    const Unit un = unit_of(blockIdx.x, fa.tile_bound, P, C, fa.GT);
+    if (un.kind == kUnitShrink || un.kind == kUnitExpand) {
+        const int t = un.t;
+        if (t >= fa.tile_bound) return;
         const uint32_t tag = (uint32_t)load_relaxed(fa.ctl + kCtlGen) + 1u;
-        if (bid < n_shr) {
-            const int t = bid / P, p = bid - t * P;
+        if (un.kind == kUnitShrink) {
+            const int p = un.sub;
             const Hdr h = load_hdr(fa.tiles, t);
             if (h.m == 0) return;
             const int k0 = p * kKP, k1 = min(op.k_in, k0 + kKP);
@@ -516,13 +609,12 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
             if (threadIdx.x == 0) store_relaxed(fa.flags + (int64_t)t * fa.FP + p, (int)tag);
             return;
         }
-        const int e = bid - n_shr;
-        const int t = e / C, cc = e - t * C;
+        const int cc = un.sub;
         const int n_tiles = fa.counts[4];
         const Hdr h = load_hdr(fa.tiles, t);
         if (h.m == 0) return;
         int l, c0, c1;
-        chunk_of(op, cc, l, c0, c1);
+        chunk_of(op, cc, fa.EC, l, c0, c1);
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
                        op.scale_of(h.slot), tag, fa.ctl, &ok};
         if (h.mseg >= fa.mfma_min)
@@ -545,7 +637,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         return;
     }
     // zero rows of pairs that get no delta (MoE only)
-    const int u = bid - n_shr - n_exp;
+    const int u = un.sub;
     const int tid = threadIdx.x;
     const int pair = u * 16 + (tid >> 4);
     if (pair >= zf.n_pairs) return;
@@ -598,7 +690,7 @@ static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, long long gr
 
 template <class Op>
 static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                                  int C, void *ws, int mfma_min, int add_inputs, ZeroFill zf, int zero_units,
+                                  int C, int EC, void *ws, int mfma_min, int add_inputs, ZeroFill zf, int zero_units,
                                   hipStream_t st) {
     char *w = static_cast<char *>(ws);
     FusedArgs fa{};
@@ -608,12 +700,18 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     fa.P = plan.P;
     fa.FP = plan.FP;
     fa.C = C;
+    fa.EC = EC;
     fa.ctl = reinterpret_cast<int *>(w);
     fa.flags = fa.ctl + 64;
     fa.part = reinterpret_cast<uint64_t *>(w + plan.flag_bytes);
     fa.mfma_min = mfma_min;
     fa.add_inputs = add_inputs;
-    const long long grid = (long long)plan.tile_bound * (plan.P + C) + zero_units;
+    // one group: every shrink unit ahead of every expand unit.  (Pipelining
+    // groups of about two workgroups per CU measured slower on the large
+    // configs: consumers that start before their producers hold slots.)
+    fa.GT = std::max(1, plan.tile_bound);
+    const int G = plan.tile_bound > 0 ? (plan.tile_bound + fa.GT - 1) / fa.GT : 0;
+    const long long grid = (long long)G * fa.GT * (plan.P + C) + zero_units;
     if (grid == 0) return hipSuccess;
     switch (rpl_of(op.n_sh * op.R)) {
     case 1: return launch_fused_r<1>(op, fa, grid, zf, st);
@@ -623,10 +721,19 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     }
 }
 
-static int chunks_of(const int *off, int n_windows) {
+static int chunks_of(const int *off, int n_windows, int EC) {
     int c = 0;
-    for (int l = 0; l < n_windows; ++l) c += (off[l + 1] - off[l] + kEC - 1) / kEC;
+    for (int l = 0; l < n_windows; ++l) c += (off[l + 1] - off[l] + EC - 1) / EC;
     return c;
+}
+
+// Columns per expand unit: 512 while that keeps the expand units of a call
+// within about 2048 workgroups, else 1024 or 2048, so that each unit's read
+// of the tile's partials and its fixed chain latency cover more columns.
+static int expand_width(const int *off, int n_windows, int tile_bound) {
+    int ec = kEB;
+    while (ec < 4 * kEB && (long long)tile_bound * chunks_of(off, n_windows, ec) > 2048) ec *= 2;
+    return ec;
 }
 
 hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
@@ -646,9 +753,10 @@ hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t
     op.n_out = d.slice_off[d.num_slices];
     op.col0 = d.offset_start;
     for (int l = 0; l <= kMaxSlices; ++l) op.off[l] = d.slice_off[l < d.num_slices ? l : d.num_slices];
-    const int C = chunks_of(d.slice_off, d.num_slices);
-    return launch_fused_op(op, tiles, counts, plan, C, ws, mfma_min, 1, ZeroFill{nullptr, nullptr, 1, 1, 1, 0}, 0,
-                           st);
+    const int EC = expand_width(d.slice_off, d.num_slices, plan.tile_bound);
+    const int C = chunks_of(d.slice_off, d.num_slices, EC);
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 1, ZeroFill{nullptr, nullptr, 1, 1, 1, 0},
+                           0, st);
 }
 
 hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
@@ -674,8 +782,9 @@ hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32
     const ZeroFill zf{m.topk_ids, m.lora_ids, m.top_k, m.E, m.L, n_pairs};
     const int zero_units = (n_pairs + 15) / 16;
     const int off[3] = {0, m.inter, 2 * m.inter};
-    const int C = chunks_of(off, 2);
-    return launch_fused_op(op, tiles, counts, plan, C, ws, mfma_min, 0, zf, zero_units, st);
+    const int EC = expand_width(off, 2, plan.tile_bound);
+    const int C = chunks_of(off, 2, EC);
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 0, zf, zero_units, st);
 }
 
 }  // namespace tl
