@@ -59,6 +59,8 @@ namespace tl {
 constexpr int kFT = 256;      // threads per workgroup
 constexpr int kKP = 512;      // k per shrink unit
 constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x tile
+constexpr int kXaBytes = kTileRows * kMaxRank * 4;  // LDS for a tile's xa (fp32, or bf16 hi/lo pairs)
+constexpr int kBStage = 128 * 32 + (128 * 32 / 128) * 8;  // bf16 per wave: 128 columns x 32 ranks + padding
 constexpr int kEB = 512;      // output columns per expand batch (128 per wave); a unit has 1, 2 or 4
 constexpr int kSpinLimit = 1 << 22;
 // control line of the workspace
@@ -290,6 +292,7 @@ struct XaSrc {
     const uint64_t *pt;  // the tile's partial blocks
     const int *flags;    // the tile's piece flags
     int P, xb;
+    bool coalesce_b;     // VALU expand: stage B through LDS with coalesced loads
     float sc;
     uint32_t tag;
     int *ctl;
@@ -365,19 +368,67 @@ __device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, in
 // owns columns c, c+1 (c = batch start + 128w + 2 lane).  The first batch's B
 // and y are loaded before the wait; each later batch's are loaded while the
 // previous batch computes.
+//
+// B in large calls (R <= 32): a wave's 128 columns are 128 * R consecutive
+// bf16, read with R / 4 fully coalesced 1 KB instructions (chunk i = lane +
+// 64u) and handed to the owning lanes through the wave's LDS stage (16 bytes
+// of padding per 256 keep both the writes and the reads free of bank
+// conflicts).  Otherwise each lane reads its two B rows directly: 64 lines of
+// 16 bytes per instruction cost more L2 requests but no LDS round trip, which
+// is what a decode-sized call is short of.
+__device__ __forceinline__ int bstage_off(int i) { return i * 8 + (i >> 4) * 8; }  // chunk i -> bf16 offset
+
 template <class Op>
-__device__ __forceinline__ void valu_load(const Op &op, const Hdr &h, int c, int c1, int R, bool add_inputs,
-                                          const uint16_t *&bp, u32x4_t (&bq)[2][4], uint32_t (&yv)[kTileRows]) {
-    const bool cok = c < c1;
-    bp = cok ? op.brow(h.slot, c) : nullptr;  // rows c and c+1 are adjacent
+__device__ __forceinline__ void valu_load_raw(const Op &op, const Hdr &h, int cw, int c1, int R,
+                                              u32x4_t (&raw)[8]) {
+    const int lane = lane_id();
+    const uint16_t *base = cw < c1 ? op.brow(h.slot, cw) : nullptr;
+    const int nl = R >> 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = lane + 64 * u;
+        const bool ok = base && u < nl && cw + (i * 8) / R < c1;
+        raw[u] = ok ? ld16(base + i * 8) : zero4();
+    }
+}
+
+__device__ __forceinline__ void valu_transpose(const u32x4_t (&raw)[8], int R, uint16_t *bst,
+                                               u32x4_t (&bq)[2][4]) {
+    const int lane = lane_id();
+    const int nl = R >> 2, cpr = R >> 3;  // loads per wave, 16-byte chunks per B row
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (u < nl) *reinterpret_cast<u32x4_t *>(bst + bstage_off(lane + 64 * u)) = raw[u];
+    // the wave reads what its own lanes wrote: LDS operations of a wave complete
+    // in order, and the wave barrier keeps the compiler from reordering them
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            bq[cc][q] = q < cpr ? *reinterpret_cast<const u32x4_t *>(bst + bstage_off((2 * lane + cc) * cpr + q))
+                                : zero4();
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <class Op>
+__device__ __forceinline__ void valu_load_b(const Op &op, const Hdr &h, int c, int c1, int R, const uint16_t *&bp,
+                                            u32x4_t (&bq)[2][4]) {
+    bp = c < c1 ? op.brow(h.slot, c) : nullptr;  // rows c and c+1 are adjacent
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int q = 0; q < 4; ++q) bq[cc][q] = (bp && 8 * q < R) ? ld16(bp + cc * R + 8 * q) : zero4();
+}
+
+template <class Op>
+__device__ __forceinline__ void valu_load_y(const Op &op, const Hdr &h, int c, int c1, bool add_inputs,
+                                            uint32_t (&yv)[kTileRows]) {
 #pragma unroll
     for (int j = 0; j < kTileRows; ++j)
-        yv[j] = (add_inputs && cok && j < h.m) ? *reinterpret_cast<const uint32_t *>(op.yrow(hdr_row(h, j)) + c)
-                                                : 0u;
+        yv[j] = (add_inputs && c < c1 && j < h.m)
+                    ? *reinterpret_cast<const uint32_t *>(op.yrow(hdr_row(h, j)) + c)
+                    : 0u;
 }
 
 template <class Op>
@@ -386,32 +437,50 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
     const int lane = lane_id(), w = wave_id();
     const int R = op.R, m = h.m;
     const int nb = (c1 - c0 + kEB - 1) / kEB;
-    const uint16_t *bp;
-    u32x4_t bq[2][4];  // ranks 0..31 of both columns
+    const bool tr = xs.coalesce_b && R <= 32;
+    const uint16_t *bp = nullptr;
+    u32x4_t raw[8], bq[2][4];  // B: coalesced chunks, then ranks 0..31 of the lane's two columns
     uint32_t yv[kTileRows];
-    valu_load(op, h, c0 + 128 * w + 2 * lane, c1, R, add_inputs, bp, bq, yv);
+    const int cl = 128 * w + 2 * lane;
+    if (tr)
+        valu_load_raw(op, h, c0 + 128 * w, c1, R, raw);
+    else
+        valu_load_b(op, h, c0 + cl, c1, R, bp, bq);
+    valu_load_y(op, h, c0 + cl, c1, add_inputs, yv);
+    // the first batch's B reaches its lanes while the producers still run
+    uint16_t *bst = reinterpret_cast<uint16_t *>(lds + kXaBytes) + w * kBStage;
+    if (tr) valu_transpose(raw, R, bst, bq);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
     stage_xa<false>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.tag, xs.ctl, lds);
     __syncthreads();
     const float *xf = reinterpret_cast<const float *>(lds);
     for (int b = 0; b < nb; ++b) {
-        const int c = c0 + kEB * b + 128 * w + 2 * lane;
+        const int c = c0 + kEB * b + cl;
         const bool cok = c < c1;
+        if (tr && b > 0) valu_transpose(raw, R, bst, bq);
         const uint16_t *bp_n = nullptr;
         u32x4_t bq_n[2][4];
         uint32_t yv_n[kTileRows];
-        if (b + 1 < nb) valu_load(op, h, c + kEB, c1, R, add_inputs, bp_n, bq_n, yv_n);
+        if (b + 1 < nb) {
+            if (tr)
+                valu_load_raw(op, h, c0 + kEB * (b + 1) + 128 * w, c1, R, raw);
+            else
+                valu_load_b(op, h, c + kEB, c1, R, bp_n, bq_n);
+            valu_load_y(op, h, c + kEB, c1, add_inputs, yv_n);
+        }
         // rows in blocks of 4, no per-row branch inside a block
         if (m > 0) valu_rows4<0>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (b + 1 < nb) {
-            bp = bp_n;
+            if (!tr) {
+                bp = bp_n;
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
+                for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) bq[cc][q] = bq_n[cc][q];
+                    for (int q = 0; q < 4; ++q) bq[cc][q] = bq_n[cc][q];
+            }
 #pragma unroll
             for (int j = 0; j < kTileRows; ++j) yv[j] = yv_n[j];
         }
@@ -582,8 +651,9 @@ struct FusedArgs {
 
 template <int RPL, int NRS, class Op>
 __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
-    __shared__ __align__(16) char lds[kTileRows * kXS * 2 > kTileRows * kMaxRank * 4 ? kTileRows * kXS * 2
-                                                                                    : kTileRows * kMaxRank * 4];
+    // shrink units: the staged x tile; expand units: xa, then the waves' B stages
+    constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = kXaBytes + 4 * kBStage * 2;
+    __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     __shared__ int ok;
     const int P = fa.P, C = fa.C;
     const int n_rr = op.n_rr();
@@ -616,7 +686,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         int l, c0, c1;
         chunk_of(op, cc, fa.EC, l, c0, c1);
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
-                       op.scale_of(h.slot), tag, fa.ctl, &ok};
+                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok};
         if (h.mseg >= fa.mfma_min)
             expand_mfma<NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         else

@@ -94,6 +94,10 @@ SMALL = [
     dict(seed=5, n=33, k_in=512, slices=(1024,), S=2, R=128),     # largest rank
     dict(seed=6, n=129, k_in=128, slices=(8, 8, 8, 8, 8, 8, 8, 8), S=5, R=8),   # 8 slices
     dict(seed=7, n=1500, k_in=256, slices=(256,), S=7, R=16, zipf=True),       # several meta chunks
+    # many tiles: expand units 2048 columns wide in 512-column batches, B staged
+    # through LDS on the vector-ALU path; ragged last batches and windows
+    dict(seed=8, n=2100, k_in=72, slices=(1040, 24), S=2100, R=24),
+    dict(seed=9, n=2400, k_in=64, slices=(2056,), S=2400, R=8),
 ]
 
 
