@@ -44,7 +44,7 @@ METRIC = "effective HBM GB/s and tokens/sec of routed LoRA delta (% of peak), 1 
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_traffic.txt")
-KERNEL_SOURCES = ["common.h", "kernels.h", "ops.h", "fused.hip"]
+KERNEL_SOURCES = ["common.h", "kernels.h", "ops.h", "fused.h", "fused_dense.hip"]
 
 
 def kernel_source_hash() -> str:

@@ -1,4 +1,4 @@
-// fused.hip -- the routed LoRA delta in one launch (shrink, then expand) for
+// fused.h -- the routed LoRA delta in one launch (shrink, then expand) for
 // gfx950, dense and routed-MoE gemm1.
 //
 // Semantics (vLLM punica_base.py, add_lora_linear = add_shrink then
@@ -48,6 +48,8 @@
 //     consecutive bf16) and multiplies them by fp32 xa read from LDS with
 //     uniform addresses; y is read and written 4 bytes per lane, so a wave's
 //     access to one row is 256 contiguous bytes.
+#pragma once
+
 #include "common.h"
 #include "kernels.h"
 #include "ops.h"
@@ -431,13 +433,15 @@ __device__ __forceinline__ void valu_load_y(const Op &op, const Hdr &h, int c, i
                     : 0u;
 }
 
-template <class Op>
+// WIDE: the call's expand units may span several batches (large calls);
+// otherwise a unit is one batch, and none of the next-batch registers exist.
+template <bool WIDE, class Op>
 __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                             const XaSrc &xs, char *lds) {
     const int lane = lane_id(), w = wave_id();
     const int R = op.R, m = h.m;
-    const int nb = (c1 - c0 + kEB - 1) / kEB;
-    const bool tr = xs.coalesce_b && R <= 32;
+    const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
+    const bool tr = WIDE && xs.coalesce_b && R <= 32;
     const uint16_t *bp = nullptr;
     u32x4_t raw[8], bq[2][4];  // B: coalesced chunks, then ranks 0..31 of the lane's two columns
     uint32_t yv[kTileRows];
@@ -461,7 +465,7 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
         const uint16_t *bp_n = nullptr;
         u32x4_t bq_n[2][4];
         uint32_t yv_n[kTileRows];
-        if (b + 1 < nb) {
+        if (WIDE && b + 1 < nb) {
             if (tr)
                 valu_load_raw(op, h, c0 + kEB * (b + 1) + 128 * w, c1, R, raw);
             else
@@ -473,7 +477,7 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
         if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-        if (b + 1 < nb) {
+        if (WIDE && b + 1 < nb) {
             if (!tr) {
                 bp = bp_n;
 #pragma unroll
@@ -517,13 +521,13 @@ __device__ __forceinline__ void mfma_load_y(const uint16_t *yp, int cw0, int c1,
     }
 }
 
-template <int NRS, class Op>
+template <int NRS, bool WIDE, class Op>
 __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                             const XaSrc &xs, char *lds) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
     const int R = op.R;
-    const int nb = (c1 - c0 + kEB - 1) / kEB;
+    const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
     // output row = col, columns cw0 + 16ct + 4kq .. +4 (8 bytes)
     const int rid = __shfl(h.rec, kRecRowIds + col, kWave);
     uint16_t *yp = col < h.m ? op.yrow(rid) : nullptr;
@@ -544,38 +548,44 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
     }
     for (int b = 0; b < nb; ++b) {
         const int cw0 = c0 + kEB * b + 128 * w;
-        // all eight column tiles first, so the MFMAs overlap; then the stores
-        f32x4_t d[8];
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            d[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NRS; ++s) {
-                d[ct] = mfma_16x16x32(bo[ct][s], hv[s], d[ct]);
-                d[ct] = mfma_16x16x32(bo[ct][s], lv[s], d[ct]);
-            }
-        }
         uint2 yv_n[8];
-        if (b + 1 < nb) {
-            mfma_load_b<NRS>(op, h, cw0 + kEB, c1, R, bo);
-            mfma_load_y(yp, cw0 + kEB, c1, add_inputs, yv_n);
-        }
+        // two halves of four column tiles: each half's MFMAs are issued
+        // together, and the second half's overlap the first half's stores
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int cy = cw0 + 16 * ct + 4 * kq;
-            if (yp && cy < c1) {
-                float v[4] = {d[ct][0], d[ct][1], d[ct][2], d[ct][3]};
-                if (add_inputs) {
-                    v[0] += bf_lo(yv[ct].x);
-                    v[1] += bf_hi(yv[ct].x);
-                    v[2] += bf_lo(yv[ct].y);
-                    v[3] += bf_hi(yv[ct].y);
+        for (int hf = 0; hf < 2; ++hf) {
+            f32x4_t d[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                d[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NRS; ++s) {
+                    d[i] = mfma_16x16x32(bo[4 * hf + i][s], hv[s], d[i]);
+                    d[i] = mfma_16x16x32(bo[4 * hf + i][s], lv[s], d[i]);
                 }
-                *reinterpret_cast<uint2 *>(yp + cy) =
-                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+            if (WIDE && hf == 1 && b + 1 < nb) {
+                // the MFMAs above were the last readers of this batch's B
+                mfma_load_b<NRS>(op, h, cw0 + kEB, c1, R, bo);
+                mfma_load_y(yp, cw0 + kEB, c1, add_inputs, yv_n);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ct = 4 * hf + i;
+                const int cy = cw0 + 16 * ct + 4 * kq;
+                if (yp && cy < c1) {
+                    float v[4] = {d[i][0], d[i][1], d[i][2], d[i][3]};
+                    if (add_inputs) {
+                        v[0] += bf_lo(yv[ct].x);
+                        v[1] += bf_hi(yv[ct].x);
+                        v[2] += bf_lo(yv[ct].y);
+                        v[3] += bf_hi(yv[ct].y);
+                    }
+                    *reinterpret_cast<uint2 *>(yp + cy) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
             }
         }
-        if (b + 1 < nb) {
+        if (WIDE && b + 1 < nb) {
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) yv[ct] = yv_n[ct];
         }
@@ -649,10 +659,10 @@ struct FusedArgs {
     int mfma_min, add_inputs;
 };
 
-template <int RPL, int NRS, class Op>
+template <int RPL, int NRS, bool WIDE, class Op>
 __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
-    constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = kXaBytes + 4 * kBStage * 2;
+    constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = WIDE ? kXaBytes + 4 * kBStage * 2 : kXaBytes;
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     __shared__ int ok;
     const int P = fa.P, C = fa.C;
@@ -688,9 +698,9 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
                        fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok};
         if (h.mseg >= fa.mfma_min)
-            expand_mfma<NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+            expand_mfma<NRS, WIDE>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         else
-            expand_valu(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+            expand_valu<WIDE>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         // the last consumer of a tile counts the tile as finished; the last
         // finished tile of the call advances the generation (two levels, so
         // no single address takes one atomic per consumer)
@@ -726,26 +736,15 @@ static int tile_bound_of(int n, int S) {
     return (int)(a < n ? a : n);
 }
 
-// Workspace: [control line, 256 B] [per tile: P piece flags .. finished consumers, FP int]
-// [tagged partials: tile_bound x P x n_rr x 16 uint64].
-FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out) {
-    (void)n_out;
-    FusedPlan p{};
-    p.tile_bound = tile_bound_of(n, num_slots);
-    p.P = (k_in + kKP - 1) / kKP;
-    p.FP = (int)align_up((size_t)p.P + 1, 64);
-    p.flag_bytes = align_up(256 + (size_t)p.tile_bound * p.FP * sizeof(int), 256);
-    p.part_bytes = align_up((size_t)p.tile_bound * p.P * n_sh * R * kTileRows * sizeof(uint64_t), 256);
-    p.total_bytes = p.flag_bytes + p.part_bytes;
-    return p;
-}
-
 static int rpl_of(int n_rr) { return n_rr >= 64 ? 4 : (n_rr + 15) / 16; }
 static int nrs_of(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }
 
 template <int RPL, int NRS, class Op>
 static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, long long grid, ZeroFill zf, hipStream_t st) {
-    hipLaunchKernelGGL((fused_kernel<RPL, NRS, Op>), dim3((unsigned)grid), dim3(kFT), 0, st, op, fa, zf);
+    if (fa.EC > kEB)
+        hipLaunchKernelGGL((fused_kernel<RPL, NRS, true, Op>), dim3((unsigned)grid), dim3(kFT), 0, st, op, fa, zf);
+    else
+        hipLaunchKernelGGL((fused_kernel<RPL, NRS, false, Op>), dim3((unsigned)grid), dim3(kFT), 0, st, op, fa, zf);
     return hipGetLastError();
 }
 
@@ -804,57 +803,6 @@ static int expand_width(const int *off, int n_windows, int tile_bound) {
     int ec = kEB;
     while (ec < 4 * kEB && (long long)tile_bound * chunks_of(off, n_windows, ec) > 2048) ec *= 2;
     return ec;
-}
-
-hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                        void *ws, int mfma_min, hipStream_t st) {
-    DenseOp op{};
-    op.x = d.x;
-    op.ldx = d.ldx;
-    op.a_pool = d.a_pool;
-    op.b_pool = d.b_pool;
-    op.scale = d.scale;
-    op.y = d.y;
-    op.ldy = d.ldy;
-    op.k_in = d.k_in;
-    op.R = d.R;
-    op.n_sh = d.num_slices;
-    op.n_sl = d.num_slices;
-    op.n_out = d.slice_off[d.num_slices];
-    op.col0 = d.offset_start;
-    for (int l = 0; l <= kMaxSlices; ++l) op.off[l] = d.slice_off[l < d.num_slices ? l : d.num_slices];
-    const int EC = expand_width(d.slice_off, d.num_slices, plan.tile_bound);
-    const int C = chunks_of(d.slice_off, d.num_slices, EC);
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 1, ZeroFill{nullptr, nullptr, 1, 1, 1, 0},
-                           0, st);
-}
-
-hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                            void *ws, int mfma_min, hipStream_t st) {
-    MoeOp op{};
-    op.x = m.x;
-    op.ldx = m.ldx;
-    op.top_k = m.top_k;
-    op.wa = m.w_ptr_a;
-    op.lsa = m.lora_stride_a;
-    op.wb = m.w_ptr_b;
-    op.lsb = m.lora_stride_b;
-    op.out = m.out;
-    op.sc = m.scale;
-    op.k_in = m.H;
-    op.R = m.R;
-    op.n_sh = m.shared_a ? 1 : 2;
-    op.n_out = 2 * m.inter;
-    op.E = m.E;
-    op.inter = m.inter;
-    op.shared = m.shared_a ? 1 : 0;
-    const int n_pairs = m.T * m.top_k;
-    const ZeroFill zf{m.topk_ids, m.lora_ids, m.top_k, m.E, m.L, n_pairs};
-    const int zero_units = (n_pairs + 15) / 16;
-    const int off[3] = {0, m.inter, 2 * m.inter};
-    const int EC = expand_width(off, 2, plan.tile_bound);
-    const int C = chunks_of(off, 2, EC);
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 0, zf, zero_units, st);
 }
 
 }  // namespace tl
