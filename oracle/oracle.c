@@ -19,6 +19,9 @@
  *  - FlashInfer docs, flashinfer.fused_moe.bgmv_moe_gemm1_lora_delta: the
  *    per-(token, slot) gate/up formula, the shared-A form, the w_ptr tables
  *    and lora_stride, lora_ids = -1 meaning no adapter.
+ *  - vLLM "punica_base.py", PunicaWrapperBase.add_lora_w2: the w2 LoRA
+ *    applied in place to the per-(token, slot) down-projection output
+ *    (intermediate_cache3) before moe_sum, routed as add_lora_w13.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): a slot >= num_slots is excluded and counted as invalid; segments
@@ -274,6 +277,58 @@ void oracle_moe_gemm1_pairs(const uint16_t *x, int64_t ldx, int32_t H,
                     d += bf(B[c * rank + r]) * u[r];
                 o[c] = scale * d;
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * O-moe-w2, evaluated at the listed pairs p = t*top_k + j.  With l =
+ * lora_ids[t], e = topk_ids[p] and w = topk_weights[p] (1 when no weights
+ * are given):
+ *   l < 0, l >= L, e < 0 or e >= E:  out[q][:] = y[p][:]
+ *   otherwise, A = w_ptr_a[e] + l*lora_stride_a ([rank][I]),
+ *              B = w_ptr_b[e] + l*lora_stride_b ([H][rank]):
+ *       xa[r]      = (w * scale) * sum_i A[r][i] * x2[p][i]
+ *       out[q][c]  = y[p][c] + sum_r xa[r] * B[c][r],   c < H
+ * (the same association as O-shrink then O-expand, so with E = 1, top_k = 1
+ * and no weights it is the dense delta bit for bit).
+ * ------------------------------------------------------------------------ */
+void oracle_moe_w2_pairs(const uint16_t *x2, int64_t ldx, int32_t I,
+                         const int64_t *w_ptr_a, int64_t lora_stride_a,
+                         const int64_t *w_ptr_b, int64_t lora_stride_b,
+                         const int32_t *topk_ids, int32_t top_k, const int32_t *lora_ids,
+                         const float *topk_weights, int32_t num_experts, int32_t num_loras,
+                         int32_t rank, int32_t H, double scale, const uint16_t *y, int64_t ldy,
+                         const int32_t *pairs, int32_t np, double *out)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t q = 0; q < np; ++q) {
+        const int32_t p = pairs[q];
+        const int32_t t = p / top_k;
+        const int32_t l = lora_ids[t];
+        const int32_t e = topk_ids[p];
+        const uint16_t *yp = y + (int64_t)p * ldy;
+        double *o = out + (int64_t)q * H;
+        for (int32_t c = 0; c < H; ++c)
+            o[c] = bf(yp[c]);
+        if (l < 0 || l >= num_loras || e < 0 || e >= num_experts)
+            continue;
+        const double w = topk_weights ? (double)topk_weights[p] : 1.0;
+        const uint16_t *A = (const uint16_t *)(intptr_t)w_ptr_a[e] + (int64_t)l * lora_stride_a;
+        const uint16_t *B = (const uint16_t *)(intptr_t)w_ptr_b[e] + (int64_t)l * lora_stride_b;
+        const uint16_t *xp = x2 + (int64_t)p * ldx;
+        double xa[256];
+        for (int32_t r = 0; r < rank; ++r) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < I; ++i)
+                acc += bf(xp[i]) * bf(A[(int64_t)r * I + i]);
+            xa[r] = (w * scale) * acc;
+        }
+        for (int32_t c = 0; c < H; ++c) {
+            double d = 0.0;
+            for (int32_t r = 0; r < rank; ++r)
+                d += xa[r] * bf(B[(int64_t)c * rank + r]);
+            o[c] += d;
         }
     }
 }

@@ -53,6 +53,11 @@ def _bind(path: str):
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_double, _i32p,
                                          ctypes.c_int32, _f64p]
+    L.oracle_moe_w2_pairs.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int32, _i64p, ctypes.c_int64,
+                                      _i64p, ctypes.c_int64, _i32p, ctypes.c_int32, _i32p, _f32p,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_double, _u16p, ctypes.c_int64, _i32p, ctypes.c_int32,
+                                      _f64p]
     return L
 
 
@@ -215,3 +220,42 @@ def case_moe_pairs(case, shared_a: bool, pairs):
     ta, sa, tb, sb = host_tables(case, shared_a)
     return moe_gemm1_pairs(case.x, ta, sa, tb, sb, shared_a, case.topk_ids, case.lora_ids,
                            case.E, case.L, case.R, case.I, case.scale, pairs)
+
+
+# ---------------------------------------------------------------- MoE w2 (down)
+def moe_w2_pairs(x2, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, topk_ids, lora_ids,
+                 topk_weights, num_experts, num_loras, rank, H, scale, y, pairs):
+    """y rows after the w2 delta for the listed pairs, [len(pairs), H] float64.
+    topk_weights may be None (no routing weight).  The w_ptr tables ([E]) hold
+    HOST addresses of the bf16 banks, which the caller keeps alive."""
+    assert rank <= 256
+    x2 = _c(x2, np.uint16)
+    I = x2.shape[1]
+    y = _c(y, np.uint16)
+    w_ptr_a, w_ptr_b = _c(w_ptr_a, np.int64), _c(w_ptr_b, np.int64)
+    topk_ids, lora_ids = _c(topk_ids, np.int32), _c(lora_ids, np.int32)
+    wts = None if topk_weights is None else _c(topk_weights, np.float32)
+    pairs = _c(pairs, np.int32)
+    out = np.empty((pairs.size, H), dtype=np.float64)
+    lib().oracle_moe_w2_pairs(_p(x2, _u16p), I, I, _p(w_ptr_a, _i64p), lora_stride_a,
+                              _p(w_ptr_b, _i64p), lora_stride_b, _p(topk_ids, _i32p),
+                              topk_ids.shape[1], _p(lora_ids, _i32p),
+                              None if wts is None else _p(wts, _f32p), num_experts, num_loras,
+                              rank, H, float(scale), _p(y, _u16p), y.shape[1], _p(pairs, _i32p),
+                              pairs.size, _p(out, _f64p))
+    return out
+
+
+def host_tables_w2(case):
+    """Host pointer tables ([E]) and element strides over a MoeW2Case's banks."""
+    E, L, R, H, I = case.E, case.L, case.R, case.H, case.I
+    ta = np.array([case.a_down.ctypes.data + e * L * R * I * 2 for e in range(E)], dtype=np.int64)
+    tb = np.array([case.b_down.ctypes.data + e * L * H * R * 2 for e in range(E)], dtype=np.int64)
+    return ta, R * I, tb, H * R
+
+
+def case_moe_w2_pairs(case, pairs, weighted: bool = True, y=None):
+    ta, sa, tb, sb = host_tables_w2(case)
+    return moe_w2_pairs(case.x2, ta, sa, tb, sb, case.topk_ids, case.lora_ids,
+                        case.topk_weights if weighted else None, case.E, case.L, case.R, case.H,
+                        case.scale, case.y if y is None else y, pairs)

@@ -256,4 +256,53 @@ def moe_gemm1(seed: int = 5) -> MoeCase:
                     name="MoE gemm1 T=2048 H=4096 E=64 top8 I=1408 R=16 L=8")
 
 
+# ---------------------------------------------------------------- MoE w2 (down) case
+@dataclass
+class MoeW2Case:
+    name: str
+    T: int
+    H: int
+    E: int
+    top_k: int
+    I: int
+    R: int
+    L: int
+    scale: float
+    topk_ids: np.ndarray      # [T, top_k] int32
+    lora_ids: np.ndarray      # [T] int32, -1 = none
+    topk_weights: np.ndarray  # [T, top_k] float32, each token's weights sum to 1
+    x2: np.ndarray            # [T*top_k, I] uint16: the activation fed to the down projection
+    a_down: np.ndarray        # [E, L, R, I]
+    b_down: np.ndarray        # [E, L, H, R]
+    y: np.ndarray             # [T*top_k, H] uint16: the per-pair down-projection output
+
+
+def make_moe_w2(seed: int, *, T: int, H: int, E: int, top_k: int, I: int, R: int, L: int,
+                neg_frac: float = 0.05, scale: float = 1.0, name: str = "custom MoE w2") -> MoeW2Case:
+    """Routed-MoE down-projection inputs, routed like make_moe.  Routing
+    weights are uniform draws normalized per token; x2 and y ~ N(0, 1);
+    A ~ N(0, 1/I), B ~ N(0, 1/R)."""
+    rng = np.random.default_rng(seed)
+    topk = np.argsort(rng.random((T, E)), axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    lora = rng.integers(0, L, size=T)
+    if neg_frac > 0:
+        lora = np.where(rng.random(T) < neg_frac, -1, lora)
+    lora = lora.astype(np.int32)
+    w = rng.random((T, top_k), dtype=np.float32) + np.float32(0.05)
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    a_down = _normal_bf16(rng, (E, L, R, I), 1.0 / np.sqrt(I))
+    b_down = _normal_bf16(rng, (E, L, H, R), 1.0 / np.sqrt(R))
+    x2 = _normal_bf16(rng, (T * top_k, I), 1.0)
+    y = _normal_bf16(rng, (T * top_k, H), 1.0)
+    return MoeW2Case(name, T, H, E, top_k, I, R, L, float(scale), np.ascontiguousarray(topk),
+                     np.ascontiguousarray(lora), np.ascontiguousarray(w), x2, a_down, b_down, y)
+
+
+def moe_w2(seed: int = 6) -> MoeW2Case:
+    """The down projection of the MoE gemm1 model: T=2048, H=4096, 64 experts,
+    top_k 8, I=1408, rank 16, 8 adapters, 5% of tokens unadapted, scale 1."""
+    return make_moe_w2(seed, T=2048, H=4096, E=64, top_k=8, I=1408, R=16, L=8,
+                       name="MoE w2 T=2048 H=4096 E=64 top8 I=1408 R=16 L=8")
+
+
 CONFIGS = {1: tiny_bgmv, 2: decode_bgmv, 3: prefill_sgmv, 4: no_reuse, 5: moe_gemm1}

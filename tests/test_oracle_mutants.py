@@ -53,6 +53,18 @@ MUTANTS = {
     "moe unadapted counted invalid": ("if (l < 0)\n                k = -1;", "if (l < 0)\n                k = S;"),
     "moe unadapted pair not zeroed": ("for (int64_t c = 0; c < width; ++c)\n            o[c] = 0.0;",
                                       "for (int64_t c = 0; c < width; ++c)\n            o[c] = 1.0;"),
+    "w2 routing weight ignored": ("const double w = topk_weights ? (double)topk_weights[p] : 1.0;",
+                                  "const double w = 1.0;"),
+    "w2 weight of token row": ("(double)topk_weights[p] : 1.0;", "(double)topk_weights[t] : 1.0;"),
+    "w2 expert of token row": ("const int32_t e = topk_ids[p];\n        const uint16_t *yp",
+                               "const int32_t e = topk_ids[t];\n        const uint16_t *yp"),
+    "w2 adapter stride dropped": (
+        "\n        const uint16_t *A = (const uint16_t *)(intptr_t)w_ptr_a[e] + (int64_t)l * lora_stride_a;",
+        "\n        const uint16_t *A = (const uint16_t *)(intptr_t)w_ptr_a[e];"),
+    "w2 B transposed": ("d += xa[r] * bf(B[(int64_t)c * rank + r]);",
+                        "d += xa[r] * bf(B[(int64_t)r * H + c]);"),
+    "w2 y dropped": ("o[c] = bf(yp[c]);", "o[c] = 0.0;"),
+    "w2 I loop short": ("for (int32_t i = 0; i < I; ++i)", "for (int32_t i = 0; i < I - 1; ++i)"),
 }
 
 RUNNER = r"""

@@ -337,6 +337,8 @@ def test_moe_skipped_and_invalid_pairs_are_zero():
     c = _small_moe()
     c.lora_ids[0] = -1
     c.lora_ids[1] = c.L            # invalid adapter
+    c.lora_ids[2] = c.lora_ids[3] = 1
+    c.topk_ids[2, 0] = 0
     c.topk_ids[2, 1] = c.E         # invalid expert
     c.topk_ids[3, 0] = -4
     got = O.case_moe_pairs(c, False, np.arange(c.T * c.top_k))
@@ -386,3 +388,87 @@ def test_moe_single_expert_top1_is_bgmv():
     dense = O.fused_rows(c.x, c.H, a_pool, b_pool, np.ones(c.L, np.float32), c.L, (c.I, c.I),
                          c.R, c.lora_ids, np.arange(c.T), np.zeros((c.T, 2 * c.I), np.uint16))
     assert np.array_equal(dense, O.case_moe_pairs(c, False, np.arange(c.T)))
+
+
+# ============================================================== MoE w2 (down) pins
+def _small_w2(seed=41, T=10, H=48, E=4, top_k=3, I_=40, R=8, L=3, neg_frac=0.25):
+    return I.make_moe_w2(seed, T=T, H=H, E=E, top_k=top_k, I=I_, R=R, L=L, neg_frac=neg_frac,
+                         scale=0.5)
+
+
+def _w2_library(case, weighted):
+    """Per pair, the delta written with numpy matmul on the bank matrices."""
+    X2 = f32(case.x2).astype(np.float64)
+    out = f32(case.y).astype(np.float64).copy()
+    for t in range(case.T):
+        l = int(case.lora_ids[t])
+        for j in range(case.top_k):
+            e = int(case.topk_ids[t, j])
+            if l < 0 or l >= case.L or e < 0 or e >= case.E:
+                continue
+            p = t * case.top_k + j
+            A = f32(case.a_down[e, l]).astype(np.float64)
+            B = f32(case.b_down[e, l]).astype(np.float64)
+            w = float(case.topk_weights[t, j]) if weighted else 1.0
+            out[p] += w * case.scale * (B @ (A @ X2[p]))
+    return out
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_w2_library_formula(weighted):
+    c = _small_w2()
+    got = O.case_moe_w2_pairs(c, np.arange(c.T * c.top_k), weighted)
+    np.testing.assert_allclose(got, _w2_library(c, weighted), rtol=1e-12, atol=1e-12)
+
+
+def test_w2_unrouted_pairs_keep_y_exactly():
+    c = _small_w2()
+    c.lora_ids[0] = -1
+    c.lora_ids[1] = c.L            # invalid adapter
+    c.lora_ids[2] = c.lora_ids[3] = 1
+    c.topk_ids[2, 0] = 0
+    c.topk_ids[2, 1] = c.E         # invalid expert
+    c.topk_ids[3, 0] = -4
+    got = O.case_moe_w2_pairs(c, np.arange(c.T * c.top_k))
+    y = f32(c.y).astype(np.float64)
+    k = c.top_k
+    for p in list(range(0, 2 * k)) + [2 * k + 1, 3 * k]:
+        assert np.array_equal(got[p], y[p])
+    assert not np.array_equal(got[2 * k], y[2 * k])
+
+
+def test_w2_unit_weights_equal_unweighted_and_weights_scale_the_delta():
+    c = _small_w2(neg_frac=0.1)
+    pairs = np.arange(c.T * c.top_k)
+    c.topk_weights[:] = 1.0
+    assert np.array_equal(O.case_moe_w2_pairs(c, pairs, True), O.case_moe_w2_pairs(c, pairs, False))
+    c.y[:] = 0
+    one = O.case_moe_w2_pairs(c, pairs, True)
+    c.topk_weights[:] = 2.0
+    assert np.array_equal(O.case_moe_w2_pairs(c, pairs, True), 2.0 * one)   # exact in fp64
+
+
+def test_w2_equals_dense_on_expanded_rows():
+    # row p = t*top_k + j is a dense row with slot l*E + e over a pool of L*E
+    # adapters with one slice of width H: unweighted, the w2 delta is the dense delta
+    c = _small_w2(neg_frac=0.2)
+    T, k, E, L, R, H, I_ = c.T, c.top_k, c.E, c.L, c.R, c.H, c.I
+    lk = np.repeat(c.lora_ids, k)
+    key = np.where(lk >= 0, lk * E + c.topk_ids.reshape(-1), -1).astype(np.int32)
+    a_pool = np.zeros((L * E, 1, R, I_), np.uint16)
+    b_pool = np.zeros((L * E, H, R), np.uint16)
+    for l in range(L):
+        for e in range(E):
+            a_pool[l * E + e, 0], b_pool[l * E + e] = c.a_down[e, l], c.b_down[e, l]
+    dense = O.fused_rows(c.x2, I_, a_pool, b_pool, np.full(L * E, c.scale, np.float32), L * E, (H,),
+                         R, key, np.arange(T * k), c.y)
+    assert np.array_equal(dense, O.case_moe_w2_pairs(c, np.arange(T * k), False))
+
+
+def test_w2_single_expert_top1_is_bgmv():
+    c = _small_w2(E=1, top_k=1, L=4, neg_frac=0.2)
+    a_pool = c.a_down[0][:, None]          # [L, 1, R, I]
+    b_pool = c.b_down[0]                   # [L, H, R]
+    dense = O.fused_rows(c.x2, c.I, a_pool, b_pool, np.full(c.L, c.scale, np.float32), c.L, (c.H,),
+                         c.R, c.lora_ids, np.arange(c.T), c.y)
+    assert np.array_equal(dense, O.case_moe_w2_pairs(c, np.arange(c.T), False))
