@@ -11,7 +11,9 @@
  * computed as a shrink (xa = scale * x @ A^T, fp32) then an expand
  * (y += xa @ B^T).  A row with a negative slot gets no delta.  The routed-MoE
  * variant (FlashInfer docs, flashinfer.fused_moe.bgmv_moe_gemm1_lora_delta)
- * gives one gate/up delta per (token, top-k slot).
+ * gives one gate/up delta per (token, top-k slot), and the down-projection
+ * variant (vLLM punica_base.py, add_lora_w2) adds one router-weighted delta
+ * to each (token, top-k slot) output row of the expert down projection.
  *
  * Conventions for every function below:
  *  - bf16 values travel as uint16_t bit patterns; float is IEEE binary32.
@@ -185,6 +187,8 @@ size_t moe_lora_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts,
  * counts {n_active_pairs, n_segments, n_invalid_pairs, n_long_segments}.
  * The delta is unweighted and kept per pair (it is added before the gated
  * activation).  out is [T][top_k][2*inter] bf16, every element written.
+ * With T = 0 only the counts are written, and x, topk_ids, lora_ids and out
+ * may be null.
  */
 int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H,
                          const int64_t *w_ptr_a, int64_t lora_stride_a,
@@ -192,6 +196,41 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H,
                          const int32_t *topk_ids, int32_t top_k, const int32_t *lora_ids,
                          int32_t num_experts, int32_t num_loras, int32_t rank, int32_t inter,
                          float scale, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_lora_w2_delta needs (I: the down projection's input
+ * width, the intermediate size). */
+size_t moe_lora_w2_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts,
+                                   int32_t num_loras, int32_t rank, int32_t I);
+
+/*
+ * Routed-MoE down-projection (w2) LoRA delta, added in place to the per-pair
+ * output of the expert down projection before the top-k sum (vLLM
+ * punica_base.py, PunicaWrapperBase.add_lora_w2; routed as the gemm1 delta).
+ * For pair p = t*top_k + j with expert e = topk_ids[t][j] and adapter
+ * l = lora_ids[t]: w_ptr_a / w_ptr_b are [num_experts] int64 tables of device
+ * addresses (16-byte aligned); adapter l's matrices for expert e start
+ * lora_stride elements * l past the entry, A is [rank][I] and B is [H][rank]
+ * (bf16); w = topk_weights[p] (fp32 [T][top_k]), or 1 when topk_weights is
+ * null (the unweighted form), and
+ *   y[p][:] = bf16(y[p][:] + (w * scale) * B @ (A @ x2[p]))
+ * with A @ x2 and the product by B accumulated in fp32 and rounded once.
+ * x2 is [T*top_k][I] bf16 with row stride ldx, y is [T*top_k][H] bf16 with
+ * row stride ldy.  Pairs with l < 0, l >= num_loras or e outside
+ * [0, num_experts) keep their y row; the last two are counted as invalid
+ * (the counts at the start of ws as for moe_lora_gemm1_delta).  With T = 0
+ * only the counts are written, and x2, topk_ids, lora_ids and y may be
+ * null.  Errors:
+ * LORA_EINVAL for bad sizes, strides or pointers, LORA_EUNSUPPORTED for a
+ * rank outside {8, 16, ..., 128}, LORA_EWORKSPACE for a missing or small
+ * workspace; nothing is launched on error.
+ */
+int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I,
+                      const int64_t *w_ptr_a, int64_t lora_stride_a,
+                      const int64_t *w_ptr_b, int64_t lora_stride_b,
+                      const int32_t *topk_ids, int32_t top_k, const int32_t *lora_ids,
+                      const float *topk_weights, int32_t num_experts, int32_t num_loras,
+                      int32_t rank, int32_t H, float scale, uint16_t *y, int64_t ldy,
+                      void *ws, size_t ws_bytes, void *stream);
 
 /* Segments with at least this many rows take the MFMA path, shorter ones the
  * vector-ALU path (default 16; the environment variable LORA_MFMA_MIN_ROWS,

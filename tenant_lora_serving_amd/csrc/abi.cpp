@@ -111,6 +111,15 @@ int check_y(const uint16_t *y, int64_t ldy, int32_t offset_start, int n_out) {
 
 int launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ELAUNCH; }
 
+// A MoE call without pairs reads and writes no rows: its row and routing
+// pointers may be null (sizes and strides are still checked).
+// (the placeholder is a non-null, 16-byte aligned address that is never read)
+template <class T>
+const T *rows_or_placeholder(const T *p, long long n_pairs) {
+    constexpr uintptr_t kPlaceholder = 256;
+    return n_pairs > 0 ? p : reinterpret_cast<const T *>(kPlaceholder);
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,7 +217,7 @@ struct MoeLayout {
     size_t counts, sorted, segoff, segslot, tiles, meta_ws, fused, total;
     tl::FusedPlan plan;
 };
-MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int H, int shared_a, int inter) {
+MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int k_in, int n_sh) {
     MoeLayout m{};
     const int n = T * top_k, S = L * E, cap = n < S ? n : S;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -225,7 +234,7 @@ MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int H, int shared_a,
     o = up(o + (size_t)tile_bound(n, S) * LORA_TILE_WORDS * sizeof(int32_t));
     m.meta_ws = o;
     o = up(o + meta_ws_bytes(n, S));
-    m.plan = tl::fused_plan(n, S, shared_a ? 1 : 2, R, H, 2 * inter);
+    m.plan = tl::fused_plan(n, S, n_sh, R, k_in, 8);
     m.fused = o;
     o = up(o + m.plan.total_bytes);
     m.total = o;
@@ -239,7 +248,7 @@ size_t moe_lora_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts, i
         return 0;
     if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return 0;
     // the regular form needs the larger partial buffer (two shrink slices)
-    return moe_layout(T, top_k, num_experts, num_loras, rank, H, 0, 8).total;
+    return moe_layout(T, top_k, num_experts, num_loras, rank, H, 2).total;
 }
 
 int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, const int64_t *w_ptr_a,
@@ -250,14 +259,16 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
     if (T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1) return LORA_EINVAL;
     if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return LORA_EINVAL;
     if (int rc = check_rank(rank)) return rc;
-    if (int rc = check_x(x, ldx, H)) return rc;
+    const long long np = (long long)T * top_k;
+    if (int rc = check_x(rows_or_placeholder(x, np), ldx, H)) return rc;
     if (inter < 8 || inter % 8 != 0 || inter > (1 << 24)) return LORA_EINVAL;
     if (lora_stride_a < 0 || lora_stride_b < 0 || lora_stride_a % 8 != 0 || lora_stride_b % 8 != 0)
         return LORA_EINVAL;
-    if (!w_ptr_a || !w_ptr_b || !topk_ids || !lora_ids || !out || !aligned16(out)) return LORA_EINVAL;
+    if (!w_ptr_a || !w_ptr_b) return LORA_EINVAL;
+    if (np > 0 && (!topk_ids || !lora_ids || !out || !aligned16(out))) return LORA_EINVAL;
     const int n = T * top_k, S = num_experts * num_loras;
     if (int rc = check_meta_shape(n, S)) return rc;
-    const MoeLayout lay = moe_layout(T, top_k, num_experts, num_loras, rank, H, shared_a, inter);
+    const MoeLayout lay = moe_layout(T, top_k, num_experts, num_loras, rank, H, shared_a ? 1 : 2);
     if (!ws || !aligned16(ws) || ws_bytes < lay.total) return LORA_EWORKSPACE;
     char *b = static_cast<char *>(ws);
     tl::MetaOut mo{reinterpret_cast<int32_t *>(b + lay.sorted), reinterpret_cast<int32_t *>(b + lay.segoff),
@@ -271,6 +282,50 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
     tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
                    lora_ids, num_experts, num_loras, rank, inter, scale, out};
     return launched(tl::launch_moe_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused, mfma_min_rows(), st));
+}
+
+size_t moe_lora_w2_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras, int32_t rank,
+                                   int32_t I) {
+    if (T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1 || check_rank(rank) != LORA_OK || I < 8)
+        return 0;
+    if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return 0;
+    return moe_layout(T, top_k, num_experts, num_loras, rank, I, 1).total;
+}
+
+int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, const int64_t *w_ptr_a,
+                      int64_t lora_stride_a, const int64_t *w_ptr_b, int64_t lora_stride_b, const int32_t *topk_ids,
+                      int32_t top_k, const int32_t *lora_ids, const float *topk_weights, int32_t num_experts,
+                      int32_t num_loras, int32_t rank, int32_t H, float scale, uint16_t *y, int64_t ldy, void *ws,
+                      size_t ws_bytes, void *stream) {
+    if (T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1) return LORA_EINVAL;
+    if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return LORA_EINVAL;
+    if (int rc = check_rank(rank)) return rc;
+    const long long np = (long long)T * top_k;
+    if (int rc = check_x(rows_or_placeholder(x2, np), ldx, I)) return rc;
+    if (H < 8 || H % 8 != 0 || H > (1 << 24)) return LORA_EINVAL;
+    if (int rc = check_y(rows_or_placeholder(y, np), ldy, 0, H)) return rc;
+    if (lora_stride_a < 0 || lora_stride_b < 0 || lora_stride_a % 8 != 0 || lora_stride_b % 8 != 0)
+        return LORA_EINVAL;
+    if (!w_ptr_a || !w_ptr_b) return LORA_EINVAL;
+    if (np > 0 && (!topk_ids || !lora_ids)) return LORA_EINVAL;
+    if (topk_weights && (reinterpret_cast<uintptr_t>(topk_weights) & 3u)) return LORA_EINVAL;
+    const int n = T * top_k, S = num_experts * num_loras;
+    if (int rc = check_meta_shape(n, S)) return rc;
+    const MoeLayout lay = moe_layout(T, top_k, num_experts, num_loras, rank, I, 1);
+    if (!ws || !aligned16(ws) || ws_bytes < lay.total) return LORA_EWORKSPACE;
+    char *b = static_cast<char *>(ws);
+    tl::MetaOut mo{reinterpret_cast<int32_t *>(b + lay.sorted), reinterpret_cast<int32_t *>(b + lay.segoff),
+                   reinterpret_cast<int32_t *>(b + lay.segslot), reinterpret_cast<int32_t *>(b + lay.counts),
+                   reinterpret_cast<int32_t *>(b + lay.tiles), tile_bound(n, S)};
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
+                                       carve_meta_ws(b + lay.meta_ws, n), st);
+    if (e != hipSuccess) return LORA_ELAUNCH;
+    if (n == 0) return LORA_OK;
+    tl::MoeW2Shape m{x2, ldx, T, I, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, top_k, topk_weights,
+                     num_experts, num_loras, rank, H, scale, y, ldy};
+    return launched(
+        tl::launch_moe_w2_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused, mfma_min_rows(), st));
 }
 
 int32_t lora_mfma_min_rows(void) { return mfma_min_rows(); }

@@ -246,11 +246,12 @@ __device__ __forceinline__ bool wait_pieces(const int *flags, int P, uint32_t ta
 }
 
 // xa of tile rows j < 16 for the R rank rows of block xb: the P partials
-// summed in piece order, times the slot's scale (rows j >= m are zero).
+// summed in piece order, times the slot's scale and, with RW, the row's
+// weight rw[j] (rows j >= m are zero).
 // MF: bf16 hi/lo pairs xl[j][0..R) = hi, xl[j][R..2R) = lo; else fp32 xf[j][R].
-template <bool MF>
+template <bool MF, bool RW>
 __device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, int xb, int R, int m, float sc,
-                                         uint32_t tag, int *ctl, char *lds) {
+                                         const float *rw, uint32_t tag, int *ctl, char *lds) {
     const int64_t pstride = (int64_t)n_rr * 16;
     // thread -> (row j, rank r) with r fastest: one pass covers 256 / R rows,
     // and a wave's loads of one piece are contiguous words
@@ -277,6 +278,7 @@ __device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, in
                 }
             }
             s *= sc;
+            if (RW) s *= rw[j];
         }
         if (MF) {
             uint16_t *xl = reinterpret_cast<uint16_t *>(lds);
@@ -298,8 +300,23 @@ struct XaSrc {
     float sc;
     uint32_t tag;
     int *ctl;
-    int *ok;  // LDS
+    int *ok;    // LDS
+    float *rw;  // LDS: the tile rows' weights (ops with row weights)
 };
+
+// Row weights of the tile into xs.rw (wave 0, lanes 0..15); called after the
+// unit's B and y loads are issued and before wait_pieces, whose barriers
+// publish them to the other waves.
+template <class Op>
+__device__ __forceinline__ void load_row_weights(const Op &op, const Hdr &h, const XaSrc &xs) {
+    if constexpr (Op::kRowWeights) {
+        if (wave_id() == 0) {
+            const int lane = lane_id();
+            const int rid = __shfl(h.rec, kRecRowIds + (lane & 15), kWave);
+            if (lane < kTileRows) xs.rw[lane] = lane < h.m ? op.row_weight(rid) : 0.f;
+        }
+    }
+}
 
 // Rows jb .. jb+3 of a vector-ALU expand (jb a compile-time multiple of 4;
 // rows past m are computed from row m - 1's xa and not stored): both of the
@@ -454,8 +471,9 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
     // the first batch's B reaches its lanes while the producers still run
     uint16_t *bst = reinterpret_cast<uint16_t *>(lds + kXaBytes) + w * kBStage;
     if (tr) valu_transpose(raw, R, bst, bq);
+    load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
-    stage_xa<false>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.tag, xs.ctl, lds);
+    stage_xa<false, Op::kRowWeights>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.rw, xs.tag, xs.ctl, lds);
     __syncthreads();
     const float *xf = reinterpret_cast<const float *>(lds);
     for (int b = 0; b < nb; ++b) {
@@ -535,8 +553,9 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
     uint2 yv[8];
     mfma_load_b<NRS>(op, h, c0 + 128 * w, c1, R, bo);
     mfma_load_y(yp, c0 + 128 * w, c1, add_inputs, yv);
+    load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
-    stage_xa<true>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.tag, xs.ctl, lds);
+    stage_xa<true, Op::kRowWeights>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.rw, xs.tag, xs.ctl, lds);
     __syncthreads();
     const uint16_t *xl = reinterpret_cast<const uint16_t *>(lds) + col * 2 * R;
     u32x4_t hv[NRS], lv[NRS];
@@ -665,6 +684,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
     constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = WIDE ? kXaBytes + 4 * kBStage * 2 : kXaBytes;
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     __shared__ int ok;
+    __shared__ float rw[Op::kRowWeights ? kTileRows : 1];
     const int P = fa.P, C = fa.C;
     const int n_rr = op.n_rr();
     const Unit un = unit_of(blockIdx.x, fa.tile_bound, P, C, fa.GT);
@@ -696,7 +716,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         int l, c0, c1;
         chunk_of(op, cc, fa.EC, l, c0, c1);
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
-                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok};
+                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw};
         if (h.mseg >= fa.mfma_min)
             expand_mfma<NRS, WIDE>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         else

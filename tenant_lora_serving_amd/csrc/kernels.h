@@ -93,4 +93,23 @@ struct MoeShape {
 hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
                             void *ws, int mfma_min, hipStream_t st);
 
+// Routed-MoE down projection: x2 [n_pairs][I] (ldx), y [n_pairs][H] (ldy) added to.
+struct MoeW2Shape {
+    const uint16_t *x2;
+    int64_t ldx;
+    int T, I;
+    const int64_t *w_ptr_a;
+    int64_t lora_stride_a;
+    const int64_t *w_ptr_b;
+    int64_t lora_stride_b;
+    int top_k;
+    const float *topk_weights;  // or null
+    int E, L, R, H;
+    float scale;
+    uint16_t *y;
+    int64_t ldy;
+};
+hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const int32_t *tiles, const int32_t *counts,
+                               const FusedPlan &plan, void *ws, int mfma_min, hipStream_t st);
+
 }  // namespace tl

@@ -5,7 +5,8 @@
 // Rank rows: the shrink computes n_rr = n_sh * R values per row, rank row
 // rr = l * R + r belonging to shrink slice l.  Output slices: the expand
 // writes n_xs column windows [xoff(l), xoff(l + 1)), each fed by the R rank
-// rows of xa block xblk(l).
+// rows of xa block xblk(l).  kRowWeights: xa of row i is also multiplied by
+// row_weight(i) (a per-row router weight).
 #pragma once
 
 #include "common.h"
@@ -25,6 +26,7 @@ struct DenseOp {
     int64_t ldy;
     int k_in, R, n_sh, n_out, col0, n_sl;
     int off[kMaxSlices + 1];
+    static constexpr bool kRowWeights = false;
 
     __device__ int n_rr() const { return n_sh * R; }
     __device__ int n_xs() const { return n_sl; }
@@ -49,6 +51,7 @@ struct DenseOp {
     }
     __device__ uint16_t *yrow(int row) const { return y + (int64_t)row * ldy + col0; }
     __device__ float scale_of(int slot) const { return scale[slot]; }
+    __device__ float row_weight(int) const { return 1.f; }
 };
 
 // Routed MoE gemm1 (FlashInfer bgmv_moe_gemm1_lora_delta): key = l*E + e,
@@ -64,6 +67,7 @@ struct MoeOp {
     uint16_t *out;
     float sc;
     int k_in, R, n_sh, n_out, E, inter, shared;
+    static constexpr bool kRowWeights = false;
 
     __device__ int n_rr() const { return n_sh * R; }
     __device__ int n_xs() const { return 2; }
@@ -87,6 +91,45 @@ struct MoeOp {
     }
     __device__ uint16_t *yrow(int pair) const { return out + (int64_t)pair * n_out; }
     __device__ float scale_of(int) const { return sc; }
+    __device__ float row_weight(int) const { return 1.f; }
+};
+
+// Routed MoE down projection (vLLM punica_base.py, add_lora_w2): rows are
+// (token, slot) pairs p, each with its own input row x2[p] (the activated
+// gemm1 output) and output row y[p] (added to in place); key = l*E + e; one
+// shrink slice and one output window [0, H); xa of pair p is scaled by the
+// pair's router weight when weights are given.
+struct MoeW2Op {
+    const uint16_t *x;
+    int64_t ldx;
+    const int64_t *wa;
+    int64_t lsa;
+    const int64_t *wb;
+    int64_t lsb;
+    const float *wt;  // [n_pairs] router weights, or null
+    uint16_t *y;
+    int64_t ldy;
+    float sc;
+    int k_in, R, n_sh, n_out, E;
+    static constexpr bool kRowWeights = true;
+
+    __device__ int n_rr() const { return R; }
+    __device__ int n_xs() const { return 1; }
+    __device__ const uint16_t *xrow(int pair) const { return x + (int64_t)pair * ldx; }
+    __device__ const uint16_t *arow(int key, int rr) const {
+        const int l = key / E, e = key - l * E;
+        return reinterpret_cast<const uint16_t *>(wa[e]) + (int64_t)l * lsa + (int64_t)rr * k_in;
+    }
+    __device__ int xslice(int) const { return 0; }
+    __device__ int xoff(int l) const { return l * n_out; }
+    __device__ int xblk(int) const { return 0; }
+    __device__ const uint16_t *brow(int key, int c) const {
+        const int l = key / E, e = key - l * E;
+        return reinterpret_cast<const uint16_t *>(wb[e]) + (int64_t)l * lsb + (int64_t)c * R;
+    }
+    __device__ uint16_t *yrow(int pair) const { return y + (int64_t)pair * ldy; }
+    __device__ float scale_of(int) const { return sc; }
+    __device__ float row_weight(int pair) const { return wt ? wt[pair] : 1.f; }
 };
 
 }  // namespace tl

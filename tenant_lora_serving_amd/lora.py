@@ -70,6 +70,12 @@ def lib():
         L.moe_lora_gemm1_delta.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64,
                                            _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
                                            _c_f, _c_p, _c_p, _c_sz, _c_p]
+        L.moe_lora_w2_workspace_bytes.restype = _c_sz
+        L.moe_lora_w2_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]
+        L.moe_lora_w2_delta.restype = ctypes.c_int
+        L.moe_lora_w2_delta.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64,
+                                        _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _c_f, _c_p, _c_i64, _c_p, _c_sz, _c_p]
         L.lora_mfma_min_rows.restype = _c_i32
         L.lora_mfma_min_rows.argtypes = []
         L.lora_set_mfma_min_rows.restype = None
@@ -82,7 +88,8 @@ def lib():
 
 EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build", "lora_shrink",
             "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused",
-            "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "lora_mfma_min_rows",
+            "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "moe_lora_w2_workspace_bytes",
+            "moe_lora_w2_delta", "lora_mfma_min_rows",
             "lora_set_mfma_min_rows", "lora_status_string"]
 
 
@@ -279,6 +286,54 @@ def moe_lora_gemm1_delta(hidden_states: torch.Tensor, w_ptr_a: torch.Tensor, lor
         _dev(out, "out", torch.bfloat16), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     _check("moe_lora_gemm1_delta", st)
     return out
+
+
+def moe_w2_workspace(T: int, top_k: int, num_experts: int, num_loras: int, rank: int, I: int,
+                     device="cuda") -> torch.Tensor:
+    b = int(lib().moe_lora_w2_workspace_bytes(T, top_k, num_experts, num_loras, rank, I))
+    return torch.zeros(max(b, 16), dtype=torch.uint8, device=device)
+
+
+def _pair_rows(t: torch.Tensor, name: str, n_pairs: int):
+    """[T*top_k, W] or [T, top_k, W] bf16 rows with unit column stride."""
+    if t.dim() == 3:
+        t = t.view(-1, t.shape[2])
+    if t.dim() != 2 or t.shape[0] != n_pairs:
+        raise ValueError(f"{name} must hold one row per (token, slot) pair")
+    return t
+
+
+def moe_lora_w2_delta(x2: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: int,
+                      w_ptr_b: torch.Tensor, lora_stride_b: int, topk_ids: torch.Tensor,
+                      lora_ids: torch.Tensor, rank: int, y: torch.Tensor, *, num_loras: int,
+                      topk_weights: torch.Tensor | None = None, scale: float = 1.0,
+                      ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Add the routed down-projection delta to y ([T*top_k, H] or [T, top_k, H])
+    in place; x2 holds the pairs' activated gemm1 outputs, [T*top_k, I]."""
+    if w_ptr_a.dim() != 1 or w_ptr_b.dim() != 1:
+        raise ValueError("w2 pointer tables are [num_experts]")
+    E = w_ptr_a.shape[0]
+    T, top_k = topk_ids.shape
+    x2v = _pair_rows(x2, "x2", T * top_k)
+    yv = _pair_rows(y, "y", T * top_k)
+    I, H = x2v.shape[1], yv.shape[1]
+    xp, ldx = _rows_ld(x2v, "x2")
+    yp, ldy = _rows_ld(yv, "y")
+    wp = None
+    if topk_weights is not None:
+        if topk_weights.shape != (T, top_k):
+            raise ValueError("topk_weights must be [T, top_k]")
+        wp = _dev(topk_weights, "topk_weights", torch.float32)
+    if ws is None:
+        ws = moe_w2_workspace(T, top_k, E, num_loras, rank, I, x2.device)
+    st = lib().moe_lora_w2_delta(
+        xp, ldx, T, I, _dev(w_ptr_a, "w_ptr_a", torch.int64), int(lora_stride_a),
+        _dev(w_ptr_b, "w_ptr_b", torch.int64), int(lora_stride_b),
+        _dev(topk_ids, "topk_ids", torch.int32), top_k, _dev(lora_ids, "lora_ids", torch.int32), wp,
+        E, int(num_loras), int(rank), H, float(scale), yp, ldy, _dev(ws, "ws", torch.uint8),
+        ws.numel(), _stream(stream))
+    _check("moe_lora_w2_delta", st)
+    return y
 
 
 def moe_counts(ws: torch.Tensor) -> torch.Tensor:

@@ -29,10 +29,10 @@ def L():
     return B.lib()
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ["lora_meta_build", "lora_shrink", "lora_expand", "lora_delta_fused",
-              "moe_lora_gemm1_delta"]:
+              "moe_lora_gemm1_delta", "moe_lora_w2_delta"]:
         assert f in fns
 
 
@@ -54,6 +54,10 @@ def test_tile_bound_and_workspace_sizes(L):
     assert L.lora_fused_workspace_bytes(256, 32, 3, 16, 4096) > 0
     assert L.lora_fused_workspace_bytes(256, 32, 3, 12, 4096) == 0  # rank not a multiple of 8
     assert L.moe_lora_workspace_bytes(2048, 8, 64, 8, 16, 4096) > 0
+    # one shrink slice over I = 1408: smaller than gemm1's two over H = 4096
+    w2 = L.moe_lora_w2_workspace_bytes(2048, 8, 64, 8, 16, 1408)
+    assert 0 < w2 < L.moe_lora_workspace_bytes(2048, 8, 64, 8, 16, 4096)
+    assert L.moe_lora_w2_workspace_bytes(2048, 8, 64, 8, 12, 1408) == 0
 
 
 def _meta(ptr=0x10000):
@@ -127,6 +131,33 @@ def test_moe_validation(L):
     assert call(wa=None) == EINVAL
     assert call(wsb=need - 1) == EWS
     assert call(top_k=0) == EINVAL
+
+
+def test_moe_w2_validation(L):
+    base = dict(x=0x1000, ldx=1408, T=16, I=1408, wa=0x2000, lsa=16 * 1408, wb=0x3000, lsb=4096 * 16,
+                topk=0x4000, top_k=8, lora=0x5000, wt=0x8000, E=64, L=8, R=16, H=4096, y=0x6000,
+                ldy=4096)
+    need = L.moe_lora_w2_workspace_bytes(16, 8, 64, 8, 16, 1408)
+
+    def call(ws=0x7000, wsb=need, **kw):
+        v = dict(base, **kw)
+        return L.moe_lora_w2_delta(v["x"], v["ldx"], v["T"], v["I"], v["wa"], v["lsa"], v["wb"], v["lsb"],
+                                   v["topk"], v["top_k"], v["lora"], v["wt"], v["E"], v["L"], v["R"],
+                                   v["H"], 1.0, v["y"], v["ldy"], ws, wsb, None)
+    assert call(I=1404) == EINVAL
+    assert call(ldx=1400) == EINVAL
+    assert call(R=20) == EUNSUP
+    assert call(H=4100) == EINVAL
+    assert call(ldy=4000) == EINVAL
+    assert call(y=0x6008) == EINVAL          # y not 16-byte aligned
+    assert call(wt=0x8002) == EINVAL         # weights not float aligned
+    assert call(lsb=7) == EINVAL
+    assert call(wb=None) == EINVAL
+    assert call(topk=None) == EINVAL
+    assert call(wsb=need - 1) == EWS
+    assert call(ws=None) == EWS
+    assert call(top_k=0) == EINVAL
+    assert call(E=0) == EINVAL
 
 
 def test_status_strings(L):

@@ -121,3 +121,9 @@ def test_moe_deterministic(moe_case):
     a, _ = run_moe(moe_case, False, ws)
     b, _ = run_moe(moe_case, False, ws)
     assert np.array_equal(a, b)
+
+
+def test_moe_no_pairs():
+    c = small_moe(9, T=0)
+    out, counts = run_moe(c, False)
+    assert out.size == 0 and counts.tolist() == [0, 0, 0, 0]

@@ -1,0 +1,151 @@
+"""GPU parity of moe_lora_w2_delta (the routed down-projection delta, added to
+y in place) against the fp64 oracle: weighted and unweighted, rows of
+unadapted and invalid pairs left bitwise unchanged, the pair counts, both
+arithmetic paths, ragged k and column tails, and the reduction to the dense
+fused delta for one expert with top-1 (bitwise: the same partial order and
+scale)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tenant_lora_serving_amd import inputs as I
+from tenant_lora_serving_amd import lora as B
+from gpu_util import assert_close, bf64, d16, d32, h16
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"default": 16, "valu": 1 << 30, "mfma": 1}
+
+
+@pytest.fixture(params=list(PATHS))
+def path(request):
+    old = B.mfma_min_rows()
+    B.set_mfma_min_rows(PATHS[request.param])
+    yield request.param
+    B.set_mfma_min_rows(old)
+
+
+def device_tables(c: I.MoeW2Case):
+    """Device banks and [E] pointer tables: adapter l of expert e starts
+    l * stride elements past entry e."""
+    E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
+    A, Bm = d16(c.a_down), d16(c.b_down)
+    ta = torch.tensor([A.data_ptr() + e * L * R * I_ * 2 for e in range(E)], dtype=torch.int64)
+    tb = torch.tensor([Bm.data_ptr() + e * L * H * R * 2 for e in range(E)], dtype=torch.int64)
+    return (A, Bm), ta.cuda(), R * I_, tb.cuda(), H * R
+
+
+def run_w2(c: I.MoeW2Case, weighted: bool, ws=None):
+    keep, ta, sa, tb, sb = device_tables(c)
+    y = d16(c.y)
+    wt = d32(c.topk_weights) if weighted else None
+    if ws is None:
+        ws = B.moe_w2_workspace(c.T, c.top_k, c.E, c.L, c.R, c.I)
+    B.moe_lora_w2_delta(d16(c.x2), ta, sa, tb, sb, d32(c.topk_ids), d32(c.lora_ids), c.R, y,
+                        num_loras=c.L, topk_weights=wt, scale=c.scale, ws=ws)
+    torch.cuda.synchronize()
+    del keep
+    return h16(y), B.moe_counts(ws).cpu().numpy()
+
+
+def check_w2(c: I.MoeW2Case, weighted: bool, sample=None, what=""):
+    print(f"moe w2 case T={c.T} E={c.E} L={c.L} I={c.I} H={c.H} R={c.R} weighted={weighted} {what}",
+          flush=True)
+    out, counts = run_w2(c, weighted)
+    lora = np.repeat(c.lora_ids, c.top_k)
+    ex = c.topk_ids.reshape(-1)
+    valid = (lora >= 0) & (lora < c.L) & (ex >= 0) & (ex < c.E)
+    assert np.array_equal(out[~valid], c.y[~valid]), "unrouted pairs must keep y bit for bit"
+    keys = O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L)
+    _, _, _, ocnt = O.meta_build(keys, c.E * c.L)
+    assert counts.tolist() == ocnt.tolist()
+    pairs = np.flatnonzero(valid)
+    if sample is not None:
+        pairs = pairs[:: max(1, len(pairs) // sample)]
+    orc = O.case_moe_w2_pairs(c, pairs, weighted)
+    return assert_close(bf64(out[pairs]), orc, f"moe w2 weighted={weighted} {what}")
+
+
+def small_w2(seed, **kw):
+    args = dict(T=50, H=264, E=5, top_k=3, I=40, R=16, L=3, neg_frac=0.2, scale=0.75)
+    args.update(kw)
+    c = I.make_moe_w2(seed, **args)
+    rng = np.random.default_rng(seed + 100)
+    c.lora_ids[rng.random(c.T) < 0.05] = c.L + 1               # invalid adapter ids
+    c.topk_ids[rng.random(c.topk_ids.shape) < 0.03] = c.E + 2  # invalid expert ids
+    return c
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_w2_small(seed, weighted, path):
+    # seed 2: three experts, so (adapter, expert) segments run past 16 rows
+    c = small_w2(seed, T=60 if seed == 1 else 400, E=5 if seed == 1 else 3)
+    check_w2(c, weighted, what=f"seed={seed} {path}")
+
+
+@pytest.mark.parametrize("R", [8, 32, 64])
+def test_w2_ragged_k_and_columns(R, path):
+    # I = 1032: three k pieces, the last 8 wide; H = 1096: column tail of 72
+    c = small_w2(3, T=90, E=2, top_k=2, I=1032, H=1096, R=R, L=2)
+    check_w2(c, True, what=f"R={R} {path}")
+
+
+def test_w2_wide_columns(path):
+    # 8000 pairs over 16 keys: about 516 tiles, so the expand units widen to
+    # 1024 columns (two 512-column batches, the last unit ragged)
+    c = small_w2(4, T=4000, E=4, top_k=2, I=264, H=2056, R=16, L=4, neg_frac=0.05)
+    check_w2(c, True, sample=300, what=f"wide {path}")
+
+
+def test_w2_no_pairs():
+    c = small_w2(5, T=0)
+    out, counts = run_w2(c, True)
+    assert out.size == 0 and counts.tolist() == [0, 0, 0, 0]
+
+
+def test_w2_single_expert_top1_equals_dense_fused():
+    c = small_w2(6, T=130, E=1, top_k=1, L=4, I=520, H=520, R=16, neg_frac=0.2)
+    c.lora_ids[c.lora_ids >= c.L] = -1
+    c.topk_ids[:] = 0
+    out, _ = run_w2(c, False)
+    a_pool = d16(np.ascontiguousarray(c.a_down[0][:, None]))   # [L, 1, R, I]
+    b_pool = d16(np.ascontiguousarray(c.b_down[0]))            # [L, H, R]
+    y = d16(c.y)
+    meta = B.lora_meta_build(d32(c.lora_ids), c.L)
+    B.lora_delta_fused(d16(c.x2), a_pool, b_pool, torch.full((c.L,), c.scale, device="cuda"), (c.H,),
+                       meta, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(out, h16(y))
+
+
+def test_w2_unit_weights_equal_unweighted():
+    c = small_w2(7, T=200, E=3)
+    c.topk_weights[:] = 1.0
+    a, _ = run_w2(c, True)
+    b, _ = run_w2(c, False)
+    assert np.array_equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def w2_case():
+    return I.moe_w2()
+
+
+def test_w2_config_full(w2_case):
+    check_w2(w2_case, True, sample=400, what="config")
+
+
+def test_w2_deterministic_and_ws_reuse(w2_case):
+    c = w2_case
+    ws = B.moe_w2_workspace(c.T, c.top_k, c.E, c.L, c.R, c.I)
+    a, _ = run_w2(c, True, ws)
+    small = small_w2(8, T=70, E=c.E, top_k=c.top_k, L=c.L, I=c.I, R=c.R, H=520)
+    check_small = run_w2(small, True, ws)[0]
+    b, _ = run_w2(c, True, ws)
+    assert np.array_equal(a, b)
+    lora = np.repeat(small.lora_ids, small.top_k)
+    ex = small.topk_ids.reshape(-1)
+    valid = np.flatnonzero((lora >= 0) & (lora < small.L) & (ex >= 0) & (ex < small.E))
+    assert_close(bf64(check_small[valid]), O.case_moe_w2_pairs(small, valid, True), "small on shared ws")
