@@ -226,7 +226,7 @@ def main():
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "fused_kernel<3, 1, DenseOp>", "kernel_us": round(fused_ms * 1e3, 3)},
+                     "kernel": "fused_kernel<3, 1, 0, DenseOp>", "kernel_us": round(fused_ms * 1e3, 3)},
         "meta_kernel_us": round(meta_ms * 1e3, 3),
     }
     if not args.no_cpu:

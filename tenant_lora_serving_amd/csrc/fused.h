@@ -450,15 +450,20 @@ __device__ __forceinline__ void valu_load_y(const Op &op, const Hdr &h, int c, i
                     : 0u;
 }
 
-// WIDE: the call's expand units may span several batches (large calls);
-// otherwise a unit is one batch, and none of the next-batch registers exist.
-template <bool WIDE, class Op>
+// Expand modes (WM): 0, a unit is one batch, and none of the next-batch
+// registers exist; 1, units may span several batches, and the vector-ALU
+// path loads batch b + 1 while it computes batch b (B coalesced through LDS
+// when R <= 32); 2, as 1 but the vector-ALU path loads each batch when it
+// starts, which frees the registers (and LDS) of the prefetch for calls
+// whose tiles are mostly on the MFMA path.
+template <int WM, class Op>
 __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                             const XaSrc &xs, char *lds) {
+    constexpr bool WIDE = WM != 0, PREFETCH = WM == 1;
     const int lane = lane_id(), w = wave_id();
     const int R = op.R, m = h.m;
     const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
-    const bool tr = WIDE && xs.coalesce_b && R <= 32;
+    const bool tr = PREFETCH && xs.coalesce_b && R <= 32;
     const uint16_t *bp = nullptr;
     u32x4_t raw[8], bq[2][4];  // B: coalesced chunks, then ranks 0..31 of the lane's two columns
     uint32_t yv[kTileRows];
@@ -480,10 +485,14 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
         const int c = c0 + kEB * b + cl;
         const bool cok = c < c1;
         if (tr && b > 0) valu_transpose(raw, R, bst, bq);
+        if (WIDE && !PREFETCH && b > 0) {
+            valu_load_b(op, h, c, c1, R, bp, bq);
+            valu_load_y(op, h, c, c1, add_inputs, yv);
+        }
         const uint16_t *bp_n = nullptr;
         u32x4_t bq_n[2][4];
         uint32_t yv_n[kTileRows];
-        if (WIDE && b + 1 < nb) {
+        if (PREFETCH && b + 1 < nb) {
             if (tr)
                 valu_load_raw(op, h, c0 + kEB * (b + 1) + 128 * w, c1, R, raw);
             else
@@ -495,7 +504,7 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
         if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-        if (WIDE && b + 1 < nb) {
+        if (PREFETCH && b + 1 < nb) {
             if (!tr) {
                 bp = bp_n;
 #pragma unroll
@@ -634,35 +643,34 @@ __device__ __forceinline__ void chunk_of(const Op &op, int cc, int EC, int &l, i
 }
 
 // ============================================================ unit order
-// Tiles are taken in groups of GT.  Workgroups run the units in the order
-//   S_0, S_1, E_0, S_2, E_1, ..., S_{G-1}, E_{G-2}, E_{G-1}, then MoE zero rows
-// (S_g: the shrink units of group g, P per tile; E_g: its expand units, C per
-// tile), so a group's consumers start while the next group's producers run
-// and the two phases of a large call overlap.  E_g only waits on S_g, which
-// precedes it.
+// Workgroup ids: the shrink units (tile t, piece p) at t*P + p, padded to a
+// multiple of 8; then the expand units; then the MoE zero-row units.  Every
+// consumer therefore has a higher id than the producers it waits on.
+// Workgroups go to the 8 XCDs round robin (id mod 8), and each XCD has its
+// own L2: with P = 8, XCD p runs piece p of every tile, so each A piece is
+// fetched by one XCD.  Expand units come in blocks of 8 tiles x C chunks; in
+// a full block, XCD x runs the C units k = x*C .. x*C + C - 1 of the
+// chunk-major order (chunk k / 8 of tile k mod 8), so a chunk's B rows, which
+// the 8 tiles of a long segment share, reach at most two L2s instead of all
+// eight.
 constexpr int kUnitShrink = 0, kUnitExpand = 1, kUnitZero = 2;
+constexpr int kXcds = 8;
 struct Unit {
     int kind, t, sub;
 };
-__device__ __forceinline__ Unit unit_of(int bid, int tile_bound, int P, int C, int GT) {
-    const int G = (tile_bound + GT - 1) / GT;
-    const int nS = GT * P, nE = GT * C;
-    const int n_main = G * (nS + nE);
-    if (bid >= n_main) return Unit{kUnitZero, 0, bid - n_main};
-    int g, local, kind;
-    if (bid < nS) {
-        kind = kUnitShrink, g = 0, local = bid;
-    } else {
-        const int r = bid - nS, q = r / (nS + nE), off = r - q * (nS + nE);
-        if (q < G - 1 && off < nS)
-            kind = kUnitShrink, g = q + 1, local = off;
-        else if (q < G - 1)
-            kind = kUnitExpand, g = q, local = off - nS;
-        else
-            kind = kUnitExpand, g = G - 1, local = off;
-    }
-    const int per = kind == kUnitShrink ? P : C;
-    return Unit{kind, g * GT + local / per, local % per};
+__device__ __forceinline__ int shrink_span(int tile_bound, int P) {
+    return (tile_bound * P + kXcds - 1) / kXcds * kXcds;
+}
+__device__ __forceinline__ Unit unit_of(int bid, int tile_bound, int P, int C) {
+    const int nS = shrink_span(tile_bound, P), nE = tile_bound * C;
+    if (bid < nS) return Unit{kUnitShrink, bid / P, bid - (bid / P) * P};
+    if (bid >= nS + nE) return Unit{kUnitZero, 0, bid - nS - nE};
+    const int e = bid - nS, blk = kXcds * C;
+    const int g = e / blk, q = e - g * blk;
+    if ((g + 1) * kXcds > tile_bound)  // last, partial block: tile-major
+        return Unit{kUnitExpand, g * kXcds + q / C, q % C};
+    const int k = (q & (kXcds - 1)) * C + q / kXcds;
+    return Unit{kUnitExpand, g * kXcds + (k & (kXcds - 1)), k / kXcds};
 }
 
 // ============================================================ kernel
@@ -670,7 +678,6 @@ struct FusedArgs {
     const int32_t *tiles;
     const int32_t *counts;  // counts[4] = tiles in use
     int tile_bound, P, FP, C;
-    int GT;          // tiles per group of the unit order
     int EC;          // output columns per expand unit (a multiple of kEB)
     uint64_t *part;  // [tile_bound][P][n_rr][16] tagged partials
     int *ctl;        // control line
@@ -678,16 +685,16 @@ struct FusedArgs {
     int mfma_min, add_inputs;
 };
 
-template <int RPL, int NRS, bool WIDE, class Op>
+template <int RPL, int NRS, int WM, class Op>
 __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
-    constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = WIDE ? kXaBytes + 4 * kBStage * 2 : kXaBytes;
+    constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = WM == 1 ? kXaBytes + 4 * kBStage * 2 : kXaBytes;
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     __shared__ int ok;
     __shared__ float rw[Op::kRowWeights ? kTileRows : 1];
     const int P = fa.P, C = fa.C;
     const int n_rr = op.n_rr();
-    const Unit un = unit_of(blockIdx.x, fa.tile_bound, P, C, fa.GT);
+    const Unit un = unit_of(blockIdx.x, fa.tile_bound, P, C);
     if (un.kind == kUnitShrink || un.kind == kUnitExpand) {
         const int t = un.t;
         if (t >= fa.tile_bound) return;
@@ -718,9 +725,9 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
                        fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw};
         if (h.mseg >= fa.mfma_min)
-            expand_mfma<NRS, WIDE>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+            expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         else
-            expand_valu<WIDE>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+            expand_valu<WM>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         // the last consumer of a tile counts the tile as finished; the last
         // finished tile of the call advances the generation (two levels, so
         // no single address takes one atomic per consumer)
@@ -760,27 +767,34 @@ static int rpl_of(int n_rr) { return n_rr >= 64 ? 4 : (n_rr + 15) / 16; }
 static int nrs_of(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }
 
 template <int RPL, int NRS, class Op>
-static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, long long grid, ZeroFill zf, hipStream_t st) {
-    if (fa.EC > kEB)
-        hipLaunchKernelGGL((fused_kernel<RPL, NRS, true, Op>), dim3((unsigned)grid), dim3(kFT), 0, st, op, fa, zf);
+static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, bool mfma_lean, long long grid, ZeroFill zf,
+                                 hipStream_t st) {
+    const dim3 g((unsigned)grid), b(kFT);
+    if (fa.EC <= kEB)
+        hipLaunchKernelGGL((fused_kernel<RPL, NRS, 0, Op>), g, b, 0, st, op, fa, zf);
+    else if (!mfma_lean)
+        hipLaunchKernelGGL((fused_kernel<RPL, NRS, 1, Op>), g, b, 0, st, op, fa, zf);
     else
-        hipLaunchKernelGGL((fused_kernel<RPL, NRS, false, Op>), dim3((unsigned)grid), dim3(kFT), 0, st, op, fa, zf);
+        hipLaunchKernelGGL((fused_kernel<RPL, NRS, 2, Op>), g, b, 0, st, op, fa, zf);
     return hipGetLastError();
 }
 
 template <int RPL, class Op>
-static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, long long grid, ZeroFill zf, hipStream_t st) {
+static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, bool mfma_lean, long long grid, ZeroFill zf,
+                                 hipStream_t st) {
     switch (nrs_of(op.R)) {
-    case 1: return launch_fused_t<RPL, 1>(op, fa, grid, zf, st);
-    case 2: return launch_fused_t<RPL, 2>(op, fa, grid, zf, st);
-    default: return launch_fused_t<RPL, 4>(op, fa, grid, zf, st);
+    case 1: return launch_fused_t<RPL, 1>(op, fa, mfma_lean, grid, zf, st);
+    case 2: return launch_fused_t<RPL, 2>(op, fa, mfma_lean, grid, zf, st);
+    default: return launch_fused_t<RPL, 4>(op, fa, mfma_lean, grid, zf, st);
     }
 }
 
+// mfma_lean: the call averages at least mfma_min rows per slot, so most of
+// its tiles are expected on the MFMA path (selects expand mode 2 over 1).
 template <class Op>
 static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                                  int C, int EC, void *ws, int mfma_min, int add_inputs, ZeroFill zf, int zero_units,
-                                  hipStream_t st) {
+                                  int C, int EC, void *ws, int mfma_min, bool mfma_lean, int add_inputs,
+                                  ZeroFill zf, int zero_units, hipStream_t st) {
     char *w = static_cast<char *>(ws);
     FusedArgs fa{};
     fa.tiles = tiles;
@@ -795,18 +809,18 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     fa.part = reinterpret_cast<uint64_t *>(w + plan.flag_bytes);
     fa.mfma_min = mfma_min;
     fa.add_inputs = add_inputs;
-    // one group: every shrink unit ahead of every expand unit.  (Pipelining
-    // groups of about two workgroups per CU measured slower on the large
-    // configs: consumers that start before their producers hold slots.)
-    fa.GT = std::max(1, plan.tile_bound);
-    const int G = plan.tile_bound > 0 ? (plan.tile_bound + fa.GT - 1) / fa.GT : 0;
-    const long long grid = (long long)G * fa.GT * (plan.P + C) + zero_units;
+    // every shrink unit ahead of every expand unit.  (Interleaving groups of
+    // producers and consumers measured slower on the large configs: consumers
+    // that start before their producers hold workgroup slots.)
+    const long long n_shrink = ((long long)plan.tile_bound * plan.P + kXcds - 1) / kXcds * kXcds;
+    const long long grid = plan.tile_bound > 0 ? n_shrink + (long long)plan.tile_bound * C + zero_units
+                                               : zero_units;
     if (grid == 0) return hipSuccess;
     switch (rpl_of(op.n_sh * op.R)) {
-    case 1: return launch_fused_r<1>(op, fa, grid, zf, st);
-    case 2: return launch_fused_r<2>(op, fa, grid, zf, st);
-    case 3: return launch_fused_r<3>(op, fa, grid, zf, st);
-    default: return launch_fused_r<4>(op, fa, grid, zf, st);
+    case 1: return launch_fused_r<1>(op, fa, mfma_lean, grid, zf, st);
+    case 2: return launch_fused_r<2>(op, fa, mfma_lean, grid, zf, st);
+    case 3: return launch_fused_r<3>(op, fa, mfma_lean, grid, zf, st);
+    default: return launch_fused_r<4>(op, fa, mfma_lean, grid, zf, st);
     }
 }
 

@@ -37,8 +37,9 @@ hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t
     for (int l = 0; l <= kMaxSlices; ++l) op.off[l] = d.slice_off[l < d.num_slices ? l : d.num_slices];
     const int EC = expand_width(d.slice_off, d.num_slices, plan.tile_bound);
     const int C = chunks_of(d.slice_off, d.num_slices, EC);
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 1, ZeroFill{nullptr, nullptr, 1, 1, 1, 0},
-                           0, st);
+    const bool lean = (long long)d.n >= (long long)mfma_min * d.num_slots;
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, lean, 1,
+                           ZeroFill{nullptr, nullptr, 1, 1, 1, 0}, 0, st);
 }
 
 }  // namespace tl

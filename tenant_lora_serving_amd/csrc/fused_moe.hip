@@ -29,7 +29,8 @@ hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32
     const int off[3] = {0, m.inter, 2 * m.inter};
     const int EC = expand_width(off, 2, plan.tile_bound);
     const int C = chunks_of(off, 2, EC);
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 0, zf, zero_units, st);
+    const bool lean = (long long)n_pairs >= (long long)mfma_min * m.E * m.L;
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, lean, 0, zf, zero_units, st);
 }
 
 }  // namespace tl

@@ -27,7 +27,8 @@ hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const int32_t *tiles, const 
     const int off[2] = {0, m.H};
     const int EC = expand_width(off, 1, plan.tile_bound);
     const int C = chunks_of(off, 1, EC);
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, 1, zf, 0, st);
+    const bool lean = (long long)m.T * m.top_k >= (long long)mfma_min * m.E * m.L;
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, lean, 1, zf, 0, st);
 }
 
 }  // namespace tl
