@@ -22,6 +22,11 @@
  *  - vLLM "punica_base.py", PunicaWrapperBase.add_lora_w2: the w2 LoRA
  *    applied in place to the per-(token, slot) down-projection output
  *    (intermediate_cache3) before moe_sum, routed as add_lora_w13.
+ *  - metrale source "lora/expert_apply.rs": expert_delta_workitems (one
+ *    work item per adapted expert with a non-empty block of the
+ *    expert-sorted rows, from the expert_offsets prefix sum),
+ *    apply_expert_lora_sorted and apply_router_lora (the delta of one pair
+ *    folded over a contiguous block of rows, in place).
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): a slot >= num_slots is excluded and counted as invalid; segments
@@ -331,4 +336,36 @@ void oracle_moe_w2_pairs(const uint16_t *x2, int64_t ldx, int32_t I,
             o[c] += d;
         }
     }
+}
+
+/* ------------------------------------------------------------------------
+ * O-expert-work: the work items of the expert-sorted fold.  expert_offsets
+ * has n_offsets entries, the prefix sum of rows per expert in the sorted
+ * layout, so there are n_experts = max(n_offsets - 1, 0) experts and expert
+ * e owns sorted rows offsets[e] .. offsets[e+1].  For each entry e of
+ * `adapted`, in order: no item when e >= n_experts or when
+ * offsets[e+1] <= offsets[e]; otherwise the item (e, offsets[e],
+ * offsets[e+1] - offsets[e]).  Returns the number of items written.
+ * ------------------------------------------------------------------------ */
+int32_t oracle_expert_workitems(const uint32_t *expert_offsets, int32_t n_offsets,
+                                const uint16_t *adapted, int32_t n_adapted,
+                                int32_t *item_expert, uint32_t *item_row_off,
+                                uint32_t *item_rows)
+{
+    const int32_t n_experts = n_offsets > 0 ? n_offsets - 1 : 0;
+    int32_t n_items = 0;
+    for (int32_t i = 0; i < n_adapted; ++i) {
+        const int32_t e = (int32_t)adapted[i];
+        if (e >= n_experts)
+            continue;
+        const uint32_t start = expert_offsets[e];
+        const uint32_t end = expert_offsets[e + 1];
+        if (end <= start)
+            continue;
+        item_expert[n_items] = e;
+        item_row_off[n_items] = start;
+        item_rows[n_items] = end - start;
+        ++n_items;
+    }
+    return n_items;
 }

@@ -20,6 +20,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 
@@ -53,6 +54,9 @@ def _bind(path: str):
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_double, _i32p,
                                          ctypes.c_int32, _f64p]
+    L.oracle_expert_workitems.restype = ctypes.c_int32
+    L.oracle_expert_workitems.argtypes = [_u32p, ctypes.c_int32, _u16p, ctypes.c_int32, _i32p,
+                                          _u32p, _u32p]
     L.oracle_moe_w2_pairs.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int32, _i64p, ctypes.c_int64,
                                       _i64p, ctypes.c_int64, _i32p, ctypes.c_int32, _i32p, _f32p,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -259,3 +263,45 @@ def case_moe_w2_pairs(case, pairs, weighted: bool = True, y=None):
     return moe_w2_pairs(case.x2, ta, sa, tb, sb, case.topk_ids, case.lora_ids,
                         case.topk_weights if weighted else None, case.E, case.L, case.R, case.H,
                         case.scale, case.y if y is None else y, pairs)
+
+
+# ---------------------------------------------------------------- expert-sorted fold
+def expert_workitems(expert_offsets, adapted):
+    """O-expert-work: [(expert, row_off, rows)] in the order of `adapted`."""
+    off = _c(expert_offsets, np.uint32).reshape(-1)
+    ad = _c(adapted, np.uint16).reshape(-1)
+    cap = max(1, ad.size)
+    ie = np.zeros(cap, np.int32)
+    io = np.zeros(cap, np.uint32)
+    ir = np.zeros(cap, np.uint32)
+    offp = _p(off, _u32p) if off.size else None
+    adp = _p(ad, _u16p) if ad.size else None
+    k = lib().oracle_expert_workitems(offp, off.size, adp, ad.size, _p(ie, _i32p), _p(io, _u32p),
+                                      _p(ir, _u32p))
+    return [(int(ie[i]), int(io[i]), int(ir[i])) for i in range(k)]
+
+
+def fold_sorted(x, k_in, base_out, items, pair_slot, a_pool, b_pool, scale, num_slots,
+                slice_sizes, max_rank, max_rows=None):
+    """The expert-sorted fold (apply_expert_lora_sorted): for each work item
+    (e, row_off, rows) whose expert has a pair (pair_slot[e] in [0, num_slots)),
+    the pair's delta on rows row_off .. row_off + rows, taken in chunks of at
+    most max_rows rows (fold_chunked); other rows keep base_out.  Returns all
+    rows, float64.  Items must not overlap."""
+    base_out = _c(base_out, np.uint16)
+    out = (base_out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    seen = np.zeros(base_out.shape[0], bool)
+    for e, r0, nr in items:
+        s = int(pair_slot[e])
+        if s < 0 or s >= num_slots:
+            continue
+        step = max(1, nr if max_rows is None else max_rows)
+        for c0 in range(r0, r0 + nr, step):
+            rows = np.arange(c0, min(r0 + nr, c0 + step), dtype=np.int32)
+            assert not seen[rows].any(), "work items overlap"
+            seen[rows] = True
+            slot = np.full(base_out.shape[0], -1, np.int32)
+            slot[rows] = s
+            out[rows] = fused_rows(x, k_in, a_pool, b_pool, scale, num_slots, slice_sizes, max_rank,
+                                   slot, rows, base_out)
+    return out

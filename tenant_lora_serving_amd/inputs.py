@@ -305,4 +305,64 @@ def moe_w2(seed: int = 6) -> MoeW2Case:
                        name="MoE w2 T=2048 H=4096 E=64 top8 I=1408 R=16 L=8")
 
 
+@dataclass
+class ExpertFoldCase:
+    name: str
+    E: int
+    n: int                     # sorted (expanded) rows
+    k_in: int
+    n_out: int
+    R: int
+    num_slots: int             # pairs in the pool (one per adapted expert)
+    expert_offsets: np.ndarray  # [E + 1] uint32 prefix sum of rows per expert
+    adapted: np.ndarray        # [num_slots] uint16 adapted experts, in pool-slot order
+    expert_slot: np.ndarray    # [E] int32 pool slot of each expert's pair, -1 = none
+    x: np.ndarray              # [n, k_in] uint16 sorted input
+    y: np.ndarray              # [n, n_out] uint16 sorted output (folded in place)
+    a_pool: np.ndarray         # [num_slots, 1, R, k_in]
+    b_pool: np.ndarray         # [num_slots, n_out, R]
+    scale: np.ndarray          # [num_slots] float32
+
+
+def make_expert_fold(seed: int, *, T: int, top_k: int, E: int, k_in: int, n_out: int, R: int,
+                     adapted_frac: float = 0.75, scale: float = 2.0,
+                     name: str = "custom expert fold") -> ExpertFoldCase:
+    """Expert-sorted rows of a routed MoE batch: each of T tokens picks top_k
+    distinct experts uniformly, expert e's rows are its tokens' copies
+    (expert_offsets is the prefix sum of the per-expert counts), and a random
+    `adapted_frac` of the experts has a pair (A ~ N(0, 1/k_in), B ~ N(0, 1/R))
+    at a random pool slot.  x, y ~ N(0, 1).  With T = n and E = 1, top_k = 1
+    it is the router fold's one block of all rows."""
+    rng = np.random.default_rng(seed)
+    topk = np.argsort(rng.random((T, E)), axis=1, kind="stable")[:, :top_k]
+    counts = np.bincount(topk.reshape(-1), minlength=E)
+    off = np.zeros(E + 1, np.uint32)
+    off[1:] = np.cumsum(counts)
+    n = int(off[-1])
+    n_ad = max(1, int(round(adapted_frac * E)))
+    adapted = rng.permutation(E)[:n_ad].astype(np.uint16)
+    slot = np.full(E, -1, np.int32)
+    slot[adapted.astype(np.int64)] = np.arange(n_ad, dtype=np.int32)
+    a_pool = _normal_bf16(rng, (n_ad, 1, R, k_in), 1.0 / np.sqrt(k_in))
+    b_pool = _normal_bf16(rng, (n_ad, n_out, R), 1.0 / np.sqrt(R))
+    x = _normal_bf16(rng, (n, k_in), 1.0)
+    y = _normal_bf16(rng, (n, n_out), 1.0)
+    return ExpertFoldCase(name, E, n, k_in, n_out, R, n_ad, off, adapted, slot, x, y, a_pool, b_pool,
+                          np.full(n_ad, scale, np.float32))
+
+
+def expert_fold(seed: int = 7) -> ExpertFoldCase:
+    """The gate_up projection of the MoE model in its expert-sorted layout:
+    T=2048 tokens, top_k 8 (16384 sorted rows), 64 experts of which 48 have a
+    pair, k_in 4096, n_out 2816 (2 x 1408), rank 16."""
+    return make_expert_fold(seed, T=2048, top_k=8, E=64, k_in=4096, n_out=2816, R=16,
+                            name="expert-sorted fold T=2048 top8 E=64 k_in=4096 n_out=2816 R=16")
+
+
+def router_fold(seed: int = 8) -> ExpertFoldCase:
+    """Router LoRA: 2048 tokens, hidden 4096, gate logits over 64 experts, rank 16."""
+    return make_expert_fold(seed, T=2048, top_k=1, E=1, k_in=4096, n_out=64, R=16, adapted_frac=1.0,
+                            name="router fold n=2048 hidden=4096 E=64 R=16")
+
+
 CONFIGS = {1: tiny_bgmv, 2: decode_bgmv, 3: prefill_sgmv, 4: no_reuse, 5: moe_gemm1}

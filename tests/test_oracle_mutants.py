@@ -65,6 +65,13 @@ MUTANTS = {
                         "d += xa[r] * bf(B[(int64_t)r * H + c]);"),
     "w2 y dropped": ("o[c] = bf(yp[c]);", "o[c] = 0.0;"),
     "w2 I loop short": ("for (int32_t i = 0; i < I; ++i)", "for (int32_t i = 0; i < I - 1; ++i)"),
+    "workitems keep empty blocks": ("        if (end <= start)\n            continue;",
+                                    "        if (end < start)\n            continue;"),
+    "workitems rows short": ("item_rows[n_items] = end - start;", "item_rows[n_items] = end - start - 1;"),
+    "workitems adapted reversed": ("const int32_t e = (int32_t)adapted[i];",
+                                   "const int32_t e = (int32_t)adapted[n_adapted - 1 - i];"),
+    "workitems start of next expert": ("const uint32_t start = expert_offsets[e];",
+                                       "const uint32_t start = expert_offsets[e + 1];"),
 }
 
 RUNNER = r"""

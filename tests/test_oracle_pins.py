@@ -472,3 +472,76 @@ def test_w2_single_expert_top1_is_bgmv():
     dense = O.fused_rows(c.x2, c.I, a_pool, b_pool, np.full(c.L, c.scale, np.float32), c.L, (c.H,),
                          c.R, c.lora_ids, np.arange(c.T), c.y)
     assert np.array_equal(dense, O.case_moe_w2_pairs(c, np.arange(c.T), False))
+
+
+# ============================================================ expert-sorted fold pins
+def test_expert_workitems_hand_example():
+    # 4 experts own sorted rows 0..3, 3..3 (empty), 3..7 and 7..12.  Adapted, in
+    # order: 2 -> (2, 3, 4); 0 -> (0, 0, 3); 9 is past the table; 1's block is
+    # empty; 3 -> (3, 7, 5).
+    got = O.expert_workitems([0, 3, 3, 7, 12], [2, 0, 9, 1, 3])
+    assert got == [(2, 3, 4), (0, 0, 3), (3, 7, 5)]
+
+
+def test_expert_workitems_degenerate():
+    assert O.expert_workitems([], [0, 1]) == []          # no table: no experts
+    assert O.expert_workitems([5], [0]) == []             # one offset: no experts
+    assert O.expert_workitems([0, 4, 9], []) == []        # nothing adapted
+    # a block whose end is not past its start is skipped, the next one is not
+    assert O.expert_workitems([0, 5, 2, 9], [1, 2]) == [(2, 2, 7)]
+    # an expert listed twice gives two items
+    assert O.expert_workitems([0, 2, 6], [1, 1]) == [(1, 2, 4), (1, 2, 4)]
+
+
+def test_expert_workitems_from_counts():
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        E = int(rng.integers(1, 40))
+        c = rng.integers(0, 5, size=E) * (rng.random(E) < 0.7)
+        off = np.concatenate([[0], np.cumsum(c)]).astype(np.uint32)
+        adapted = rng.permutation(E + 5)[: int(rng.integers(0, E + 5))]
+        want = [(int(e), int(c[:e].sum()), int(c[e])) for e in adapted if e < E and c[e] > 0]
+        assert O.expert_workitems(off, adapted) == want
+
+
+def _fold_case(seed=12, **kw):
+    args = dict(T=24, top_k=3, E=7, k_in=72, n_out=40, R=8, adapted_frac=0.6)
+    args.update(kw)
+    return I.make_expert_fold(seed, **args)
+
+
+def _fold(c, max_rows=None):
+    items = O.expert_workitems(c.expert_offsets, c.adapted)
+    return O.fold_sorted(c.x, c.k_in, c.y, items, c.expert_slot, c.a_pool, c.b_pool, c.scale,
+                         c.num_slots, (c.n_out,), c.R, max_rows)
+
+
+def test_fold_leaves_unadapted_rows_and_chunking_does_not_matter():
+    c = _fold_case()
+    whole = _fold(c)
+    row_expert = np.repeat(np.arange(c.E), np.diff(c.expert_offsets.astype(np.int64)))
+    unadapted = c.expert_slot[row_expert] < 0
+    assert unadapted.any() and (~unadapted).any()
+    assert np.array_equal(whole[unadapted], f32(c.y[unadapted]).astype(np.float64))
+    assert not np.array_equal(whole[~unadapted], f32(c.y[~unadapted]).astype(np.float64))
+    for mr in (1, 5):
+        assert np.array_equal(_fold(c, mr), whole)
+
+
+def test_fold_equals_dense_with_per_row_slots():
+    # the fold is the dense delta with each sorted row routed to its expert's slot
+    c = _fold_case(seed=13, E=9, adapted_frac=0.5)
+    row_expert = np.repeat(np.arange(c.E), np.diff(c.expert_offsets.astype(np.int64)))
+    slot = c.expert_slot[row_expert].astype(np.int32)
+    dense = O.fused_rows(c.x, c.k_in, c.a_pool, c.b_pool, c.scale, c.num_slots, (c.n_out,), c.R, slot,
+                         np.arange(c.n), c.y)
+    assert np.array_equal(_fold(c), dense)
+
+
+def test_router_fold_is_one_pair_over_all_rows():
+    c = I.make_expert_fold(14, T=30, top_k=1, E=1, k_in=64, n_out=16, R=8, adapted_frac=1.0)
+    x = f32(c.x).astype(np.float64)
+    A = f32(c.a_pool[0, 0]).astype(np.float64)
+    Bm = f32(c.b_pool[0]).astype(np.float64)
+    want = f32(c.y).astype(np.float64) + (float(c.scale[0]) * (x @ A.T)) @ Bm.T
+    np.testing.assert_allclose(_fold(c), want, rtol=1e-12, atol=1e-12)
