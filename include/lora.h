@@ -116,10 +116,33 @@ size_t lora_meta_workspace_bytes(int32_t n, int32_t num_slots);
  * invalid, excluded and counted in counts[2]).  All meta arrays are written
  * on the device; the result is unique (bit-exact).  n == 0 writes
  * counts = 0 and seg_offsets[0] = 0.  num_slots in [1, 1<<20]; when n > 1024
- * num_slots must be at most 16384 (LORA_EUNSUPPORTED otherwise).
+ * num_slots must be at most 8192 (LORA_EUNSUPPORTED otherwise).
  */
 int lora_meta_build(const int32_t *slot, int32_t n, int32_t num_slots, lora_meta_t meta,
                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Metadata for the expert-sorted fold (metrale source lora/expert_apply.rs:
+ * expert_delta_workitems, apply_expert_lora_sorted, apply_router_lora),
+ * built on the device from the expert_offsets prefix sum with no host copy.
+ * expert_offsets is [num_experts + 1] uint32 (device): expert e owns sorted
+ * rows expert_offsets[e] .. expert_offsets[e+1]; expert_slot is
+ * [num_experts] int32 (device), the pool slot of expert e's pair, or -1 when
+ * e has none.  The result is exactly lora_meta_build over n rows with
+ * slot[r] = expert_slot[e] for the e whose block holds r and -1 for rows in
+ * no block (and for rows >= expert_offsets[num_experts]), so
+ * lora_delta_fused with it folds each adapted expert's pair over its block
+ * of rows; a slot >= num_slots is counted as invalid.  The router fold is
+ * the case of one block {0, n} and one slot.  Offsets that are not
+ * non-decreasing are outside the contract: each row then still gets at most
+ * one expert (the one a binary search for the first offset above the row
+ * finds).  Workspace as for lora_meta_build.  Errors: LORA_EINVAL for bad
+ * sizes or null pointers, LORA_EUNSUPPORTED as for lora_meta_build,
+ * LORA_EWORKSPACE for a missing or small workspace.
+ */
+int lora_meta_from_offsets(const uint32_t *expert_offsets, int32_t num_experts,
+                           const int32_t *expert_slot, int32_t n, int32_t num_slots,
+                           lora_meta_t meta, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Shrink (vLLM punica_base.py, add_shrink semantics; metrale lora_delta,

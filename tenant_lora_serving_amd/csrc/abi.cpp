@@ -143,6 +143,20 @@ int lora_meta_build(const int32_t *slot, int32_t n, int32_t num_slots, lora_meta
                                           static_cast<hipStream_t>(stream)));
 }
 
+int lora_meta_from_offsets(const uint32_t *expert_offsets, int32_t num_experts, const int32_t *expert_slot,
+                           int32_t n, int32_t num_slots, lora_meta_t meta, void *ws, size_t ws_bytes,
+                           void *stream) {
+    if (int rc = check_meta_shape(n, num_slots)) return rc;
+    if (num_experts < 0 || num_experts > kMaxSlots) return LORA_EINVAL;
+    if (!meta_ok(meta) || !expert_offsets || (num_experts > 0 && !expert_slot)) return LORA_EINVAL;
+    const size_t need = meta_ws_bytes(n, num_slots);
+    if (need && (!ws || ws_bytes < need)) return LORA_EWORKSPACE;
+    tl::MetaOut out{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
+                    tile_bound(n, num_slots)};
+    return launched(tl::launch_meta_blocks(expert_offsets, expert_slot, num_experts, n, num_slots, out,
+                                           carve_meta_ws(ws, n), static_cast<hipStream_t>(stream)));
+}
+
 int lora_shrink(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
                 const float *scale, int32_t num_slots, int32_t num_slices, int32_t max_rank, lora_meta_t meta,
                 float *xa, void *stream) {

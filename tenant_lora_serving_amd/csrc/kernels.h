@@ -35,6 +35,8 @@ size_t meta_dyn_lds(int n, int S);
 hipError_t launch_meta_dense(const int32_t *slot, int n, int S, MetaOut out, MetaWs ws, hipStream_t st);
 hipError_t launch_meta_moe(const int32_t *topk, const int32_t *lora, int top_k, int E, int L, int n_pairs,
                            MetaOut out, MetaWs ws, hipStream_t st);
+hipError_t launch_meta_blocks(const uint32_t *offsets, const int32_t *block_slot, int n_blocks, int n, int S,
+                              MetaOut out, MetaWs ws, hipStream_t st);
 
 // Shapes of a dense call, validated by the caller.
 struct DenseShape {

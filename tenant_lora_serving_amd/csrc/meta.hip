@@ -46,6 +46,31 @@ struct SlotSrcMoe {
     }
 };
 
+// Expert-sorted rows (metrale expert_apply.rs: expert e owns sorted rows
+// offsets[e] .. offsets[e+1] of the expert_offsets prefix sum): key of row r
+// = slot[e] of the expert whose block holds r, -1 when none does.  The block
+// is found by binary search for the first offset above r, so every row gets
+// at most one expert even when the offsets are not a prefix sum.
+struct SlotSrcBlocks {
+    const uint32_t *off;  // [nb + 1]
+    const int32_t *slot;  // [nb]
+    int nb;
+    __device__ int32_t key(int r) const {
+        const uint32_t ur = (uint32_t)r;
+        int lo = 0, hi = nb + 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= ur)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        const int e = lo - 1;
+        if (e < 0 || e >= nb || off[e] > ur || ur >= off[e + 1]) return -1;
+        return slot[e];
+    }
+};
+
 struct MetaShared {
     uint32_t key[kMT];
     int32_t val[kMT];
@@ -412,6 +437,11 @@ hipError_t launch_meta_dense(const int32_t *slot, int n, int S, MetaOut out, Met
 hipError_t launch_meta_moe(const int32_t *topk, const int32_t *lora, int top_k, int E, int L, int n_pairs,
                            MetaOut out, MetaWs ws, hipStream_t st) {
     return launch_meta(SlotSrcMoe{topk, lora, top_k, E, L}, n_pairs, L * E, out, ws, st);
+}
+
+hipError_t launch_meta_blocks(const uint32_t *offsets, const int32_t *block_slot, int n_blocks, int n, int S,
+                              MetaOut out, MetaWs ws, hipStream_t st) {
+    return launch_meta(SlotSrcBlocks{offsets, block_slot, n_blocks}, n, S, out, ws, st);
 }
 
 }  // namespace tl

@@ -52,6 +52,9 @@ def lib():
         L.lora_meta_workspace_bytes.argtypes = [_c_i32, _c_i32]
         L.lora_meta_build.restype = ctypes.c_int
         L.lora_meta_build.argtypes = [_c_p, _c_i32, _c_i32, _MetaStruct, _c_p, _c_sz, _c_p]
+        L.lora_meta_from_offsets.restype = ctypes.c_int
+        L.lora_meta_from_offsets.argtypes = [_c_p, _c_i32, _c_p, _c_i32, _c_i32, _MetaStruct, _c_p, _c_sz,
+                                             _c_p]
         L.lora_shrink.restype = ctypes.c_int
         L.lora_shrink.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                   _MetaStruct, _c_p, _c_p]
@@ -86,7 +89,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build", "lora_shrink",
+EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build",
+            "lora_meta_from_offsets", "lora_shrink",
             "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused",
             "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "moe_lora_w2_workspace_bytes",
             "moe_lora_w2_delta", "lora_mfma_min_rows",
@@ -175,6 +179,26 @@ def lora_meta_build(slot: torch.Tensor, num_slots: int, meta: LoraMeta | None = 
 
 
 # ---------------------------------------------------------------- dense delta
+def lora_meta_from_offsets(expert_offsets: torch.Tensor, expert_slot: torch.Tensor, n: int,
+                           num_slots: int, meta: LoraMeta | None = None, stream=None) -> LoraMeta:
+    """Metadata of the expert-sorted fold: sorted row r takes the pool slot
+    expert_slot[e] of the expert e whose block of the expert_offsets prefix
+    sum ([E + 1] uint32 as int32 bits) holds it."""
+    E = expert_slot.numel()
+    if expert_offsets.numel() != E + 1:
+        raise ValueError("expert_offsets must have num_experts + 1 entries")
+    if expert_offsets.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("expert_offsets must be 32-bit")
+    if meta is None:
+        meta = LoraMeta.allocate(n, num_slots, expert_slot.device)
+    assert meta.n == n and meta.num_slots == num_slots, "metadata buffers sized for another batch"
+    st = lib().lora_meta_from_offsets(_dev(expert_offsets, "expert_offsets"), E,
+                                      _dev(expert_slot, "expert_slot", torch.int32), n, num_slots,
+                                      meta.struct(), meta.ws.data_ptr(), meta.ws.numel(), _stream(stream))
+    _check("lora_meta_from_offsets", st)
+    return meta
+
+
 def _pool_dims(a_pool=None, b_pool=None):
     if a_pool is not None:
         if a_pool.dim() != 4:
@@ -339,3 +363,32 @@ def moe_lora_w2_delta(x2: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: in
 def moe_counts(ws: torch.Tensor) -> torch.Tensor:
     """{n_active_pairs, n_segments, n_invalid_pairs, n_long_segments} of the last MoE call."""
     return ws[:16].view(torch.int32)
+
+
+# ---------------------------------------------------------------- expert-sorted and router folds
+def apply_expert_lora_sorted(x: torch.Tensor, base_out: torch.Tensor, expert_offsets: torch.Tensor,
+                             expert_slot: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor,
+                             scale: torch.Tensor, meta: LoraMeta | None = None,
+                             ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Fold each adapted expert's pair onto its block of the expert-sorted
+    output in place: base_out[r] += delta of pair expert_slot[e] for the rows
+    r of expert e (one pool slot per pair, one output slice)."""
+    n = x.shape[0]
+    meta = lora_meta_from_offsets(expert_offsets, expert_slot, n, a_pool.shape[0], meta, stream)
+    return lora_delta_fused(x, a_pool, b_pool, scale, (b_pool.shape[1],), meta, base_out, ws=ws,
+                            stream=stream)
+
+
+def apply_router_lora(router_in: torch.Tensor, gate_logits: torch.Tensor, a: torch.Tensor,
+                      b: torch.Tensor, scale: float, meta: LoraMeta | None = None,
+                      ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Fold the router pair (a [R, hidden], b [num_experts, R]) onto
+    gate_logits [n, num_experts] in place: one block of all n rows."""
+    n = router_in.shape[0]
+    dev = router_in.device
+    offsets = torch.tensor([0, n], dtype=torch.int32).to(dev, non_blocking=True)
+    slot0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    meta = lora_meta_from_offsets(offsets, slot0, n, 1, meta, stream)
+    scale_t = torch.full((1,), float(scale), dtype=torch.float32, device=dev)
+    return lora_delta_fused(router_in, a.reshape(1, 1, *a.shape), b.reshape(1, *b.shape), scale_t,
+                            (b.shape[0],), meta, gate_logits, ws=ws, stream=stream)

@@ -32,7 +32,7 @@ def L():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ["lora_meta_build", "lora_shrink", "lora_expand", "lora_delta_fused",
-              "moe_lora_gemm1_delta", "moe_lora_w2_delta"]:
+              "moe_lora_gemm1_delta", "moe_lora_w2_delta", "lora_meta_from_offsets"]:
         assert f in fns
 
 
@@ -131,6 +131,18 @@ def test_moe_validation(L):
     assert call(wa=None) == EINVAL
     assert call(wsb=need - 1) == EWS
     assert call(top_k=0) == EINVAL
+
+
+def test_meta_from_offsets_validation(L):
+    m = _meta()
+    assert L.lora_meta_from_offsets(None, 64, 0x2000, 100, 48, m, None, 0, None) == EINVAL
+    assert L.lora_meta_from_offsets(0x1000, 64, None, 100, 48, m, None, 0, None) == EINVAL
+    assert L.lora_meta_from_offsets(0x1000, -1, 0x2000, 100, 48, m, None, 0, None) == EINVAL
+    assert L.lora_meta_from_offsets(0x1000, 64, 0x2000, -5, 48, m, None, 0, None) == EINVAL
+    assert L.lora_meta_from_offsets(0x1000, 64, 0x2000, 100, 0, m, None, 0, None) == EINVAL
+    assert L.lora_meta_from_offsets(0x1000, 64, 0x2000, 100, 48, _meta(0), None, 0, None) == EINVAL
+    assert L.lora_meta_from_offsets(0x1000, 64, 0x2000, 5000, 48, m, None, 0, None) == EWS
+    assert L.lora_meta_from_offsets(0x1000, 64, 0x2000, 5000, 9000, m, 0x3000, 1 << 20, None) == EUNSUP
 
 
 def test_moe_w2_validation(L):

@@ -29,6 +29,11 @@ def check_meta(slot: np.ndarray, S: int):
     print(f"meta case n={slot.size} S={S}", flush=True)
     meta = B.lora_meta_build(d32(slot), S)
     torch.cuda.synchronize()
+    return assert_meta_matches(meta, slot, S)
+
+
+def assert_meta_matches(meta, slot: np.ndarray, S: int):
+    """Device metadata == the oracle's for the per-row slots, bit for bit."""
     rows, offs, sl, cnt = O.meta_build(slot, S)
     g_cnt = meta.counts.cpu().numpy()
     na, ns = int(cnt[0]), int(cnt[1])
