@@ -545,3 +545,59 @@ def test_router_fold_is_one_pair_over_all_rows():
     Bm = f32(c.b_pool[0]).astype(np.float64)
     want = f32(c.y).astype(np.float64) + (float(c.scale[0]) * (x @ A.T)) @ Bm.T
     np.testing.assert_allclose(_fold(c), want, rtol=1e-12, atol=1e-12)
+
+
+# ============================================================ tensor-parallel shard pins
+def _tp_case(seed=21, n=20, k_in=96, slices=(48, 32), S=3, R=16):
+    return I.make_dense(seed, n=n, k_in=k_in, slice_sizes=slices, num_slots=S, max_rank=R,
+                        slot_kind="uniform_neg")
+
+
+def test_rank_sharded_shrink_is_the_column_block_of_the_full_shrink():
+    # column-parallel S-LoRA: A split along the rank; each shard's xa is the
+    # matching rank columns of the full xa, exactly
+    c = _tp_case()
+    rows = np.arange(c.n)
+    full = O.shrink_rows(c.x, c.k_in, c.a_pool, c.scale, c.num_slots, c.num_slices, c.max_rank,
+                         c.slot, rows)
+    tp, rs = 2, c.max_rank // 2
+    for r in range(tp):
+        a_sh = np.ascontiguousarray(c.a_pool[:, :, r * rs:(r + 1) * rs, :])
+        part = O.shrink_rows(c.x, c.k_in, a_sh, c.scale, c.num_slots, c.num_slices, rs, c.slot, rows)
+        np.testing.assert_array_equal(part, full[:, :, r * rs:(r + 1) * rs])
+
+
+def test_k_sharded_shrink_partials_sum_to_the_full_shrink():
+    # row-parallel S-LoRA: x and A split along k; the all-reduce of the shards'
+    # xa is the full xa (up to the order of the fp64 sum)
+    c = _tp_case(seed=22, slices=(40,))
+    rows = np.arange(c.n)
+    active = (c.slot >= 0) & (c.slot < c.num_slots)
+    full = O.shrink_rows(c.x, c.k_in, c.a_pool, c.scale, c.num_slots, 1, c.max_rank, c.slot, rows)
+    tp = 4
+    ks = c.k_in // tp
+    total = np.zeros_like(full)
+    for r in range(tp):
+        x_sh = np.ascontiguousarray(c.x[:, r * ks:(r + 1) * ks])
+        a_sh = np.ascontiguousarray(c.a_pool[..., r * ks:(r + 1) * ks])
+        total += O.shrink_rows(x_sh, ks, a_sh, c.scale, c.num_slots, 1, c.max_rank, c.slot, rows)
+    np.testing.assert_allclose(total[active], full[active], rtol=1e-12, atol=1e-14)
+
+
+def test_offset_expand_of_a_column_shard_is_the_slice_of_the_full_expand():
+    # row-parallel S-LoRA: B split along the output; shard r adds its columns
+    # at offset_start = r * N / tp and leaves every other column alone
+    c = _tp_case(seed=23, slices=(64,))
+    rows = np.arange(c.n)
+    xa = np.random.default_rng(5).standard_normal((c.n, 1, c.max_rank))
+    full = O.expand_rows(xa, c.b_pool, c.num_slots, (64,), c.max_rank, c.slot, rows, c.y)
+    y = f32(c.y).astype(np.float64)
+    tp, ns = 4, 16
+    for r in range(tp):
+        b_sh = np.ascontiguousarray(c.b_pool[:, r * ns:(r + 1) * ns, :])
+        got = O.expand_rows(xa, b_sh, c.num_slots, (ns,), c.max_rank, c.slot, rows, c.y,
+                            offset_start=r * ns)
+        cols = np.arange(r * ns, (r + 1) * ns)
+        np.testing.assert_array_equal(got[:, cols], full[:, cols])
+        rest = np.setdiff1d(np.arange(64), cols)
+        np.testing.assert_array_equal(got[:, rest], y[:, rest])
