@@ -392,3 +392,28 @@ def apply_router_lora(router_in: torch.Tensor, gate_logits: torch.Tensor, a: tor
     scale_t = torch.full((1,), float(scale), dtype=torch.float32, device=dev)
     return lora_delta_fused(router_in, a.reshape(1, 1, *a.shape), b.reshape(1, *b.shape), scale_t,
                             (b.shape[0],), meta, gate_logits, ws=ws, stream=stream)
+
+
+# ---------------------------------------------------------------- logits and embedding variants
+def add_lora_logits(y: torch.Tensor, x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor,
+                    scale: torch.Tensor, sampler_slot: torch.Tensor, meta: LoraMeta | None = None,
+                    ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """LM-head logits delta: y[i, :vocab] += (scale[s] * x[i] @ A_s^T) @ B_s^T
+    for each sampled row i with s = sampler_slot[i] (a_pool [S, 1, R, hidden],
+    b_pool [S, vocab, R]), in place."""
+    meta = lora_meta_build(sampler_slot, a_pool.shape[0], meta, stream)
+    return lora_delta_fused(x, a_pool, b_pool, scale, (b_pool.shape[1],), meta, y, ws=ws,
+                            stream=stream)
+
+
+def add_lora_embedding(y: torch.Tensor, x: torch.Tensor, b_pool: torch.Tensor, slot: torch.Tensor,
+                       add_inputs: bool = True, meta: LoraMeta | None = None,
+                       stream=None) -> torch.Tensor:
+    """Embedding delta, expand only: y[i] (+)= x[i] @ B_s^T for s = slot[i],
+    with x [n, R] float32 (the adapter's embedding rows of the tokens) and
+    b_pool [S, hidden, R]."""
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise TypeError("x must be a 2-D float32 tensor [n, R]")
+    meta = lora_meta_build(slot, b_pool.shape[0], meta, stream)
+    return lora_expand(x.reshape(1, *x.shape), b_pool, (b_pool.shape[1],), meta, y,
+                       add_inputs=add_inputs, stream=stream)
