@@ -181,6 +181,9 @@ __device__ __forceinline__ void store_relaxed(int *p, int v) {
 __device__ __forceinline__ int atomic_add_relaxed(int *p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int xchg_relaxed(int *p, int v) {
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // 64-bit words read and written as single atomic units: a value with the
 // tag of the call that wrote it travels in one word, so a reader that sees
 // the tag also sees the value, with no fence on either side.

@@ -65,6 +65,8 @@ constexpr int kXaBytes = kTileRows * kMaxRank * 4;  // LDS for a tile's xa (fp32
 constexpr int kBStage = 128 * 32 + (128 * 32 / 128) * 8;  // bf16 per wave: 128 columns x 32 ranks + padding
 constexpr int kEB = 512;      // output columns per expand batch (128 per wave); a unit has 1, 2 or 4
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its units take several k steps
+constexpr int kFlagWords = 64;      // 64-bit words per tile: piece flags, then the finished-consumer count
 // control line of the workspace
 constexpr int kCtlError = 0;  // set when a bounded wait gave up
 constexpr int kCtlGen = 1;    // completed calls on this workspace
@@ -113,11 +115,12 @@ __device__ __forceinline__ void store_x(const u32x4_t (&xv)[4], uint16_t *xs) {
 }
 __device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 
-// Vector-ALU shrink of one unit into pu[j * n_rr + rr] (rr < n_rr, j < m).
+// Vector-ALU shrink of a one-step unit (k1 - k0 <= kKP) into pu[j * n_rr + rr]
+// (rr < n_rr, j < m).
 // Lane (rl = lane / 16, kl = lane % 16) of wave w holds rank rows
 // rb + 4w + rl + 16i (i < RPL) at k = k0 + 128s + 8kl (s < 4).
 template <int RPL, class Op>
-__device__ __forceinline__ void shrink_valu(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
+__device__ __forceinline__ void shrink_valu_1(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
                                             uint64_t *pu, uint32_t tag) {
     const int lane = lane_id(), w = wave_id();
     const int rl = lane >> 4, kl = lane & 15;
@@ -184,10 +187,10 @@ __device__ __forceinline__ void shrink_valu(const Op &op, const Hdr &h, int k0, 
     }
 }
 
-// MFMA shrink of one unit: wave w takes rank-row groups g = w, w+4, ... of 16;
+// MFMA shrink of a one-step unit: wave w takes rank-row groups g = w, w+4, ... of 16;
 // D[tile row][rank row] = x[16 x 32k] . A^T over 16 steps of 32 k.
 template <class Op>
-__device__ __forceinline__ void shrink_mfma(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
+__device__ __forceinline__ void shrink_mfma_1(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
                                             uint64_t *pu, uint32_t tag) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
@@ -224,15 +227,157 @@ __device__ __forceinline__ void shrink_mfma(const Op &op, const Hdr &h, int k0, 
     }
 }
 
+// Vector-ALU shrink of a unit of several k steps: as shrink_valu_1 for each
+// step of kKP, x staged once per (rank-row pass, step), and the per-row sums
+// of the steps added up before they are stored.
+template <int RPL, class Op>
+__device__ __forceinline__ void shrink_valu_n(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
+                                            uint64_t *pu, uint32_t tag) {
+    const int lane = lane_id(), w = wave_id();
+    const int rl = lane >> 4, kl = lane & 15;
+    const int n_rr = op.n_rr(), m = h.m;
+    u32x4_t a[RPL][4];
+    auto load_a = [&](int rb, int ks, int ke) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int rr = rb + 4 * w + rl + 16 * i;
+            const uint16_t *ap = rr < n_rr ? op.arow(h.slot, rr) : nullptr;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = ks + 128 * s + 8 * kl;
+                a[i][s] = (ap && k < ke) ? ld16_stream(ap + k) : zero4();
+            }
+        }
+    };
+    // x of k step [ks, ke) into LDS, with the A of pass rb issued before the barrier
+    auto stage = [&](int rb, int ks, int ke, bool reuse) {
+        u32x4_t xv[4];
+        load_x(op, h, ks, ke, xv);  // x first: the LDS store below waits only for these
+        load_a(rb, ks, ke);
+        if (reuse) __syncthreads();  // every wave is done with the previous x
+        store_x(xv, xs);
+        __syncthreads();
+    };
+    for (int rb = 0; rb < n_rr; rb += 16 * RPL) {
+        float sv[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = k0; ks < k1; ks += kKP) {
+            const int ke = min(k1, ks + kKP);
+            stage(rb, ks, ke, rb > 0 || ks > k0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (4 * b < m) {
+                    float acc[RPL][4];
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = 0.f;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        u32x4_t xv[4];
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) xv[jj] = lds16(xs + (4 * b + jj) * kXS + 128 * s + 8 * kl);
+#pragma unroll
+                        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) acc[i][jj] = dot8(a[i][s], xv[jj], acc[i][jj]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = group_sum(acc[i][jj], 4);
+                    // lane kl keeps value kl = 4i + jj of its row of lanes
+                    float v = acc[0][0];
+#pragma unroll
+                    for (int q = 1; q < 4 * RPL; ++q) v = kl == q ? acc[q >> 2][q & 3] : v;
+                    sv[b] += v;
+                }
+            }
+        }
+        const int i = kl >> 2, jj = kl & 3;
+        const int rr = rb + 4 * w + rl + 16 * i;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = 4 * b + jj;
+            if (kl < 4 * RPL && rr < n_rr && j < m) store_word64(pu + j * n_rr + rr, tagged(sv[b], tag));
+        }
+    }
+}
+
+// MFMA shrink of a unit of several k steps: as shrink_mfma_1 for each step,
+// the accumulators kept across the steps;
+// D[tile row][rank row] = x[16 x 32k] . A^T over 16 steps of 32 k.
+template <class Op>
+__device__ __forceinline__ void shrink_mfma_n(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
+                                            uint64_t *pu, uint32_t tag) {
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 15, kq = lane >> 4;
+    const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
+    u32x4_t av[16];
+    auto load_a = [&](int g, int ks, int ke) {
+        const int rr = 16 * g + col;
+        const uint16_t *ap = (g < G && rr < n_rr) ? op.arow(h.slot, rr) : nullptr;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int k = ks + 32 * s + 8 * kq;
+            av[s] = (ap && k < ke) ? ld16_stream(ap + k) : zero4();
+        }
+    };
+    auto stage = [&](int g, int ks, int ke, bool reuse) {
+        u32x4_t xv[4];
+        load_x(op, h, ks, ke, xv);
+        load_a(g, ks, ke);
+        if (reuse) __syncthreads();  // every wave is done with the previous x
+        store_x(xv, xs);
+        __syncthreads();
+    };
+    auto store = [&](int g, const f32x4_t &acc) {
+        // lane holds D[4kq + i][col]: tile rows 4kq..4kq+3 of rank row rr
+        const int rr = 16 * g + col;
+        if (g < G && rr < n_rr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kq + i < h.m) store_word64(pu + (4 * kq + i) * n_rr + rr, tagged(acc[i], tag));
+        }
+    };
+    // passes of 8 groups of 16 rank rows (two per wave, the same number of
+    // passes for every wave); the accumulators live across the steps, and x
+    // is staged once per step of a pass
+    const int passes = (G + 7) >> 3;
+    for (int ps = 0; ps < passes; ++ps) {
+        const int g0 = w + 8 * ps, g1 = g0 + 4;
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = k0; ks < k1; ks += kKP) {
+            const int ke = min(k1, ks + kKP);
+            stage(g0, ks, ke, ps > 0 || ks > k0);
+            if (g0 < G) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    acc0 = mfma_16x16x32(lds16(xs + col * kXS + 32 * s + 8 * kq), av[s], acc0);
+            }
+            if (g1 < G) {
+                load_a(g1, ks, ke);
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    acc1 = mfma_16x16x32(lds16(xs + col * kXS + 32 * s + 8 * kq), av[s], acc1);
+            }
+        }
+        store(g0, acc0);
+        store(g1, acc1);
+    }
+}
+
 // ============================================================ expand units
 // Wait until pieces [0, P) of the tile carry this call's tag (threads p < P
-// poll flag p with relaxed loads); false if a bounded wait gave up.
-__device__ __forceinline__ bool wait_pieces(const int *flags, int P, uint32_t tag, int *ctl, int *ok_lds) {
+// poll flag p with relaxed loads); false if a bounded wait gave up.  A flag is
+// the word {tag, tag}: whatever an earlier call of another layout left at its
+// address (a flag, or a partial word {value, older tag}) has an older tag in
+// its upper half.
+__device__ __forceinline__ bool wait_pieces(const uint64_t *flags, int P, uint32_t tag, int *ctl, int *ok_lds) {
     if (threadIdx.x == 0) *ok_lds = 1;
     __syncthreads();
     for (int p = threadIdx.x; p < P; p += kFT) {
         int spins = 0;
-        while ((uint32_t)load_relaxed(flags + p) != tag) {
+        while ((uint32_t)(load_word64(flags + p) >> 32) != tag) {
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
                 atomicExch(ctl + kCtlError, 1);
@@ -294,7 +439,7 @@ __device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, in
 // What an expand unit needs to find its xa.
 struct XaSrc {
     const uint64_t *pt;  // the tile's partial blocks
-    const int *flags;    // the tile's piece flags
+    const uint64_t *flags;  // the tile's piece flags
     int P, xb;
     bool coalesce_b;     // VALU expand: stage B through LDS with coalesced loads
     float sc;
@@ -677,16 +822,19 @@ __device__ __forceinline__ Unit unit_of(int bid, int tile_bound, int P, int C) {
 struct FusedArgs {
     const int32_t *tiles;
     const int32_t *counts;  // counts[4] = tiles in use
-    int tile_bound, P, FP, C;
+    int tile_bound, P, C;
+    int KS;          // k steps of kKP per shrink unit
     int EC;          // output columns per expand unit (a multiple of kEB)
     uint64_t *part;  // [tile_bound][P][n_rr][16] tagged partials
     int *ctl;        // control line
-    int *flags;      // [tile_bound][FP]: piece flags, then the tile's finished consumers at FP - 1
+    uint64_t *flags;  // [tile_bound][kFlagWords]: piece flags, then the tile's finished consumers
     int mfma_min, add_inputs;
 };
 
+// Mode 2 (calls whose tiles are mostly on the MFMA path) asks for three waves
+// per SIMD: its registers fit without spills up to rank 64.
 template <int RPL, int NRS, int WM, class Op>
-__global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
+__global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
     constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = WM == 1 ? kXaBytes + 4 * kBStage * 2 : kXaBytes;
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
@@ -703,17 +851,35 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
             const int p = un.sub;
             const Hdr h = load_hdr(fa.tiles, t);
             if (h.m == 0) return;
-            const int k0 = p * kKP, k1 = min(op.k_in, k0 + kKP);
+            uint64_t *fl = fa.flags + (int64_t)t * kFlagWords;
+            // piece 0 zeroes the tile's consumer count (whatever an earlier
+            // call left there); the exchange returns before its flag is
+            // stored, and every consumer counts only after seeing that flag
+            int old = 0;
+            if (p == 0 && threadIdx.x == 0) old = xchg_relaxed(reinterpret_cast<int *>(fl + kFlagWords - 1), 0);
+            // (k0 written as a multiple of kKP: the loads' addressing depends on it)
+            const int k0 = (p * fa.KS) * kKP, k1 = min(op.k_in, k0 + fa.KS * kKP);
             uint64_t *pu = fa.part + ((int64_t)t * P + p) * n_rr * 16;
             uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
-            if (h.mseg >= fa.mfma_min)
-                shrink_mfma(op, h, k0, k1, xs, pu, tag);
-            else
-                shrink_valu<RPL>(op, h, k0, k1, xs, pu, tag);
+            // units of several k steps exist only in the wide modes
+            if (h.mseg >= fa.mfma_min) {
+                if (WM != 0 && fa.KS > 1)
+                    shrink_mfma_n(op, h, k0, k1, xs, pu, tag);
+                else
+                    shrink_mfma_1(op, h, k0, k1, xs, pu, tag);
+            } else {
+                if (WM != 0 && fa.KS > 1)
+                    shrink_valu_n<RPL>(op, h, k0, k1, xs, pu, tag);
+                else
+                    shrink_valu_1<RPL>(op, h, k0, k1, xs, pu, tag);
+            }
             // raise the flag after every wave has issued its stores (the tags,
             // not this order, are what make the hand-off correct)
             __syncthreads();
-            if (threadIdx.x == 0) store_relaxed(fa.flags + (int64_t)t * fa.FP + p, (int)tag);
+            if (threadIdx.x == 0) {
+                asm volatile("" : : "v"(old) : "memory");  // the exchange has returned
+                store_word64(fl + p, ((uint64_t)tag << 32) | tag);
+            }
             return;
         }
         const int cc = un.sub;
@@ -722,7 +888,7 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         if (h.m == 0) return;
         int l, c0, c1;
         chunk_of(op, cc, fa.EC, l, c0, c1);
-        const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * fa.FP, P, op.xblk(l),
+        const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P, op.xblk(l),
                        fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw};
         if (h.mseg >= fa.mfma_min)
             expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
@@ -732,9 +898,8 @@ __global__ __launch_bounds__(kFT) void fused_kernel(Op op, FusedArgs fa, ZeroFil
         // finished tile of the call advances the generation (two levels, so
         // no single address takes one atomic per consumer)
         if (threadIdx.x == 0) {
-            int *tile_done = fa.flags + (int64_t)t * fa.FP + fa.FP - 1;
+            int *tile_done = reinterpret_cast<int *>(fa.flags + (int64_t)t * kFlagWords + kFlagWords - 1);
             if (atomic_add_relaxed(tile_done, 1) == C - 1) {
-                store_relaxed(tile_done, 0);
                 if (atomic_add_relaxed(fa.ctl + kCtlDone, 1) == n_tiles - 1) {
                     store_relaxed(fa.ctl + kCtlDone, 0);
                     store_relaxed(fa.ctl + kCtlGen, (int)tag);
@@ -770,7 +935,7 @@ template <int RPL, int NRS, class Op>
 static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, bool mfma_lean, long long grid, ZeroFill zf,
                                  hipStream_t st) {
     const dim3 g((unsigned)grid), b(kFT);
-    if (fa.EC <= kEB)
+    if (fa.EC <= kEB && fa.KS == 1)
         hipLaunchKernelGGL((fused_kernel<RPL, NRS, 0, Op>), g, b, 0, st, op, fa, zf);
     else if (!mfma_lean)
         hipLaunchKernelGGL((fused_kernel<RPL, NRS, 1, Op>), g, b, 0, st, op, fa, zf);
@@ -800,19 +965,30 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     fa.tiles = tiles;
     fa.counts = counts;
     fa.tile_bound = plan.tile_bound;
-    fa.P = plan.P;
-    fa.FP = plan.FP;
+    // k steps per shrink unit: one while the call has few tiles (decode: its
+    // latency wants every piece in flight at once); wide calls give each unit
+    // several steps so that about kShrinkUnits units remain; and at most
+    // kFlagWords - 1 pieces fit a tile's flag block
+    const int steps = (op.k_in + kKP - 1) / kKP;
+    int ks = 1;
+    if (EC > kEB && plan.tile_bound > 0) {
+        const int pieces = std::min(steps, std::max(1, (kShrinkUnits + plan.tile_bound - 1) / plan.tile_bound));
+        ks = (steps + pieces - 1) / pieces;
+    }
+    ks = std::max(ks, (steps + kFlagWords - 2) / (kFlagWords - 1));
+    fa.KS = ks;
+    fa.P = (steps + ks - 1) / ks;
     fa.C = C;
     fa.EC = EC;
     fa.ctl = reinterpret_cast<int *>(w);
-    fa.flags = fa.ctl + 64;
+    fa.flags = reinterpret_cast<uint64_t *>(w + 256);
     fa.part = reinterpret_cast<uint64_t *>(w + plan.flag_bytes);
     fa.mfma_min = mfma_min;
     fa.add_inputs = add_inputs;
     // every shrink unit ahead of every expand unit.  (Interleaving groups of
     // producers and consumers measured slower on the large configs: consumers
     // that start before their producers hold workgroup slots.)
-    const long long n_shrink = ((long long)plan.tile_bound * plan.P + kXcds - 1) / kXcds * kXcds;
+    const long long n_shrink = ((long long)plan.tile_bound * fa.P + kXcds - 1) / kXcds * kXcds;
     const long long grid = plan.tile_bound > 0 ? n_shrink + (long long)plan.tile_bound * C + zero_units
                                                : zero_units;
     if (grid == 0) return hipSuccess;

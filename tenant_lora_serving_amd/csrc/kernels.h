@@ -56,8 +56,6 @@ struct DenseShape {
 // Fused-call workspace layout (all sizes derived from the shape).
 struct FusedPlan {
     int tile_bound;  // tile records the meta build wrote
-    int P;           // k pieces of the shrink
-    int FP;          // ints per tile: P piece flags and a consumer count (P + 1 rounded up to 64)
     size_t flag_bytes, part_bytes, total_bytes;
 };
 FusedPlan fused_plan(int n, int num_slots, int num_slices, int R, int k_in, int n_out);

@@ -189,6 +189,37 @@ def test_fused_workspace_reused_across_shapes(decode_case):
     assert ws[:16].view(torch.int32).cpu().tolist()[:3] == [0, 6, 0]
 
 
+def test_fused_workspace_reused_across_layouts(decode_case):
+    """Calls whose tile counts, pieces per tile and rank rows differ share one
+    workspace: each call's flags and consumer counts land where an earlier
+    call kept partials of another layout, and every result is still right."""
+    few_tiles_big_partials = small_case(12, n=40, k_in=4096, slices=(64, 32), S=3, R=64)
+    many_tiles_multi_step = small_case(13, n=5000, k_in=4096, slices=(4096,), S=4, R=16, neg=0.05)
+    cases = [decode_case, few_tiles_big_partials, decode_case, many_tiles_multi_step,
+             few_tiles_big_partials, decode_case]
+    need = max(int(B.lib().lora_fused_workspace_bytes(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in))
+               for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, case in enumerate(cases):
+        print(f"layout reuse call {i}: n={case.n} k_in={case.k_in} R={case.max_rank}", flush=True)
+        dv = Dev(case)
+        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, case.slice_sizes, dv.meta, dv.y, ws=ws)
+        torch.cuda.synchronize()
+        rows = np.arange(case.n) if case.n <= 512 else np.arange(case.n)[::17]
+        check_y(dv, h16(dv.y), rows, f"layout reuse {i}")
+    assert ws[:16].view(torch.int32).cpu().tolist()[:3] == [0, len(cases), 0]
+
+
+def test_fused_k_beyond_one_flag_block(path):
+    # 65 k steps: more pieces than a tile's flag block holds, so each shrink
+    # unit takes two steps even in a decode-sized call
+    c = small_case(14, n=24, k_in=65 * 512 + 8, slices=(48,), S=3, R=16)
+    dv = Dev(c)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
+    torch.cuda.synchronize()
+    check_y(dv, h16(dv.y), np.arange(c.n), f"k_in={c.k_in} {path}")
+
+
 def test_zero_scale_is_bitwise_noop(decode_case):
     c = decode_case
     dv = Dev(c)
