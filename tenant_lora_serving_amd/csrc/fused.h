@@ -394,8 +394,70 @@ __device__ __forceinline__ bool wait_pieces(const uint64_t *flags, int P, uint32
 // summed in piece order, times the slot's scale and, with RW, the row's
 // weight rw[j] (rows j >= m are zero).
 // MF: bf16 hi/lo pairs xl[j][0..R) = hi, xl[j][R..2R) = lo; else fp32 xf[j][R].
-template <bool MF, bool RW>
+// Thread -> (row j, rank r) with r fastest, in Q = 16R / 256 <= QM passes; the
+// loads of every pass are issued together, 16 words per thread in flight
+// (QM passes x 16/QM pieces per round trip).
+template <bool MF, bool RW, int QM>
 __device__ __forceinline__ void stage_xa(const uint64_t *pt, int P, int n_rr, int xb, int R, int m, float sc,
+                                         const float *rw, uint32_t tag, int *ctl, char *lds) {
+    constexpr int PB = 16 / QM;
+    const int64_t pstride = (int64_t)n_rr * 16;
+    const int n_ent = R * kTileRows;
+    const uint64_t *qp[QM];
+    bool ok[QM];
+    float s[QM];
+#pragma unroll
+    for (int q = 0; q < QM; ++q) {
+        const int idx = threadIdx.x + kFT * q, j = idx / R, r = idx - j * R;
+        ok[q] = idx < n_ent && j < m;
+        qp[q] = pt + (int64_t)j * n_rr + xb * R + r;
+        s[q] = 0.f;
+    }
+    for (int p0 = 0; p0 < P; p0 += PB) {
+        uint64_t v[QM][PB];
+#pragma unroll
+        for (int q = 0; q < QM; ++q)
+#pragma unroll
+            for (int u = 0; u < PB; ++u)
+                v[q][u] = (ok[q] && p0 + u < P) ? load_word64(qp[q] + (p0 + u) * pstride) : 0;
+#pragma unroll
+        for (int q = 0; q < QM; ++q)
+#pragma unroll
+            for (int u = 0; u < PB; ++u) {
+                if (ok[q] && p0 + u < P) {
+                    // a flag can become visible before the data it announces
+                    int spins = 0;
+                    while ((uint32_t)(v[q][u] >> 32) != tag && spins++ < kSpinLimit)
+                        v[q][u] = load_word64(qp[q] + (p0 + u) * pstride);
+                    if ((uint32_t)(v[q][u] >> 32) != tag) atomicExch(ctl + kCtlError, 1);
+                    s[q] += __uint_as_float((uint32_t)v[q][u]);
+                }
+            }
+    }
+#pragma unroll
+    for (int q = 0; q < QM; ++q) {
+        const int idx = threadIdx.x + kFT * q, j = idx / R, r = idx - j * R;
+        if (idx >= n_ent) continue;
+        float x = 0.f;
+        if (ok[q]) {
+            x = s[q] * sc;
+            if (RW) x *= rw[j];
+        }
+        if (MF) {
+            uint16_t *xl = reinterpret_cast<uint16_t *>(lds);
+            const float hi = bf16_round(x);
+            xl[j * 2 * R + r] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+            xl[j * 2 * R + R + r] = __builtin_bit_cast(uint16_t, (__bf16)(x - hi));
+        } else {
+            reinterpret_cast<float *>(lds)[j * R + r] = x;
+        }
+    }
+}
+
+// stage_xa pass by pass (each pass's pieces in flight together): fewer live
+// registers, for the vector-ALU expand, whose prefetch registers are live here.
+template <bool MF, bool RW>
+__device__ __forceinline__ void stage_xa_passes(const uint64_t *pt, int P, int n_rr, int xb, int R, int m, float sc,
                                          const float *rw, uint32_t tag, int *ctl, char *lds) {
     const int64_t pstride = (int64_t)n_rr * 16;
     // thread -> (row j, rank r) with r fastest: one pass covers 256 / R rows,
@@ -601,7 +663,7 @@ __device__ __forceinline__ void valu_load_y(const Op &op, const Hdr &h, int c, i
 // when R <= 32); 2, as 1 but the vector-ALU path loads each batch when it
 // starts, which frees the registers (and LDS) of the prefetch for calls
 // whose tiles are mostly on the MFMA path.
-template <int WM, class Op>
+template <int WM, int NRS, class Op>
 __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                             const XaSrc &xs, char *lds) {
     constexpr bool WIDE = WM != 0, PREFETCH = WM == 1;
@@ -623,7 +685,8 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
     if (tr) valu_transpose(raw, R, bst, bq);
     load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
-    stage_xa<false, Op::kRowWeights>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.rw, xs.tag, xs.ctl, lds);
+    stage_xa_passes<false, Op::kRowWeights>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.rw, xs.tag, xs.ctl,
+                                            lds);
     __syncthreads();
     const float *xf = reinterpret_cast<const float *>(lds);
     for (int b = 0; b < nb; ++b) {
@@ -709,7 +772,8 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
     mfma_load_y(yp, c0 + 128 * w, c1, add_inputs, yv);
     load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
-    stage_xa<true, Op::kRowWeights>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.rw, xs.tag, xs.ctl, lds);
+    stage_xa<true, Op::kRowWeights, 2 * NRS>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.rw, xs.tag, xs.ctl,
+                                             lds);
     __syncthreads();
     const uint16_t *xl = reinterpret_cast<const uint16_t *>(lds) + col * 2 * R;
     u32x4_t hv[NRS], lv[NRS];
@@ -893,7 +957,7 @@ __global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kern
         if (h.mseg >= fa.mfma_min)
             expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         else
-            expand_valu<WM>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+            expand_valu<WM, NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         // the last consumer of a tile counts the tile as finished; the last
         // finished tile of the call advances the generation (two levels, so
         // no single address takes one atomic per consumer)
