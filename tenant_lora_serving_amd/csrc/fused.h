@@ -852,12 +852,15 @@ __device__ __forceinline__ void chunk_of(const Op &op, int cc, int EC, int &l, i
 }
 
 // ============================================================ unit order
-// Workgroup ids: the shrink units (tile t, piece p) at t*P + p, padded to a
-// multiple of 8; then the expand units; then the MoE zero-row units.  Every
-// consumer therefore has a higher id than the producers it waits on.
-// Workgroups go to the 8 XCDs round robin (id mod 8), and each XCD has its
-// own L2: with P = 8, XCD p runs piece p of every tile, so each A piece is
-// fetched by one XCD.  Expand units come in blocks of 8 tiles x C chunks; in
+// Workgroup ids: the shrink units first (padded to a multiple of 8), then
+// the expand units, then the MoE zero-row units, so every consumer has a
+// higher id than the producers it waits on.  Workgroups go to the 8 XCDs
+// round robin (id mod 8), and each XCD has its own L2.  Shrink units
+// (tile t, piece p), u = t*P + p: with P a multiple of 8, unit u sits at id u,
+// so XCD p runs piece p of every tile and each A piece is fetched by one XCD;
+// otherwise XCD x runs the contiguous run of units x*U/8 .. (x+1)*U/8 in order
+// (U the padded count), so the tiles of one segment, which read the same A,
+// run one after another on the same XCD.  Expand units come in blocks of 8 tiles x C chunks; in
 // a full block, XCD x runs the C units k = x*C .. x*C + C - 1 of the
 // chunk-major order (chunk k / 8 of tile k mod 8), so a chunk's B rows, which
 // the 8 tiles of a long segment share, reach at most two L2s instead of all
@@ -872,7 +875,10 @@ __device__ __forceinline__ int shrink_span(int tile_bound, int P) {
 }
 __device__ __forceinline__ Unit unit_of(int bid, int tile_bound, int P, int C) {
     const int nS = shrink_span(tile_bound, P), nE = tile_bound * C;
-    if (bid < nS) return Unit{kUnitShrink, bid / P, bid - (bid / P) * P};
+    if (bid < nS) {
+        const int u = (P & (kXcds - 1)) == 0 ? bid : (bid & (kXcds - 1)) * (nS / kXcds) + bid / kXcds;
+        return Unit{kUnitShrink, u / P, u - (u / P) * P};
+    }
     if (bid >= nS + nE) return Unit{kUnitZero, 0, bid - nS - nE};
     const int e = bid - nS, blk = kXcds * C;
     const int g = e / blk, q = e - g * blk;
