@@ -309,14 +309,22 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
     if (tid == 0) n_long = n_invalid = 0;
     __syncthreads();
     if (tid < n && raw >= S) atomicAdd(&n_invalid, 1);
-    // rank among the wave's rows of the same slot: with few slots one ballot
-    // per slot value (no scalar round trips), else one per distinct slot
+    // rank among the wave's rows of the same slot.  Few slots: one ballot per
+    // bit of the slot number, a lane's group being the lanes that agree on
+    // every bit; else one ballot per distinct slot present in the wave.
     int rank = 0;
-    if (S <= kSmallBallotSlots) {
-        for (int k = 0; k < S; ++k) {
-            const uint64_t same = __ballot(key == k);
-            if (key == k) rank = __popcll(same & lanemask_lt());
-            if (lane == 0) tab[k * W + w] = __popcll(same);
+    const bool few = S <= kSmallBallotSlots;
+    if (few) {
+        uint64_t same = __ballot(active);
+        const int nbits = S > 1 ? 32 - __clz(S - 1) : 0;
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t mb = __ballot(active && bit);
+            same &= bit ? mb : ~mb;
+        }
+        if (active) {
+            rank = __popcll(same & lanemask_lt());
+            if (rank == 0) tab[key * W + w] = __popcll(same);  // the group's first lane
         }
     } else {
         uint64_t pending = __ballot(active);
@@ -330,39 +338,77 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
         }
     }
     __syncthreads();
-    // per-slot totals: {rows, segments, tiles}, scanned over the slots
-    const int per = (S + NT - 1) / NT;
-    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
-    Int3 loc = {0, 0, 0};
-    for (int k = s0; k < s1; ++k) {
-        int t = 0;
-#pragma unroll
-        for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
-        loc = loc + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
-        if (t >= kTileRows) atomicAdd(&n_long, 1);
-    }
     Int3 tot;
-    Int3 run = block_excl_scan3<NT>(loc, scan3, tot);
-    for (int k = s0; k < s1; ++k) {
-        int t = 0;
-        int base = run.a;
+    if (few) {
+        // wave 0 scans the slots, lane k holding slot k
+        if (w == 0) {
+            const int k = lane;
+            int t = 0;
+            if (k < S) {
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) {
-            const int c = tab[k * W + ww];
-            tab[k * W + ww] = base;
-            base += c;
-            t += c;
+                for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
+            }
+            const Int3 v = {t, t > 0, (t + kTileRows - 1) / kTileRows};
+            const Int3 inc = wave_incl_scan3(v);
+            const Int3 run = {inc.a - v.a, inc.b - v.b, inc.c - v.c};
+            if (k < S) {
+                int base = run.a;
+#pragma unroll
+                for (int ww = 0; ww < W; ++ww) {
+                    const int c = tab[k * W + ww];
+                    tab[k * W + ww] = base;
+                    base += c;
+                }
+                seg_idx[k] = run.b;
+                tile_off[k] = run.c;
+                start[k] = run.a;
+                if (t > 0) {
+                    out.seg_offsets[run.b] = run.a;
+                    out.seg_slot[run.b] = k;
+                }
+            }
+            const uint64_t lng = __ballot(k < S && t >= kTileRows);
+            if (lane == kWave - 1) {
+                scan3[0] = inc;  // the last lane's inclusive sums are the totals
+                n_long = __popcll(lng);
+            }
         }
-        seg_idx[k] = run.b;
-        tile_off[k] = run.c;
-        start[k] = run.a;
-        if (t > 0) {
-            out.seg_offsets[run.b] = run.a;
-            out.seg_slot[run.b] = k;
+        __syncthreads();
+        tot = scan3[0];
+    } else {
+        // per-slot totals: {rows, segments, tiles}, scanned over the slots
+        const int per = (S + NT - 1) / NT;
+        const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+        Int3 loc = {0, 0, 0};
+        for (int k = s0; k < s1; ++k) {
+            int t = 0;
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
+            loc = loc + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+            if (t >= kTileRows) atomicAdd(&n_long, 1);
         }
-        run = run + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+        Int3 run = block_excl_scan3<NT>(loc, scan3, tot);
+        for (int k = s0; k < s1; ++k) {
+            int t = 0;
+            int base = run.a;
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) {
+                const int c = tab[k * W + ww];
+                tab[k * W + ww] = base;
+                base += c;
+                t += c;
+            }
+            seg_idx[k] = run.b;
+            tile_off[k] = run.c;
+            start[k] = run.a;
+            if (t > 0) {
+                out.seg_offsets[run.b] = run.a;
+                out.seg_slot[run.b] = k;
+            }
+            run = run + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (active) {
         const int pos = tab[key * W + w] + rank;
         const int st = start[key];
