@@ -13,9 +13,10 @@ that no step finds its adapters in the 256 MB Infinity Cache.
 
 Timed region: exactly K steps, replayed from one HIP graph, bracketed by
 torch.cuda.synchronize().  value = algorithmic bytes of the K steps / wall
-time (GB/s).  The fused kernel's own average duration is measured with HIP
-events around each launch on the launch stream in a second region of K
-eager launches; it gives the roofline fraction against 8 TB/s.  The fp64 CPU
+time (GB/s).  The fused kernel's own average duration is measured with two
+HIP events on the launch stream bracketing a second region of K back-to-back
+eager launches (elapsed / K); it gives the roofline fraction against 8 TB/s.
+The metadata kernel is timed the same way.  The fp64 CPU
 oracle is timed on the same batch on the host cores (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -177,28 +178,24 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
 
-    # ---- kernel durations: HIP events around each launch on the launch stream
-    for s in sets:
-        B.lora_meta_build(s["slot"], case.num_slots, s["meta"])
+    # ---- kernel durations: HIP events on the launch stream bracketing K
+    # back-to-back launches of one kernel (the metadata is built beforehand)
+    B.lora_meta_build(sets[0]["slot"], case.num_slots, sets[0]["meta"])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        s = sets[i % copies]
-        ev[i][0].record(stream)
-        B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes, s["meta"], s["y"],
-                           ws=s["ws"])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    fused_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    evm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        s = sets[i % copies]
-        evm[i][0].record(stream)
-        B.lora_meta_build(s["slot"], case.num_slots, s["meta"])
-        evm[i][1].record(stream)
-    torch.cuda.synchronize()
-    meta_ms = float(np.mean([a.elapsed_time(b) for a, b in evm]))
+
+    def region(launch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            launch(sets[i % copies])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    fused_ms = region(lambda s: B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes,
+                                                   s["meta"], s["y"], ws=s["ws"]))
+    meta_ms = region(lambda s: B.lora_meta_build(s["slot"], case.num_slots, s["meta"]))
 
     value = bytes_step * K / wall / 1e9
     fused_gbs = bytes_step / (fused_ms * 1e-3) / 1e9
