@@ -64,6 +64,7 @@ constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x ti
 constexpr int kXaBytes = kTileRows * kMaxRank * 4;  // LDS for a tile's xa (fp32, or bf16 hi/lo pairs)
 constexpr int kBStage = 128 * 32 + (128 * 32 / 128) * 8;  // bf16 per wave: 128 columns x 32 ranks + padding
 constexpr int kEB = 512;      // output columns per expand batch (128 per wave); a unit has 1, 2 or 4
+constexpr int kDtStride = 68;  // fp32 row stride of a wave's 16 x 64 output tile in LDS (64 + 4 pad)
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its units take several k steps
 constexpr int kFlagWords = 64;      // 64-bit words per tile: piece flags, then the finished-consumer count
@@ -747,13 +748,20 @@ __device__ __forceinline__ void mfma_load_b(const Op &op, const Hdr &h, int cw0,
         }
     }
 }
-__device__ __forceinline__ void mfma_load_y(const uint16_t *yp, int cw0, int c1, bool add_inputs, uint2 (&yv)[8]) {
-    const int kq = lane_id() >> 4;
+// y of a wave's 16 rows x 128 columns in the row-major order of its stores:
+// yv[4hf + j] holds row 4j + lane/16, columns cw0 + 64hf + 4(lane%16) .. +4
+// (a row's 64 columns are 16 lanes x 8 contiguous bytes).
+__device__ __forceinline__ void mfma_load_y(uint16_t *const (&yr)[4], int cw0, int c1, bool add_inputs,
+                                            uint2 (&yv)[8]) {
+    const int cl = 4 * (lane_id() & 15);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        const int cy = cw0 + 16 * ct + 4 * kq;
-        yv[ct] = (add_inputs && yp && cy < c1) ? *reinterpret_cast<const uint2 *>(yp + cy) : make_uint2(0u, 0u);
-    }
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cy = cw0 + 64 * hf + cl;
+            yv[4 * hf + j] = (add_inputs && yr[j] && cy < c1) ? *reinterpret_cast<const uint2 *>(yr[j] + cy)
+                                                              : make_uint2(0u, 0u);
+        }
 }
 
 template <int NRS, bool WIDE, class Op>
@@ -763,13 +771,21 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
     const int col = lane & 15, kq = lane >> 4;
     const int R = op.R;
     const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
-    // output row = col, columns cw0 + 16ct + 4kq .. +4 (8 bytes)
-    const int rid = __shfl(h.rec, kRecRowIds + col, kWave);
-    uint16_t *yp = col < h.m ? op.yrow(rid) : nullptr;
+    // D comes out as row = col, columns 16ct + 4kq .. +4; y is read and
+    // written row-major (rows 4j + lane/16, 8 bytes per lane) and the two
+    // meet through a per-wave fp32 tile in LDS
+    uint16_t *yr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 4 * j + (lane >> 4);
+        const int rid = __shfl(h.rec, kRecRowIds + row, kWave);
+        yr[j] = row < h.m ? op.yrow(rid) : nullptr;
+    }
+    float *dt = reinterpret_cast<float *>(lds + kXaBytes) + w * kTileRows * kDtStride;
     u32x4_t bo[8][NRS];
     uint2 yv[8];
     mfma_load_b<NRS>(op, h, c0 + 128 * w, c1, R, bo);
-    mfma_load_y(yp, c0 + 128 * w, c1, add_inputs, yv);
+    mfma_load_y(yr, c0 + 128 * w, c1, add_inputs, yv);
     load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
     stage_xa<true, Op::kRowWeights, 2 * NRS>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.rw, xs.tag, xs.ctl,
@@ -803,24 +819,32 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
             if (WIDE && hf == 1 && b + 1 < nb) {
                 // the MFMAs above were the last readers of this batch's B
                 mfma_load_b<NRS>(op, h, cw0 + kEB, c1, R, bo);
-                mfma_load_y(yp, cw0 + kEB, c1, add_inputs, yv_n);
+                mfma_load_y(yr, cw0 + kEB, c1, add_inputs, yv_n);
             }
+            // the half's 16 x 64 block through the wave's LDS tile: written in
+            // the MFMA layout, read back row-major, added to y, stored
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ct = 4 * hf + i;
-                const int cy = cw0 + 16 * ct + 4 * kq;
-                if (yp && cy < c1) {
-                    float v[4] = {d[i][0], d[i][1], d[i][2], d[i][3]};
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4_t *>(dt + col * kDtStride + 16 * i + 4 * kq) = d[i];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4_t o = *reinterpret_cast<const f32x4_t *>(dt + (4 * j + (lane >> 4)) * kDtStride +
+                                                                    4 * (lane & 15));
+                const int cy = cw0 + 64 * hf + 4 * (lane & 15);
+                if (yr[j] && cy < c1) {
+                    float v[4] = {o[0], o[1], o[2], o[3]};
                     if (add_inputs) {
-                        v[0] += bf_lo(yv[ct].x);
-                        v[1] += bf_hi(yv[ct].x);
-                        v[2] += bf_lo(yv[ct].y);
-                        v[3] += bf_hi(yv[ct].y);
+                        const uint2 yy = yv[4 * hf + j];
+                        v[0] += bf_lo(yy.x);
+                        v[1] += bf_hi(yy.x);
+                        v[2] += bf_lo(yy.y);
+                        v[3] += bf_hi(yy.y);
                     }
-                    *reinterpret_cast<uint2 *>(yp + cy) =
+                    *reinterpret_cast<uint2 *>(yr[j] + cy) =
                         make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
             }
+            __builtin_amdgcn_wave_barrier();
         }
         if (WIDE && b + 1 < nb) {
 #pragma unroll
@@ -906,7 +930,9 @@ struct FusedArgs {
 template <int RPL, int NRS, int WM, class Op>
 __global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
-    constexpr int kLdsShrink = kTileRows * kXS * 2, kLdsExpand = WM == 1 ? kXaBytes + 4 * kBStage * 2 : kXaBytes;
+    constexpr int kLdsShrink = kTileRows * kXS * 2;
+    constexpr int kLdsStage = WM == 1 ? 4 * kBStage * 2 : 0, kLdsTile = 4 * kTileRows * kDtStride * 4;
+    constexpr int kLdsExpand = kXaBytes + (kLdsStage > kLdsTile ? kLdsStage : kLdsTile);
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     __shared__ int ok;
     __shared__ float rw[Op::kRowWeights ? kTileRows : 1];
