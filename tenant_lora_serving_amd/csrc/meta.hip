@@ -25,6 +25,10 @@
 namespace tl {
 
 constexpr int kMT = 1024;  // threads per workgroup = rows per chunk
+constexpr int kMetaTable = 16384;  // LDS ints for the assembling workgroup's [chunk][slot] table and slot arrays
+constexpr int kAsmBatch = 8;       // chunks whose entries the assembling workgroup loads at once
+
+__host__ __device__ inline bool meta_table_fits(int n_chunks, int S) { return (long long)(4 + n_chunks) * S <= kMetaTable; }
 
 struct SlotSrcDense {
     const int32_t *slot;
@@ -202,16 +206,50 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
     __threadfence();
 
     int *start = dyn, *segidx = dyn + S, *tileoff = dyn + 2 * S, *rc = dyn + 3 * S;
+    // With a [chunk][slot] table in LDS, every chunk's rows are placed at once:
+    // cb[c][s] = rows of slot s in chunks before c.  Otherwise the chunks are
+    // scattered one after another, rc[s] counting the rows already placed.
+    const bool table = meta_table_fits(n_chunks, S);
+    int *cb = dyn + 4 * S;
+    if (table) {
+        for (int i = tid; i < n_chunks * S; i += kMT) cb[i] = 0;
+    }
     for (int s = tid; s < S; s += kMT) rc[s] = 0;
     __syncthreads();
-    // rows per slot (integer atomics: order does not matter)
-    for (int cc = 0; cc < n_chunks; ++cc) {
-        const int64_t idx = (int64_t)cc * kMT + tid;
-        const uint32_t k2 = (uint32_t)ws.keys[idx];
-        const int ol = ws.offlen[idx];
-        if (k2 < (uint32_t)S && (ol & 0xffff) == 0) atomicAdd(&rc[k2], ol >> 16);
+    // rows per slot (and per chunk): each run's first entry carries its length;
+    // the loads of kAsmBatch chunks are issued before any is used
+    for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
+        uint32_t kb[kAsmBatch];
+        int ob[kAsmBatch];
+#pragma unroll
+        for (int u = 0; u < kAsmBatch; ++u) {
+            const int64_t idx = (int64_t)(c0 + u) * kMT + tid;
+            kb[u] = c0 + u < n_chunks ? (uint32_t)ws.keys[idx] : (uint32_t)S;
+            ob[u] = c0 + u < n_chunks ? ws.offlen[idx] : 1;
+        }
+#pragma unroll
+        for (int u = 0; u < kAsmBatch; ++u) {
+            if (kb[u] < (uint32_t)S && (ob[u] & 0xffff) == 0) {
+                if (table)
+                    cb[(c0 + u) * S + kb[u]] = ob[u] >> 16;
+                else
+                    atomicAdd(&rc[kb[u]], ob[u] >> 16);
+            }
+        }
     }
     __syncthreads();
+    if (table) {
+        for (int s2 = tid; s2 < S; s2 += kMT) {
+            int acc = 0;
+            for (int cc = 0; cc < n_chunks; ++cc) {
+                const int v = cb[cc * S + s2];
+                cb[cc * S + s2] = acc;
+                acc += v;
+            }
+            rc[s2] = acc;
+        }
+        __syncthreads();
+    }
     // scan {rows, segments, tiles} over slots, each thread a contiguous block
     const int per = (S + kMT - 1) / kMT;
     const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
@@ -248,8 +286,39 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
         out.counts[4] = tot.c;
         out.counts[5] = out.counts[6] = out.counts[7] = 0;
     }
+    if (table) {
+        for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
+            uint32_t kb[kAsmBatch];
+            int ob[kAsmBatch], rb[kAsmBatch];
+#pragma unroll
+            for (int u = 0; u < kAsmBatch; ++u) {
+                const int64_t idx = (int64_t)(c0 + u) * kMT + tid;
+                const bool in = c0 + u < n_chunks;
+                kb[u] = in ? (uint32_t)ws.keys[idx] : (uint32_t)S;
+                ob[u] = in ? ws.offlen[idx] : 0;
+                rb[u] = in ? ws.rows[idx] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kAsmBatch; ++u) {
+                const int cc = c0 + u;
+                const uint32_t k2 = kb[u];
+                if (k2 >= (uint32_t)S) continue;
+                const int ol = ob[u];
+                const int row = rb[u];
+                const int o = cb[cc * S + k2] + (ol & 0xffff);
+                const int dest = start[k2] + o;
+                const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
+                out.sorted_rows[dest] = row;
+                const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
+                int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+                rec[kRecRowIds + j] = row;
+                if (j == 0)
+                    write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2]);
+            }
+        }
+    }
     // scatter the chunks in order; rc[s] counts the rows of slot s already placed
-    for (int cc = 0; cc < n_chunks; ++cc) {
+    for (int cc = 0; !table && cc < n_chunks; ++cc) {
         const int64_t idx = (int64_t)cc * kMT + tid;
         const uint32_t k2 = (uint32_t)ws.keys[idx];
         const int ol = ws.offlen[idx];
@@ -446,7 +515,11 @@ static size_t small_lds(int n, int S) { return ((size_t)S * (small_threads(n) / 
 
 int meta_chunks(int n) { return n <= 0 ? 1 : (n + kMT - 1) / kMT; }
 
-size_t meta_dyn_lds(int n, int S) { return meta_chunks(n) > 1 ? (size_t)4 * S * sizeof(int) : 0; }
+size_t meta_dyn_lds(int n, int S) {
+    const int c = meta_chunks(n);
+    if (c <= 1) return 0;
+    return (size_t)(meta_table_fits(c, S) ? 4 + c : 4) * S * sizeof(int);
+}
 
 template <int NT, class Src>
 static hipError_t launch_small(Src src, int n, int S, MetaOut out, hipStream_t st) {
