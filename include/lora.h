@@ -242,7 +242,12 @@ size_t moe_lora_w2_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts
  * [0, num_experts) keep their y row; the last two are counted as invalid
  * (the counts at the start of ws as for moe_lora_gemm1_delta).  With T = 0
  * only the counts are written, and x2, topk_ids, lora_ids and y may be
- * null.  Errors:
+ * null.  reuse_routing != 0 skips the pair metadata build and uses the one
+ * already in ws (vLLM's add_lora_w2 reuses the routing add_lora_w13 built):
+ * the caller guarantees that the previous MoE call on this workspace (gemm1
+ * or w2) had the same T, top_k, num_experts, num_loras, topk_ids and
+ * lora_ids; a workspace of the larger of moe_lora_workspace_bytes and
+ * moe_lora_w2_workspace_bytes serves both calls.  Errors:
  * LORA_EINVAL for bad sizes, strides or pointers, LORA_EUNSUPPORTED for a
  * rank outside {8, 16, ..., 128}, LORA_EWORKSPACE for a missing or small
  * workspace; nothing is launched on error.
@@ -253,7 +258,7 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I,
                       const int32_t *topk_ids, int32_t top_k, const int32_t *lora_ids,
                       const float *topk_weights, int32_t num_experts, int32_t num_loras,
                       int32_t rank, int32_t H, float scale, uint16_t *y, int64_t ldy,
-                      void *ws, size_t ws_bytes, void *stream);
+                      int32_t reuse_routing, void *ws, size_t ws_bytes, void *stream);
 
 /* Segments with at least this many rows take the MFMA path, shorter ones the
  * vector-ALU path (default 16; the environment variable LORA_MFMA_MIN_ROWS,

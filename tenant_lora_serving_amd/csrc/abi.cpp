@@ -309,8 +309,8 @@ size_t moe_lora_w2_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts
 int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, const int64_t *w_ptr_a,
                       int64_t lora_stride_a, const int64_t *w_ptr_b, int64_t lora_stride_b, const int32_t *topk_ids,
                       int32_t top_k, const int32_t *lora_ids, const float *topk_weights, int32_t num_experts,
-                      int32_t num_loras, int32_t rank, int32_t H, float scale, uint16_t *y, int64_t ldy, void *ws,
-                      size_t ws_bytes, void *stream) {
+                      int32_t num_loras, int32_t rank, int32_t H, float scale, uint16_t *y, int64_t ldy,
+                      int32_t reuse_routing, void *ws, size_t ws_bytes, void *stream) {
     if (T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1) return LORA_EINVAL;
     if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return LORA_EINVAL;
     if (int rc = check_rank(rank)) return rc;
@@ -332,9 +332,11 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, con
                    reinterpret_cast<int32_t *>(b + lay.segslot), reinterpret_cast<int32_t *>(b + lay.counts),
                    reinterpret_cast<int32_t *>(b + lay.tiles), tile_bound(n, S)};
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
-                                       carve_meta_ws(b + lay.meta_ws, n), st);
-    if (e != hipSuccess) return LORA_ELAUNCH;
+    if (!reuse_routing) {
+        const hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
+                                                 carve_meta_ws(b + lay.meta_ws, n), st);
+        if (e != hipSuccess) return LORA_ELAUNCH;
+    }
     if (n == 0) return LORA_OK;
     tl::MoeW2Shape m{x2, ldx, T, I, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, top_k, topk_weights,
                      num_experts, num_loras, rank, H, scale, y, ldy};

@@ -78,7 +78,7 @@ def lib():
         L.moe_lora_w2_delta.restype = ctypes.c_int
         L.moe_lora_w2_delta.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64,
                                         _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
-                                        _c_f, _c_p, _c_i64, _c_p, _c_sz, _c_p]
+                                        _c_f, _c_p, _c_i64, _c_i32, _c_p, _c_sz, _c_p]
         L.lora_mfma_min_rows.restype = _c_i32
         L.lora_mfma_min_rows.argtypes = []
         L.lora_set_mfma_min_rows.restype = None
@@ -331,9 +331,14 @@ def moe_lora_w2_delta(x2: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: in
                       w_ptr_b: torch.Tensor, lora_stride_b: int, topk_ids: torch.Tensor,
                       lora_ids: torch.Tensor, rank: int, y: torch.Tensor, *, num_loras: int,
                       topk_weights: torch.Tensor | None = None, scale: float = 1.0,
-                      ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                      ws: torch.Tensor | None = None, reuse_routing: bool = False,
+                      stream=None) -> torch.Tensor:
     """Add the routed down-projection delta to y ([T*top_k, H] or [T, top_k, H])
-    in place; x2 holds the pairs' activated gemm1 outputs, [T*top_k, I]."""
+    in place; x2 holds the pairs' activated gemm1 outputs, [T*top_k, I].
+    reuse_routing: ws holds the pair metadata of this routing from the
+    previous MoE call on it (the gemm1 delta), so it is not rebuilt."""
+    if reuse_routing and ws is None:
+        raise ValueError("reuse_routing needs the workspace of the previous MoE call")
     if w_ptr_a.dim() != 1 or w_ptr_b.dim() != 1:
         raise ValueError("w2 pointer tables are [num_experts]")
     E = w_ptr_a.shape[0]
@@ -354,8 +359,8 @@ def moe_lora_w2_delta(x2: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: in
         xp, ldx, T, I, _dev(w_ptr_a, "w_ptr_a", torch.int64), int(lora_stride_a),
         _dev(w_ptr_b, "w_ptr_b", torch.int64), int(lora_stride_b),
         _dev(topk_ids, "topk_ids", torch.int32), top_k, _dev(lora_ids, "lora_ids", torch.int32), wp,
-        E, int(num_loras), int(rank), H, float(scale), yp, ldy, _dev(ws, "ws", torch.uint8),
-        ws.numel(), _stream(stream))
+        E, int(num_loras), int(rank), H, float(scale), yp, ldy, 1 if reuse_routing else 0,
+        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     _check("moe_lora_w2_delta", st)
     return y
 

@@ -155,7 +155,7 @@ def test_moe_w2_validation(L):
         v = dict(base, **kw)
         return L.moe_lora_w2_delta(v["x"], v["ldx"], v["T"], v["I"], v["wa"], v["lsa"], v["wb"], v["lsb"],
                                    v["topk"], v["top_k"], v["lora"], v["wt"], v["E"], v["L"], v["R"],
-                                   v["H"], 1.0, v["y"], v["ldy"], ws, wsb, None)
+                                   v["H"], 1.0, v["y"], v["ldy"], 0, ws, wsb, None)
     assert call(I=1404) == EINVAL
     assert call(ldx=1400) == EINVAL
     assert call(R=20) == EUNSUP

@@ -149,3 +149,33 @@ def test_w2_deterministic_and_ws_reuse(w2_case):
     ex = small.topk_ids.reshape(-1)
     valid = np.flatnonzero((lora >= 0) & (lora < small.L) & (ex >= 0) & (ex < small.E))
     assert_close(bf64(check_small[valid]), O.case_moe_w2_pairs(small, valid, True), "small on shared ws")
+
+
+def test_w2_reuses_the_gemm1_routing():
+    """The down projection after gemm1 on one workspace: with reuse_routing the
+    pair metadata gemm1 built is used as is, and the result is bit for bit the
+    one of a call that builds it."""
+    c = small_w2(9, T=300, E=4, top_k=2, I=264, H=520, R=16, L=3)
+    g = I.make_moe(9, T=c.T, H=136, E=c.E, top_k=c.top_k, I=64, R=c.R, L=c.L)
+    g.topk_ids[:] = c.topk_ids
+    g.lora_ids[:] = c.lora_ids
+    n1 = int(B.lib().moe_lora_workspace_bytes(c.T, c.top_k, c.E, c.L, c.R, g.H))
+    n2 = int(B.lib().moe_lora_w2_workspace_bytes(c.T, c.top_k, c.E, c.L, c.R, c.I))
+    ws = torch.zeros(max(n1, n2), dtype=torch.uint8, device="cuda")
+    # gemm1 on the shared workspace builds the routing
+    Ag, Au, Bg, Bu = d16(g.a_gate), d16(g.a_up), d16(g.b_gate), d16(g.b_up)
+    ta = torch.tensor([[M.data_ptr() + e * g.L * g.R * g.H * 2 for e in range(g.E)] for M in (Ag, Au)],
+                      dtype=torch.int64).cuda()
+    tb = torch.tensor([[M.data_ptr() + e * g.L * g.I * g.R * 2 for e in range(g.E)] for M in (Bg, Bu)],
+                      dtype=torch.int64).cuda()
+    B.moe_lora_gemm1_delta(d16(g.x), ta, g.R * g.H, tb, g.I * g.R, d32(g.topk_ids), d32(g.lora_ids), g.R,
+                           g.I, num_loras=g.L, ws=ws)
+    keep, wa, sa, wb, sb = device_tables(c)
+    y_reuse = d16(c.y)
+    B.moe_lora_w2_delta(d16(c.x2), wa, sa, wb, sb, d32(c.topk_ids), d32(c.lora_ids), c.R, y_reuse,
+                        num_loras=c.L, topk_weights=d32(c.topk_weights), scale=c.scale, ws=ws,
+                        reuse_routing=True)
+    torch.cuda.synchronize()
+    fresh, _ = run_w2(c, True)
+    assert np.array_equal(h16(y_reuse), fresh)
+    del keep
