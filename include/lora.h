@@ -93,7 +93,8 @@ enum {
  *       Each segment is cut into tiles of at most 16 consecutive sorted rows.
  *       Record t (32 int32): [0] slot, [1] first sorted position, [2] rows in
  *       the tile (0 marks an unused record), [3] rows in the whole segment,
- *       [4] segment index, [8..23] the tile's original row ids.
+ *       [4] segment index, [5] the tile's index within its segment,
+ *       [8..23] the tile's original row ids.
  * Entries past n_active / n_segments are left unwritten.
  */
 typedef struct {

@@ -16,7 +16,8 @@ constexpr int kWave = 64;
 constexpr int kTileRows = 16;    // rows per tile record (the MFMA M dimension)
 constexpr int kTileWords = 32;   // int32 words per tile record
 // tile record fields
-constexpr int kRecSlot = 0, kRecPos = 1, kRecRows = 2, kRecSegRows = 3, kRecSeg = 4, kRecRowIds = 8;
+constexpr int kRecSlot = 0, kRecPos = 1, kRecRows = 2, kRecSegRows = 3, kRecSeg = 4, kRecSegTile = 5,
+              kRecRowIds = 8;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }

@@ -367,6 +367,53 @@ __device__ __forceinline__ void shrink_mfma_n(const Op &op, const Hdr &h, int k0
     }
 }
 
+// MFMA shrink of two consecutive tiles of one segment (tile rows of h0, then
+// of h1, staged together), several k steps: each A fragment feeds both
+// tiles' MFMAs, so the segment's A is read once for the pair.  Wave w owns
+// rank-row group w (at most 4 groups).
+template <class Op>
+__device__ __forceinline__ void shrink_mfma_pair(const Op &op, const Hdr &h0, const Hdr &h1, int k0, int k1,
+                                                 uint16_t *xs, uint64_t *pu0, uint64_t *pu1, uint32_t tag) {
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 15, kq = lane >> 4;
+    const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
+    const int rr = 16 * w + col;
+    const uint16_t *ap = (w < G && rr < n_rr) ? op.arow(h0.slot, rr) : nullptr;
+    u32x4_t av[16];
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    uint16_t *xs1 = xs + kTileRows * kXS;
+    for (int ks = k0; ks < k1; ks += kKP) {
+        const int ke = min(k1, ks + kKP);
+        u32x4_t xv0[4], xv1[4];
+        load_x(op, h0, ks, ke, xv0);
+        load_x(op, h1, ks, ke, xv1);
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            const int k = ks + 32 * s2 + 8 * kq;
+            av[s2] = (ap && k < ke) ? ld16_stream(ap + k) : zero4();
+        }
+        if (ks > k0) __syncthreads();  // every wave is done with the previous x
+        store_x(xv0, xs);
+        store_x(xv1, xs1);
+        __syncthreads();
+        if (w < G) {
+#pragma unroll
+            for (int s2 = 0; s2 < 16; ++s2) {
+                acc0 = mfma_16x16x32(lds16(xs + col * kXS + 32 * s2 + 8 * kq), av[s2], acc0);
+                acc1 = mfma_16x16x32(lds16(xs1 + col * kXS + 32 * s2 + 8 * kq), av[s2], acc1);
+            }
+        }
+    }
+    // lane holds D[4kq + i][col]: tile rows 4kq..4kq+3 of rank row rr
+    if (w < G && rr < n_rr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (4 * kq + i < h0.m) store_word64(pu0 + (4 * kq + i) * n_rr + rr, tagged(acc0[i], tag));
+            if (4 * kq + i < h1.m) store_word64(pu1 + (4 * kq + i) * n_rr + rr, tagged(acc1[i], tag));
+        }
+    }
+}
+
 // ============================================================ expand units
 // Wait until pieces [0, P) of the tile carry this call's tag (threads p < P
 // poll flag p with relaxed loads); false if a bounded wait gave up.  A flag is
@@ -930,7 +977,7 @@ struct FusedArgs {
 template <int RPL, int NRS, int WM, class Op>
 __global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
-    constexpr int kLdsShrink = kTileRows * kXS * 2;
+    constexpr int kLdsShrink = (WM != 0 ? 2 : 1) * kTileRows * kXS * 2;  // wide modes stage tile pairs
     constexpr int kLdsStage = WM == 1 ? 4 * kBStage * 2 : 0, kLdsTile = 4 * kTileRows * kDtStride * 4;
     constexpr int kLdsExpand = kXaBytes + (kLdsStage > kLdsTile ? kLdsStage : kLdsTile);
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
@@ -947,6 +994,31 @@ __global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kern
             const int p = un.sub;
             const Hdr h = load_hdr(fa.tiles, t);
             if (h.m == 0) return;
+            const int k0p = (p * fa.KS) * kKP, k1p = min(op.k_in, k0p + fa.KS * kKP);
+            // wide calls: MFMA segments with at most 64 rank rows are shrunk two
+            // tiles at a time, by the unit of the pair's first tile (the tile
+            // with an even index within its segment); the second tile's unit
+            // has nothing to do
+            if (WM != 0 && h.mseg >= fa.mfma_min && n_rr <= 64) {
+                const int jt = __builtin_amdgcn_readlane(h.rec, kRecSegTile);
+                if (jt & 1) return;
+                if (h.mseg > kTileRows * (jt + 1)) {
+                    const Hdr h1 = load_hdr(fa.tiles, t + 1);
+                    uint64_t *fl0 = fa.flags + (int64_t)t * kFlagWords, *fl1 = fl0 + kFlagWords;
+                    int old = 0;
+                    if (p == 0 && threadIdx.x < 2)
+                        old = xchg_relaxed(reinterpret_cast<int *>((threadIdx.x == 0 ? fl0 : fl1) + kFlagWords - 1), 0);
+                    shrink_mfma_pair(op, h, h1, k0p, k1p, reinterpret_cast<uint16_t *>(lds),
+                                     fa.part + ((int64_t)t * P + p) * n_rr * 16,
+                                     fa.part + ((int64_t)(t + 1) * P + p) * n_rr * 16, tag);
+                    __syncthreads();
+                    if (threadIdx.x < 2) {
+                        asm volatile("" : : "v"(old) : "memory");  // the exchange has returned
+                        store_word64((threadIdx.x == 0 ? fl0 : fl1) + p, ((uint64_t)tag << 32) | tag);
+                    }
+                    return;
+                }
+            }
             uint64_t *fl = fa.flags + (int64_t)t * kFlagWords;
             // piece 0 zeroes the tile's consumer count (whatever an earlier
             // call left there); the exchange returns before its flag is

@@ -115,13 +115,13 @@ __device__ __forceinline__ void radix_pass(uint32_t &key, int32_t &val, int shif
 }
 
 __device__ __forceinline__ void write_tile_header(int32_t *rec, int slot, int pos, int rows, int seg_rows,
-                                                  int seg) {
+                                                  int seg, int jt) {
     rec[kRecSlot] = slot;
     rec[kRecPos] = pos;
     rec[kRecRows] = rows;
     rec[kRecSegRows] = seg_rows;
     rec[kRecSeg] = seg;
-    rec[5] = 0;
+    rec[kRecSegTile] = jt;
     rec[6] = 0;
     rec[7] = 0;
 }
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
             const int t = sh.run_tile[run_id] + off / kTileRows, j = off % kTileRows;
             int32_t *rec = out.tiles + (int64_t)t * kTileWords;
             rec[kRecRowIds + j] = val;
-            if (j == 0) write_tile_header(rec, (int)key, tid, min(kTileRows, len - off), len, run_id);
+            if (j == 0) write_tile_header(rec, (int)key, tid, min(kTileRows, len - off), len, run_id, off / kTileRows);
         }
         if (tid == 0) {
             out.seg_offsets[n_seg] = n_active;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
             out.counts[5] = out.counts[6] = out.counts[7] = 0;
         }
         for (int t = n_tiles + tid; t < out.tile_bound; t += kMT)
-            write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0);
+            write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0, 0);
         return;
     }
 
@@ -313,7 +313,8 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
                 int32_t *rec = out.tiles + (int64_t)t * kTileWords;
                 rec[kRecRowIds + j] = row;
                 if (j == 0)
-                    write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2]);
+                    write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
+                                      o / kTileRows);
             }
         }
     }
@@ -334,14 +335,15 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
             int32_t *rec = out.tiles + (int64_t)t * kTileWords;
             rec[kRecRowIds + j] = row;
             if (j == 0)
-                write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2]);
+                write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
+                                      o / kTileRows);
         }
         __syncthreads();
         if (a2 && off2 == 0) rc[k2] += len2;
         __syncthreads();
     }
     for (int t = tot.c + tid; t < out.tile_bound; t += kMT)
-        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0);
+        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0, 0);
     if (tid == 0) {
         store_relaxed(&ws.ctl[0], 0);
         store_relaxed(&ws.ctl[1], 0);
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
         const int t = tile_off[key] + q / kTileRows, j = q % kTileRows;
         int32_t *rec = out.tiles + (int64_t)t * kTileWords;
         rec[kRecRowIds + j] = tid;
-        if (j == 0) write_tile_header(rec, key, pos, min(kTileRows, len - q), len, seg_idx[key]);
+        if (j == 0) write_tile_header(rec, key, pos, min(kTileRows, len - q), len, seg_idx[key], q / kTileRows);
     }
     if (tid == 0) {
         out.seg_offsets[tot.b] = tot.a;
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
         out.counts[5] = out.counts[6] = out.counts[7] = 0;
     }
     for (int t = tot.c + tid; t < out.tile_bound; t += NT)
-        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0);
+        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0, 0);
 }
 
 static int small_threads(int n) { return n <= 64 ? 64 : (n <= 256 ? 256 : 1024); }

@@ -20,7 +20,7 @@ def expected_tiles(rows, offs, sl):
         for o in range(0, m, 16):
             k = min(16, m - o)
             p = int(offs[g]) + o
-            out.append((int(sl[g]), p, k, m, g, rows[p:p + k].tolist()))
+            out.append((int(sl[g]), p, k, m, g, o // 16, rows[p:p + k].tolist()))
     return out
 
 
@@ -46,9 +46,9 @@ def assert_meta_matches(meta, slot: np.ndarray, S: int):
     bound = B.lib().lora_meta_max_tiles(slot.size, S)
     assert len(exp) <= bound
     tiles = meta.tiles.cpu().numpy().reshape(-1, 32)
-    for t, (s, p, k, m, g, rid) in enumerate(exp):
+    for t, (s, p, k, m, g, jt, rid) in enumerate(exp):
         rec = tiles[t]
-        assert rec[:5].tolist() == [s, p, k, m, g], (t, rec[:5])
+        assert rec[:6].tolist() == [s, p, k, m, g, jt], (t, rec[:6])
         assert rec[8:8 + k].tolist() == rid
     for t in range(len(exp), bound):
         assert tiles[t][2] == 0
