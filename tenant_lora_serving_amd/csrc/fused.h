@@ -546,6 +546,28 @@ __device__ __forceinline__ void stage_xa_passes(const uint64_t *pt, int P, int n
     }
 }
 
+// wait_pieces for two tiles at once (threads p < P poll the first tile's
+// flags, threads P <= p < 2P the second's).
+__device__ __forceinline__ bool wait_pieces2(const uint64_t *f0, const uint64_t *f1, int P, uint32_t tag, int *ctl,
+                                             int *ok_lds) {
+    if (threadIdx.x == 0) *ok_lds = 1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * P; i += kFT) {
+        const uint64_t *f = i < P ? f0 + i : f1 + (i - P);
+        int spins = 0;
+        while ((uint32_t)(load_word64(f) >> 32) != tag) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kSpinLimit) {
+                atomicExch(ctl + kCtlError, 1);
+                *ok_lds = 0;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*ok_lds) != 0;
+}
+
 // What an expand unit needs to find its xa.
 struct XaSrc {
     const uint64_t *pt;  // the tile's partial blocks
@@ -900,6 +922,101 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
     }
 }
 
+// MFMA expand of two consecutive tiles of one segment (wide calls, ranks up
+// to 32): each batch's B feeds the MFMAs of both tiles, so it is read once per
+// pair.  xa of the two tiles is staged side by side in LDS and both tiles' y
+// of a batch is loaded when the batch starts (the first batch's before the
+// wait); each half-batch goes through the wave's LDS tile once per tile.
+template <int NRS, class Op>
+__device__ __forceinline__ void expand_mfma_pair(const Op &op, const Hdr &h0, const Hdr &h1, int c0, int c1,
+                                                 bool add_inputs, const XaSrc &xs0, const XaSrc &xs1, char *lds) {
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 15, kq = lane >> 4;
+    const int R = op.R;
+    const int nb = (c1 - c0 + kEB - 1) / kEB;
+    uint16_t *yr[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 4 * j + (lane >> 4);
+        const int rid0 = __shfl(h0.rec, kRecRowIds + row, kWave);
+        const int rid1 = __shfl(h1.rec, kRecRowIds + row, kWave);
+        yr[0][j] = row < h0.m ? op.yrow(rid0) : nullptr;
+        yr[1][j] = row < h1.m ? op.yrow(rid1) : nullptr;
+    }
+    float *dt = reinterpret_cast<float *>(lds + 2 * kXaBytes) + w * kTileRows * kDtStride;
+    u32x4_t bo[8][NRS];
+    uint2 yv[2][8];
+    mfma_load_b<NRS>(op, h0, c0 + 128 * w, c1, R, bo);
+    mfma_load_y(yr[0], c0 + 128 * w, c1, add_inputs, yv[0]);
+    mfma_load_y(yr[1], c0 + 128 * w, c1, add_inputs, yv[1]);
+    load_row_weights(op, h0, xs0);
+    load_row_weights(op, h1, xs1);
+    if (!wait_pieces2(xs0.flags, xs1.flags, xs0.P, xs0.tag, xs0.ctl, xs0.ok)) return;
+    stage_xa<true, Op::kRowWeights, 2 * NRS>(xs0.pt, xs0.P, op.n_rr(), xs0.xb, R, h0.m, xs0.sc, xs0.rw, xs0.tag,
+                                             xs0.ctl, lds);
+    stage_xa<true, Op::kRowWeights, 2 * NRS>(xs1.pt, xs1.P, op.n_rr(), xs1.xb, R, h1.m, xs1.sc, xs1.rw, xs1.tag,
+                                             xs1.ctl, lds + kXaBytes);
+    __syncthreads();
+    u32x4_t hv[2][NRS], lv[2][NRS];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const uint16_t *xl = reinterpret_cast<const uint16_t *>(lds + rt * kXaBytes) + col * 2 * R;
+#pragma unroll
+        for (int s = 0; s < NRS; ++s) {
+            const int rk = 32 * s + 8 * kq;
+            hv[rt][s] = rk < R ? lds16(xl + rk) : zero4();
+            lv[rt][s] = rk < R ? lds16(xl + R + rk) : zero4();
+        }
+    }
+    for (int b = 0; b < nb; ++b) {
+        const int cw0 = c0 + kEB * b + 128 * w;
+        if (b > 0) {
+            mfma_load_y(yr[0], cw0, c1, add_inputs, yv[0]);
+            mfma_load_y(yr[1], cw0, c1, add_inputs, yv[1]);
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4_t d[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    d[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < NRS; ++s) {
+                        d[i] = mfma_16x16x32(bo[4 * hf + i][s], hv[rt][s], d[i]);
+                        d[i] = mfma_16x16x32(bo[4 * hf + i][s], lv[rt][s], d[i]);
+                    }
+                }
+                if (hf == 1 && rt == 1 && b + 1 < nb) mfma_load_b<NRS>(op, h0, cw0 + kEB, c1, R, bo);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<f32x4_t *>(dt + col * kDtStride + 16 * i + 4 * kq) = d[i];
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4_t o = *reinterpret_cast<const f32x4_t *>(dt + (4 * j + (lane >> 4)) * kDtStride +
+                                                                        4 * (lane & 15));
+                    const int cy = cw0 + 64 * hf + 4 * (lane & 15);
+                    if (yr[rt][j] && cy < c1) {
+                        float v[4] = {o[0], o[1], o[2], o[3]};
+                        if (add_inputs) {
+                            const uint2 yy = yv[rt][4 * hf + j];
+                            v[0] += bf_lo(yy.x);
+                            v[1] += bf_hi(yy.x);
+                            v[2] += bf_lo(yy.y);
+                            v[3] += bf_hi(yy.y);
+                        }
+                        *reinterpret_cast<uint2 *>(yr[rt][j] + cy) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+    }
+}
+
 // Expand chunk cc -> output window l and columns [c0, c1) (chunks of EC
 // columns, window by window); slice offsets are read at constant indices.
 template <class Op>
@@ -979,10 +1096,11 @@ __global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kern
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
     constexpr int kLdsShrink = (WM != 0 ? 2 : 1) * kTileRows * kXS * 2;  // wide modes stage tile pairs
     constexpr int kLdsStage = WM == 1 ? 4 * kBStage * 2 : 0, kLdsTile = 4 * kTileRows * kDtStride * 4;
-    constexpr int kLdsExpand = kXaBytes + (kLdsStage > kLdsTile ? kLdsStage : kLdsTile);
+    constexpr int kLdsExpand =  // wide modes at rank <= 32 stage the xa of tile pairs
+        (WM != 0 && NRS == 1 ? 2 : 1) * kXaBytes + (kLdsStage > kLdsTile ? kLdsStage : kLdsTile);
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     __shared__ int ok;
-    __shared__ float rw[Op::kRowWeights ? kTileRows : 1];
+    __shared__ float rw[Op::kRowWeights ? 2 * kTileRows : 1];
     const int P = fa.P, C = fa.C;
     const int n_rr = op.n_rr();
     const Unit un = unit_of(blockIdx.x, fa.tile_bound, P, C);
@@ -1056,24 +1174,46 @@ __global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kern
         if (h.m == 0) return;
         int l, c0, c1;
         chunk_of(op, cc, fa.EC, l, c0, c1);
-        const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P, op.xblk(l),
-                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw};
-        if (h.mseg >= fa.mfma_min)
-            expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
-        else
-            expand_valu<WM, NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         // the last consumer of a tile counts the tile as finished; the last
         // finished tile of the call advances the generation (two levels, so
         // no single address takes one atomic per consumer)
-        if (threadIdx.x == 0) {
-            int *tile_done = reinterpret_cast<int *>(fa.flags + (int64_t)t * kFlagWords + kFlagWords - 1);
+        auto finish = [&](int tt) {
+            int *tile_done = reinterpret_cast<int *>(fa.flags + (int64_t)tt * kFlagWords + kFlagWords - 1);
             if (atomic_add_relaxed(tile_done, 1) == C - 1) {
                 if (atomic_add_relaxed(fa.ctl + kCtlDone, 1) == n_tiles - 1) {
                     store_relaxed(fa.ctl + kCtlDone, 0);
                     store_relaxed(fa.ctl + kCtlGen, (int)tag);
                 }
             }
+        };
+        // wide calls: MFMA segments of rank <= 32 are expanded two tiles at a
+        // time by the units of the pair's first tile, which count both tiles
+        // (at rank 64 the second tile's registers would spill)
+        if (WM != 0 && NRS == 1 && h.mseg >= fa.mfma_min) {
+            const int jt = __builtin_amdgcn_readlane(h.rec, kRecSegTile);
+            if (jt & 1) return;
+            if (h.mseg > kTileRows * (jt + 1)) {
+                const Hdr h1 = load_hdr(fa.tiles, t + 1);
+                const float sc = op.scale_of(h.slot);
+                const XaSrc xs0{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P,
+                                op.xblk(l), true, sc, tag, fa.ctl, &ok, rw};
+                const XaSrc xs1{fa.part + (int64_t)(t + 1) * P * n_rr * 16, fa.flags + (int64_t)(t + 1) * kFlagWords,
+                                P, op.xblk(l), true, sc, tag, fa.ctl, &ok, rw + kTileRows};
+                expand_mfma_pair<NRS>(op, h, h1, c0, c1, fa.add_inputs != 0, xs0, xs1, lds);
+                if (threadIdx.x == 0) {
+                    finish(t);
+                    finish(t + 1);
+                }
+                return;
+            }
         }
+        const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P, op.xblk(l),
+                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw};
+        if (h.mseg >= fa.mfma_min)
+            expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+        else
+            expand_valu<WM, NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+        if (threadIdx.x == 0) finish(t);
         return;
     }
     // zero rows of pairs that get no delta (MoE only)
