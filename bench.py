@@ -21,6 +21,14 @@ oracle is timed on the same batch on the host cores (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --calibrate-copy   # a plain 512 MiB device copy, for counter scaling
+    python bench.py --workload prefill|no_reuse|moe|moe_shared|w2|w2_reuse [--steps K]
+
+The other workloads (prefill SGMV, one adapter per row, MoE gemm1 regular and
+shared-A, MoE w2 with and without gemm1's routing) print a secondary line of
+the same form for profiling: K calls back to back on the launch stream,
+bracketed by HIP events, inputs rotating over copies worth > 1 GiB where they
+are smaller; no graph, no CPU baseline, traffic null (counters are recorded
+beside the kernel traces instead).
 
 HBM traffic of the fused kernel (roofline.traffic) comes from rocprofv3
 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/fused_decode_traffic.txt,
@@ -107,6 +115,130 @@ def cpu_baseline(case, bytes_per_step: int, min_s: float, max_s: float) -> dict:
             "sample": f"the full {case.n}-row decode batch, fp64 fused delta, {passes} passes in {el:.1f} s"}
 
 
+def moe_bytes(topk_ids, lora_ids, L, E, a_elems, b_elems, x_row, out_row, out_all_pairs):
+    """Activations of adapted tokens or pairs, each touched (adapter, expert)
+    pair's weights once, and the output rows (every pair for gemm1, which
+    writes zero rows; read and written for the routed pairs of w2)."""
+    import numpy as np
+    T, top_k = topk_ids.shape
+    lo = np.repeat(lora_ids, top_k)
+    ex = topk_ids.reshape(-1)
+    valid = (lo >= 0) & (lo < L) & (ex >= 0) & (ex < E)
+    keys = np.unique(lo[valid] * E + ex[valid])
+    w = len(keys) * (a_elems + b_elems) * 2
+    if out_all_pairs:  # gemm1: x per adapted token, out for every pair
+        t_act = int(((lora_ids >= 0) & (lora_ids < L)).sum())
+        return t_act * x_row + w + T * top_k * out_row
+    return int(valid.sum()) * (x_row + out_row) + w
+
+
+def secondary(args):
+    """One of the non-headline workloads, timed as K back-to-back calls."""
+    import numpy as np
+    import torch
+
+    from tenant_lora_serving_amd import inputs as I
+    from tenant_lora_serving_amd import lora as B
+
+    torch.cuda.set_device(0)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def rotate(footprint):
+        return args.copies or max(1, math.ceil((1 << 30) / footprint)) if footprint < (1 << 29) else 1
+
+    w = args.workload
+    if w in ("prefill", "no_reuse"):
+        case = I.prefill_sgmv() if w == "prefill" else I.no_reuse()
+        nbytes = algorithmic_bytes(case)
+        rows = case.n
+        copies = rotate(case.a_pool.nbytes + case.b_pool.nbytes + case.x.nbytes + case.y.nbytes)
+        meta = B.lora_meta_build(torch.from_numpy(case.slot).cuda(), case.num_slots)
+        ws = B.fused_workspace(case.n, case.num_slots, case.num_slices, case.max_rank, case.k_in)
+        sc = torch.from_numpy(case.scale).cuda()
+        sets = [dict(x=d16(case.x), a=d16(case.a_pool), b=d16(case.b_pool), y=d16(case.y)) for _ in range(copies)]
+        call = lambda s: B.lora_delta_fused(s["x"], s["a"], s["b"], sc, case.slice_sizes, meta, s["y"], ws=ws)
+        kernel = "fused_kernel (shrink + expand)"
+        desc = {"workload": case.name, "rows": case.n, "k_in": case.k_in, "slices": list(case.slice_sizes),
+                "num_slots": case.num_slots, "max_rank": case.max_rank,
+                "note": "metadata built once, outside the timed calls"}
+    elif w in ("moe", "moe_shared"):
+        c = I.moe_gemm1()
+        E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
+        if w == "moe_shared":
+            mats = [d16(c.a_shared), d16(c.b_fused)]
+            ta = torch.tensor([mats[0].data_ptr() + e * L * R * H * 2 for e in range(E)], dtype=torch.int64)
+            tb = torch.tensor([mats[1].data_ptr() + e * L * 2 * I_ * R * 2 for e in range(E)], dtype=torch.int64)
+            sb, a_el, b_el = 2 * I_ * R, R * H, 2 * I_ * R
+        else:
+            mats = [d16(m) for m in (c.a_gate, c.a_up, c.b_gate, c.b_up)]
+            ta = torch.tensor([[mats[i].data_ptr() + e * L * R * H * 2 for e in range(E)] for i in (0, 1)],
+                              dtype=torch.int64)
+            tb = torch.tensor([[mats[i].data_ptr() + e * L * I_ * R * 2 for e in range(E)] for i in (2, 3)],
+                              dtype=torch.int64)
+            sb, a_el, b_el = I_ * R, 2 * R * H, 2 * I_ * R
+        ta, tb = ta.cuda(), tb.cuda()
+        nbytes = moe_bytes(c.topk_ids, c.lora_ids, L, E, a_el, b_el, H * 2, 2 * I_ * 2, True)
+        rows, copies = c.T, 1
+        x, tk, lo = d16(c.x), torch.from_numpy(c.topk_ids).cuda(), torch.from_numpy(c.lora_ids).cuda()
+        ws = B.moe_workspace(c.T, c.top_k, E, L, R, H)
+        out = torch.empty((c.T, c.top_k, 2 * I_), dtype=torch.bfloat16, device="cuda")
+        sets = [None]
+        call = lambda s: B.moe_lora_gemm1_delta(x, ta, R * H, tb, sb, tk, lo, R, I_, num_loras=L,
+                                                scale=c.scale, out=out, ws=ws)
+        kernel = "meta_kernel (pairs) + fused_kernel"
+        desc = {"workload": c.name + (" shared-A" if w == "moe_shared" else " regular"), "tokens": c.T,
+                "pairs": c.T * c.top_k, "note": "one call builds the pair metadata and applies the delta"}
+    elif w in ("w2", "w2_reuse"):
+        c = I.moe_w2()
+        E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
+        mats = [d16(c.a_down), d16(c.b_down)]
+        ta = torch.tensor([mats[0].data_ptr() + e * L * R * I_ * 2 for e in range(E)], dtype=torch.int64).cuda()
+        tb = torch.tensor([mats[1].data_ptr() + e * L * H * R * 2 for e in range(E)], dtype=torch.int64).cuda()
+        nbytes = moe_bytes(c.topk_ids, c.lora_ids, L, E, R * I_, H * R, I_ * 2, H * 4, False)
+        rows, copies = c.T, 1
+        x2, y = d16(c.x2), d16(c.y)
+        tk, lo = torch.from_numpy(c.topk_ids).cuda(), torch.from_numpy(c.lora_ids).cuda()
+        wt = torch.from_numpy(c.topk_weights).cuda()
+        ws = B.moe_w2_workspace(c.T, c.top_k, E, L, R, I_)
+        reuse = w == "w2_reuse"
+        if reuse:  # the routing of an earlier call on this workspace stands in for gemm1's
+            B.moe_lora_w2_delta(x2, ta, R * I_, tb, H * R, tk, lo, R, y, num_loras=L, topk_weights=wt, ws=ws)
+        sets = [None]
+        call = lambda s: B.moe_lora_w2_delta(x2, ta, R * I_, tb, H * R, tk, lo, R, y, num_loras=L,
+                                             topk_weights=wt, scale=c.scale, ws=ws, reuse_routing=reuse)
+        kernel = "fused_kernel" if reuse else "meta_kernel (pairs) + fused_kernel"
+        desc = {"workload": c.name + (" reusing gemm1's routing" if reuse else ""), "tokens": c.T,
+                "pairs": c.T * c.top_k}
+    else:
+        raise SystemExit(f"unknown workload {w!r}")
+
+    for i in range(args.warmup):
+        call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        call(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    desc.update({"bytes_per_call": int(nbytes), "input_copies": copies, "mfma_min_rows": B.mfma_min_rows(),
+                 "kernel_sources": kernel_source_hash()})
+    print(json.dumps({
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded)", "secondary": True,
+        "config": desc, "tokens_per_s": round(rows / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kernel,
+                     "kernel_us": round(ms * 1e3, 3)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +248,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "no_reuse", "moe", "moe_shared", "w2", "w2_reuse"])
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -124,6 +258,9 @@ def main():
         print("bench.py measures one GPU only: this build runs the routed LoRA delta on a single "
               "MI355X (no multi-GPU path); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "decode":
+        secondary(args)
+        return
 
     import numpy as np
     import torch
