@@ -660,6 +660,44 @@ __device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, in
     }
 }
 
+// valu_rows4 for one-batch units at rank 16: the lane's two B rows arrive
+// converted to fp32 (once per unit rather than once per block of rows) and
+// the block's 16 xa reads (uniform-address LDS reads of 4 ranks of one row)
+// are all issued before its FMAs.  The FMAs are those of valu_rows4, in the
+// same order, so the two give the same bits.
+template <int JB, class Op>
+__device__ __forceinline__ void valu_rows4_r16(const Op &op, const Hdr &h, int m, int c, bool cok, bool add_inputs,
+                                               const float (&b0)[16], const float (&b1)[16],
+                                               const uint32_t (&yv)[kTileRows], const float *xf) {
+    float o0[4] = {0.f, 0.f, 0.f, 0.f}, o1[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t xa[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xa[q][j] = *reinterpret_cast<const f32x4_t *>(xf + min(JB + j, m - 1) * 16 + 4 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o0[j] = __builtin_fmaf(xa[q][j][e], b0[4 * q + e], o0[j]);
+                o1[j] = __builtin_fmaf(xa[q][j][e], b1[4 * q + e], o1[j]);
+            }
+    if (!cok) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (JB + j < m) {
+            float v0 = o0[j], v1 = o1[j];
+            if (add_inputs) {
+                v0 += bf_lo(yv[JB + j]);
+                v1 += bf_hi(yv[JB + j]);
+            }
+            *reinterpret_cast<uint32_t *>(op.yrow(hdr_row(h, JB + j)) + c) = pack_bf16x2(v0, v1);
+        }
+    }
+}
+
 // Vector-ALU expand of columns [c0, c1) in batches of kEB: in a batch, lane
 // owns columns c, c+1 (c = batch start + 128w + 2 lane).  The first batch's B
 // and y are loaded before the wait; each later batch's are loaded while the
@@ -776,6 +814,25 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
             else
                 valu_load_b(op, h, c + kEB, c1, R, bp_n, bq_n);
             valu_load_y(op, h, c + kEB, c1, add_inputs, yv_n);
+        }
+        if constexpr (!WIDE) {
+            if (R == 16) {
+                float b0[16], b1[16];
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        b0[8 * q + 2 * e] = bf_lo(bq[0][q][e]);
+                        b0[8 * q + 2 * e + 1] = bf_hi(bq[0][q][e]);
+                        b1[8 * q + 2 * e] = bf_lo(bq[1][q][e]);
+                        b1[8 * q + 2 * e + 1] = bf_hi(bq[1][q][e]);
+                    }
+                if (m > 0) valu_rows4_r16<0>(op, h, m, c, cok, add_inputs, b0, b1, yv, xf);
+                if (m > 4) valu_rows4_r16<4>(op, h, m, c, cok, add_inputs, b0, b1, yv, xf);
+                if (m > 8) valu_rows4_r16<8>(op, h, m, c, cok, add_inputs, b0, b1, yv, xf);
+                if (m > 12) valu_rows4_r16<12>(op, h, m, c, cok, add_inputs, b0, b1, yv, xf);
+                continue;  // one batch
+            }
         }
         // rows in blocks of 4, no per-row branch inside a block
         if (m > 0) valu_rows4<0>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
@@ -1089,10 +1146,10 @@ struct FusedArgs {
     int mfma_min, add_inputs;
 };
 
-// Mode 2 (calls whose tiles are mostly on the MFMA path) asks for three waves
-// per SIMD: its registers fit without spills up to rank 64.
+// Modes 0 and 2 ask for three waves per SIMD: their registers fit without
+// spills up to rank 64 (mode 1 holds a second batch's B and y and gets two).
 template <int RPL, int NRS, int WM, class Op>
-__global__ __launch_bounds__(kFT, (WM == 2 && NRS <= 2) ? 3 : 1) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
+__global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
     constexpr int kLdsShrink = (WM != 0 ? 2 : 1) * kTileRows * kXS * 2;  // wide modes stage tile pairs
     constexpr int kLdsStage = WM == 1 ? 4 * kBStage * 2 : 0, kLdsTile = 4 * kTileRows * kDtStride * 4;
