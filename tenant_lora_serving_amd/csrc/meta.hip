@@ -14,10 +14,14 @@
 //     Inactive and invalid rows get the key S and sort to the end.
 //  2. Runs of one slot in the sorted chunk are found with a block scan.
 //  3. One chunk: the workgroup writes every output directly.
-//     Several chunks: each writes its sorted chunk to the workspace, then the
-//     last workgroup to finish (atomic ticket, release/acquire at agent
-//     scope) counts rows per slot in LDS, scans the counts, and scatters all
-//     chunks in order, so rows keep ascending order within a slot.
+//     Several chunks: each writes its sorted chunk to the workspace.  When a
+//     [chunk][slot] table of run lengths fits LDS, a second launch of one
+//     workgroup per chunk follows: each builds the table from the workspace,
+//     scans it (rows of a slot in earlier chunks come first, so rows keep
+//     ascending order within a slot) and places its own chunk's rows.
+//     Otherwise the last workgroup to finish the first launch (atomic ticket,
+//     release/acquire at agent scope) scans the per-slot counts and scatters
+//     every chunk in order.
 // No step waits on another workgroup, so nothing can hang.
 #include "common.h"
 #include "kernels.h"
@@ -126,9 +130,162 @@ __device__ __forceinline__ void write_tile_header(int32_t *rec, int slot, int po
     rec[7] = 0;
 }
 
+// Assembly of a multi-chunk build from the chunks' sorted entries in the
+// workspace: rows per slot (and per chunk), a scan over slots, then the
+// scatter of every chunk (only < 0) or of chunk `only` alone, which needs
+// the [chunk][slot] table.  Workgroup `only == 0` (or the single assembler)
+// writes the segment arrays and the counts.
+__device__ void meta_assemble(int S, int n_chunks, MetaOut out, MetaWs ws, MetaShared &sh, int *dyn, int only) {
+    const int tid = threadIdx.x;
+    int *start = dyn, *segidx = dyn + S, *tileoff = dyn + 2 * S, *rc = dyn + 3 * S;
+    // With a [chunk][slot] table in LDS, every chunk's rows are placed at once:
+    // cb[c][s] = rows of slot s in chunks before c.  Otherwise the chunks are
+    // scattered one after another, rc[s] counting the rows already placed.
+    const bool table = meta_table_fits(n_chunks, S);
+    const bool writer = only < 0 || only == 0;  // writes the per-segment outputs and counts
+    int *cb = dyn + 4 * S;
+    if (table) {
+        for (int i = tid; i < n_chunks * S; i += kMT) cb[i] = 0;
+    }
+    for (int s = tid; s < S; s += kMT) rc[s] = 0;
+    __syncthreads();
+    // rows per slot (and per chunk): each run's first entry carries its length;
+    // the loads of kAsmBatch chunks are issued before any is used
+    for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
+        uint32_t kb[kAsmBatch];
+        int ob[kAsmBatch];
+#pragma unroll
+        for (int u = 0; u < kAsmBatch; ++u) {
+            const int64_t idx = (int64_t)(c0 + u) * kMT + tid;
+            kb[u] = c0 + u < n_chunks ? (uint32_t)ws.keys[idx] : (uint32_t)S;
+            ob[u] = c0 + u < n_chunks ? ws.offlen[idx] : 1;
+        }
+#pragma unroll
+        for (int u = 0; u < kAsmBatch; ++u) {
+            if (kb[u] < (uint32_t)S && (ob[u] & 0xffff) == 0) {
+                if (table)
+                    cb[(c0 + u) * S + kb[u]] = ob[u] >> 16;
+                else
+                    atomicAdd(&rc[kb[u]], ob[u] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    if (table) {
+        for (int s2 = tid; s2 < S; s2 += kMT) {
+            int acc = 0;
+            for (int cc = 0; cc < n_chunks; ++cc) {
+                const int v = cb[cc * S + s2];
+                cb[cc * S + s2] = acc;
+                acc += v;
+            }
+            rc[s2] = acc;
+        }
+        __syncthreads();
+    }
+    // scan {rows, segments, tiles} over slots, each thread a contiguous block
+    const int per = (S + kMT - 1) / kMT;
+    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+    Int3 loc = {0, 0, 0};
+    int lng = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int v = rc[s];
+        loc = loc + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
+        lng += v >= kTileRows;
+    }
+    Int3 tot;
+    Int3 run = block_excl_scan3<kMT>(loc, sh.scan3, tot);
+    int n_long;
+    block_excl_scan<kMT>(lng, sh.scan, n_long);
+    for (int s = s0; s < s1; ++s) {
+        const int v = rc[s];
+        start[s] = run.a;
+        segidx[s] = run.b;
+        tileoff[s] = run.c;
+        if (v > 0 && writer) {
+            out.seg_offsets[run.b] = run.a;
+            out.seg_slot[run.b] = s;
+        }
+        run = run + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
+        rc[s] = 0;
+    }
+    __syncthreads();
+    if (tid == 0 && writer) {
+        out.seg_offsets[tot.b] = tot.a;
+        out.counts[0] = tot.a;
+        out.counts[1] = tot.b;
+        out.counts[2] = __hip_atomic_load(&ws.ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        out.counts[3] = n_long;
+        out.counts[4] = tot.c;
+        out.counts[5] = out.counts[6] = out.counts[7] = 0;
+    }
+    if (table) {
+        // every chunk, or only chunk `only`
+        const int cbeg = only < 0 ? 0 : only, cend = only < 0 ? n_chunks : only + 1;
+        for (int c0 = cbeg; c0 < cend; c0 += kAsmBatch) {
+            uint32_t kb[kAsmBatch];
+            int ob[kAsmBatch], rb[kAsmBatch];
+#pragma unroll
+            for (int u = 0; u < kAsmBatch; ++u) {
+                const int64_t idx = (int64_t)(c0 + u) * kMT + tid;
+                const bool in = c0 + u < cend;
+                kb[u] = in ? (uint32_t)ws.keys[idx] : (uint32_t)S;
+                ob[u] = in ? ws.offlen[idx] : 0;
+                rb[u] = in ? ws.rows[idx] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kAsmBatch; ++u) {
+                const int cc = c0 + u;
+                const uint32_t k2 = kb[u];
+                if (k2 >= (uint32_t)S) continue;
+                const int ol = ob[u];
+                const int row = rb[u];
+                const int o = cb[cc * S + k2] + (ol & 0xffff);
+                const int dest = start[k2] + o;
+                const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
+                out.sorted_rows[dest] = row;
+                const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
+                int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+                rec[kRecRowIds + j] = row;
+                if (j == 0)
+                    write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
+                                      o / kTileRows);
+            }
+        }
+    }
+    // scatter the chunks in order; rc[s] counts the rows of slot s already placed
+    for (int cc = 0; !table && cc < n_chunks; ++cc) {
+        const int64_t idx = (int64_t)cc * kMT + tid;
+        const uint32_t k2 = (uint32_t)ws.keys[idx];
+        const int ol = ws.offlen[idx];
+        const int off2 = ol & 0xffff, len2 = ol >> 16;
+        const bool a2 = k2 < (uint32_t)S;
+        if (a2) {
+            const int row = ws.rows[idx];
+            const int o = rc[k2] + off2;
+            const int dest = start[k2] + o;
+            const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
+            out.sorted_rows[dest] = row;
+            const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
+            int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+            rec[kRecRowIds + j] = row;
+            if (j == 0)
+                write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
+                                      o / kTileRows);
+        }
+        __syncthreads();
+        if (a2 && off2 == 0) rc[k2] += len2;
+        __syncthreads();
+    }
+    // empty records past the last tile, shared by the assembling workgroups
+    const int g = only < 0 ? 0 : only, ng = only < 0 ? 1 : n_chunks;
+    for (int t = tot.c + g * kMT + tid; t < out.tile_bound; t += ng * kMT)
+        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0, 0);
+}
+
 template <class Src>
 __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_chunks, MetaOut out,
-                                                   MetaWs ws) {
+                                                   MetaWs ws, int split) {
     __shared__ MetaShared sh;
     extern __shared__ int dyn[];
     const int tid = threadIdx.x;
@@ -198,6 +355,7 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
         ws.offlen[idx] = off | (len << 16);
     }
     if (tid == 0 && n_inv_chunk) atomicAdd(&ws.ctl[1], n_inv_chunk);
+    if (split) return;  // meta_assemble_kernel follows in the same stream
     __threadfence();
     __syncthreads();
     if (tid == 0) sh.flag_last = atomic_add_acqrel(&ws.ctl[0], 1) == n_chunks - 1;
@@ -205,149 +363,20 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
     if (!sh.flag_last) return;
     __threadfence();
 
-    int *start = dyn, *segidx = dyn + S, *tileoff = dyn + 2 * S, *rc = dyn + 3 * S;
-    // With a [chunk][slot] table in LDS, every chunk's rows are placed at once:
-    // cb[c][s] = rows of slot s in chunks before c.  Otherwise the chunks are
-    // scattered one after another, rc[s] counting the rows already placed.
-    const bool table = meta_table_fits(n_chunks, S);
-    int *cb = dyn + 4 * S;
-    if (table) {
-        for (int i = tid; i < n_chunks * S; i += kMT) cb[i] = 0;
-    }
-    for (int s = tid; s < S; s += kMT) rc[s] = 0;
-    __syncthreads();
-    // rows per slot (and per chunk): each run's first entry carries its length;
-    // the loads of kAsmBatch chunks are issued before any is used
-    for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
-        uint32_t kb[kAsmBatch];
-        int ob[kAsmBatch];
-#pragma unroll
-        for (int u = 0; u < kAsmBatch; ++u) {
-            const int64_t idx = (int64_t)(c0 + u) * kMT + tid;
-            kb[u] = c0 + u < n_chunks ? (uint32_t)ws.keys[idx] : (uint32_t)S;
-            ob[u] = c0 + u < n_chunks ? ws.offlen[idx] : 1;
-        }
-#pragma unroll
-        for (int u = 0; u < kAsmBatch; ++u) {
-            if (kb[u] < (uint32_t)S && (ob[u] & 0xffff) == 0) {
-                if (table)
-                    cb[(c0 + u) * S + kb[u]] = ob[u] >> 16;
-                else
-                    atomicAdd(&rc[kb[u]], ob[u] >> 16);
-            }
-        }
-    }
-    __syncthreads();
-    if (table) {
-        for (int s2 = tid; s2 < S; s2 += kMT) {
-            int acc = 0;
-            for (int cc = 0; cc < n_chunks; ++cc) {
-                const int v = cb[cc * S + s2];
-                cb[cc * S + s2] = acc;
-                acc += v;
-            }
-            rc[s2] = acc;
-        }
-        __syncthreads();
-    }
-    // scan {rows, segments, tiles} over slots, each thread a contiguous block
-    const int per = (S + kMT - 1) / kMT;
-    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
-    Int3 loc = {0, 0, 0};
-    int lng = 0;
-    for (int s = s0; s < s1; ++s) {
-        const int v = rc[s];
-        loc = loc + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
-        lng += v >= kTileRows;
-    }
-    Int3 tot;
-    Int3 run = block_excl_scan3<kMT>(loc, sh.scan3, tot);
-    int n_long;
-    block_excl_scan<kMT>(lng, sh.scan, n_long);
-    for (int s = s0; s < s1; ++s) {
-        const int v = rc[s];
-        start[s] = run.a;
-        segidx[s] = run.b;
-        tileoff[s] = run.c;
-        if (v > 0) {
-            out.seg_offsets[run.b] = run.a;
-            out.seg_slot[run.b] = s;
-        }
-        run = run + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
-        rc[s] = 0;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        out.seg_offsets[tot.b] = tot.a;
-        out.counts[0] = tot.a;
-        out.counts[1] = tot.b;
-        out.counts[2] = __hip_atomic_load(&ws.ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        out.counts[3] = n_long;
-        out.counts[4] = tot.c;
-        out.counts[5] = out.counts[6] = out.counts[7] = 0;
-    }
-    if (table) {
-        for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
-            uint32_t kb[kAsmBatch];
-            int ob[kAsmBatch], rb[kAsmBatch];
-#pragma unroll
-            for (int u = 0; u < kAsmBatch; ++u) {
-                const int64_t idx = (int64_t)(c0 + u) * kMT + tid;
-                const bool in = c0 + u < n_chunks;
-                kb[u] = in ? (uint32_t)ws.keys[idx] : (uint32_t)S;
-                ob[u] = in ? ws.offlen[idx] : 0;
-                rb[u] = in ? ws.rows[idx] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < kAsmBatch; ++u) {
-                const int cc = c0 + u;
-                const uint32_t k2 = kb[u];
-                if (k2 >= (uint32_t)S) continue;
-                const int ol = ob[u];
-                const int row = rb[u];
-                const int o = cb[cc * S + k2] + (ol & 0xffff);
-                const int dest = start[k2] + o;
-                const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
-                out.sorted_rows[dest] = row;
-                const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
-                int32_t *rec = out.tiles + (int64_t)t * kTileWords;
-                rec[kRecRowIds + j] = row;
-                if (j == 0)
-                    write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
-                                      o / kTileRows);
-            }
-        }
-    }
-    // scatter the chunks in order; rc[s] counts the rows of slot s already placed
-    for (int cc = 0; !table && cc < n_chunks; ++cc) {
-        const int64_t idx = (int64_t)cc * kMT + tid;
-        const uint32_t k2 = (uint32_t)ws.keys[idx];
-        const int ol = ws.offlen[idx];
-        const int off2 = ol & 0xffff, len2 = ol >> 16;
-        const bool a2 = k2 < (uint32_t)S;
-        if (a2) {
-            const int row = ws.rows[idx];
-            const int o = rc[k2] + off2;
-            const int dest = start[k2] + o;
-            const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
-            out.sorted_rows[dest] = row;
-            const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
-            int32_t *rec = out.tiles + (int64_t)t * kTileWords;
-            rec[kRecRowIds + j] = row;
-            if (j == 0)
-                write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
-                                      o / kTileRows);
-        }
-        __syncthreads();
-        if (a2 && off2 == 0) rc[k2] += len2;
-        __syncthreads();
-    }
-    for (int t = tot.c + tid; t < out.tile_bound; t += kMT)
-        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0, 0);
+    meta_assemble(S, n_chunks, out, ws, sh, dyn, -1);
     if (tid == 0) {
         store_relaxed(&ws.ctl[0], 0);
         store_relaxed(&ws.ctl[1], 0);
     }
+}
+
+// Second launch of a split build: workgroup c places chunk c.  The invalid
+// count is read (and cleared for the next call) by workgroup 0 alone.
+__global__ __launch_bounds__(kMT) void meta_assemble_kernel(int S, int n_chunks, MetaOut out, MetaWs ws) {
+    __shared__ MetaShared sh;
+    extern __shared__ int dyn[];
+    meta_assemble(S, n_chunks, out, ws, sh, dyn, blockIdx.x);
+    if (blockIdx.x == 0 && threadIdx.x == 0) store_relaxed(&ws.ctl[1], 0);
 }
 
 // ------------------------------------------------------------ small batches
@@ -547,7 +576,14 @@ static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hip
     if (dyn > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_kernel<Src>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), dyn, st, src, n, S, chunks, out, ws);
+    const int split = chunks > 1 && meta_table_fits(chunks, S);
+    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), split ? 0 : dyn, st, src, n, S, chunks, out, ws,
+                       split);
+    if (!split) return hipGetLastError();
+    if (dyn > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_assemble_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    hipLaunchKernelGGL(meta_assemble_kernel, dim3(chunks), dim3(kMT), dyn, st, S, chunks, out, ws);
     return hipGetLastError();
 }
 
