@@ -16,7 +16,9 @@ torch.cuda.synchronize().  value = algorithmic bytes of the K steps / wall
 time (GB/s).  The fused kernel's own average duration is measured with two
 HIP events on the launch stream bracketing a second region of K back-to-back
 eager launches (elapsed / K); it gives the roofline fraction against 8 TB/s.
-The metadata kernel is timed the same way.  The fp64 CPU
+The metadata kernel is timed the same way, and so is a plain device copy
+moving the same number of bytes (plain_copy_same_bytes: what the memory
+system gives a transfer of this size, next to the kernel).  The fp64 CPU
 oracle is timed on the same batch on the host cores (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -333,6 +335,26 @@ def main():
     fused_ms = region(lambda s: B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes,
                                                    s["meta"], s["y"], ws=s["ws"]))
     meta_ms = region(lambda s: B.lora_meta_build(s["slot"], case.num_slots, s["meta"]))
+    # what a plain device copy moving the same bytes (half read, half written)
+    # takes when timed the same way, rotating over as many buffers
+    half = bytes_step // 2
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(copies)]
+    cbufs = [{"src": a_, "dst": b_} for a_, b_ in bufs]
+
+    def copy_region():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            c_ = cbufs[i % copies]
+            c_["dst"].copy_(c_["src"])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    copy_region()
+    copy_ms = copy_region()
+    del bufs, cbufs
 
     value = bytes_step * K / wall / 1e9
     fused_gbs = bytes_step / (fused_ms * 1e-3) / 1e9
@@ -362,6 +384,10 @@ def main():
                      "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "fused_kernel<3, 1, 0, DenseOp>", "kernel_us": round(fused_ms * 1e3, 3)},
         "meta_kernel_us": round(meta_ms * 1e3, 3),
+        "plain_copy_same_bytes": {"us": round(copy_ms * 1e3, 3),
+                                  "GB/s": round(2 * half / (copy_ms * 1e-3) / 1e9, 2),
+                                  "note": "device copy of half the step's bytes (read + write = the step's "
+                                          "bytes), K launches bracketed by events, buffers rotated"},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(case, bytes_step, args.cpu_seconds, 30.0)
