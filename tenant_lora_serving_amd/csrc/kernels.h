@@ -21,8 +21,10 @@ struct MetaOut {
     int tile_bound;
 };
 
-// Workspace of a multi-chunk meta build: ctl[0] ticket, ctl[1] invalid rows
-// (both zero between calls), then rows / keys / offset+length per chunk row.
+// Workspace of a multi-chunk meta build: ctl[0] the single assembler's
+// ticket (unused when the build assembles in a second launch), ctl[1] invalid
+// rows (both zero between calls), then rows / keys / offset+length per chunk
+// row.
 struct MetaWs {
     int32_t *ctl;
     int32_t *rows;
