@@ -105,3 +105,22 @@ def test_meta_reuse_buffers_and_determinism():
     rows, offs, sl, cnt = O.meta_build(slot, 40)
     assert m.sorted_rows.cpu().numpy()[:cnt[0]].tolist() == rows.tolist()
     assert m.ws[:8].view(torch.int32).cpu().tolist() == [0, 0]
+
+
+def test_meta_assembly_paths_share_a_workspace():
+    """Builds that assemble in a second launch (the [chunk][slot] table fits)
+    and builds whose last workgroup assembles alone (8192 slots), one after
+    another on one workspace: each matches the oracle and leaves the
+    workspace counters at zero for the next."""
+    shapes = [(4000, 40), (5000, 8192), (20000, 300), (3000, 8192), (4000, 40)]
+    wsb = max(int(B.lib().lora_meta_workspace_bytes(n, S)) for n, S in shapes)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    for i, (n, S) in enumerate(shapes):
+        rng = np.random.default_rng(300 + i)
+        slot = rng.integers(-2, S + 2, size=n).astype(np.int32)
+        print(f"meta shared-ws case n={n} S={S}", flush=True)
+        m = B.LoraMeta.allocate(n, S)
+        m.ws = ws
+        B.lora_meta_build(d32(slot), S, m)
+        torch.cuda.synchronize()
+        assert_meta_matches(m, slot, S)
