@@ -15,10 +15,11 @@
 //  2. Runs of one slot in the sorted chunk are found with a block scan.
 //  3. One chunk: the workgroup writes every output directly.
 //     Several chunks: each writes its sorted chunk to the workspace.  When a
-//     [chunk][slot] table of run lengths fits LDS, a second launch of one
-//     workgroup per chunk follows: each builds the table from the workspace,
-//     scans it (rows of a slot in earlier chunks come first, so rows keep
-//     ascending order within a slot) and places its own chunk's rows.
+//     [chunk][slot] table of run lengths fits LDS and there are at most 64
+//     chunks, a second launch of one workgroup per chunk follows: each builds
+//     the table from the workspace, scans it (rows of a slot in earlier
+//     chunks come first, so rows keep ascending order within a slot) and
+//     places its own chunk's rows.
 //     Otherwise the last workgroup to finish the first launch (atomic ticket,
 //     release/acquire at agent scope) scans the per-slot counts and scatters
 //     every chunk in order.
@@ -31,6 +32,7 @@ namespace tl {
 constexpr int kMT = 1024;  // threads per workgroup = rows per chunk
 constexpr int kMetaTable = 16384;  // LDS ints for the assembling workgroup's [chunk][slot] table and slot arrays
 constexpr int kAsmBatch = 8;       // chunks whose entries the assembling workgroup loads at once
+constexpr int kSplitMaxChunks = 64;  // a split build's workgroups each read every chunk's entries
 
 __host__ __device__ inline bool meta_table_fits(int n_chunks, int S) { return (long long)(4 + n_chunks) * S <= kMetaTable; }
 
@@ -576,7 +578,9 @@ static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hip
     if (dyn > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_kernel<Src>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    const int split = chunks > 1 && meta_table_fits(chunks, S);
+    // every workgroup of the second launch reads all chunks' entries (work
+    // quadratic in the chunk count), so very long batches assemble alone
+    const int split = chunks > 1 && chunks <= kSplitMaxChunks && meta_table_fits(chunks, S);
     hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), split ? 0 : dyn, st, src, n, S, chunks, out, ws,
                        split);
     if (!split) return hipGetLastError();

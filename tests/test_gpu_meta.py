@@ -112,7 +112,8 @@ def test_meta_assembly_paths_share_a_workspace():
     and builds whose last workgroup assembles alone (8192 slots), one after
     another on one workspace: each matches the oracle and leaves the
     workspace counters at zero for the next."""
-    shapes = [(4000, 40), (5000, 8192), (20000, 300), (3000, 8192), (4000, 40)]
+    # (70000, 5): 69 chunks, past the split build's limit, so its table path assembles alone
+    shapes = [(4000, 40), (5000, 8192), (20000, 300), (3000, 8192), (70000, 5), (4000, 40)]
     wsb = max(int(B.lib().lora_meta_workspace_bytes(n, S)) for n, S in shapes)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     for i, (n, S) in enumerate(shapes):
