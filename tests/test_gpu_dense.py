@@ -260,3 +260,42 @@ def test_fused_prefill_full():
     starts = np.concatenate([[0], np.cumsum(c.meta["seq_lens"])])
     rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1, rng.choice(c.n, 40, replace=False)]))
     check_y(dv, y, rows, "prefill")
+
+
+def fused_bits(c: I.DenseCase, slot, a_pool, b_pool, scale, x, y):
+    meta = B.lora_meta_build(d32(slot), c.num_slots)
+    yd = d16(y)
+    B.lora_delta_fused(d16(x), d16(a_pool), d16(b_pool), d32(scale), c.slice_sizes, meta, yd)
+    torch.cuda.synchronize()
+    return h16(yd)
+
+
+@pytest.mark.parametrize("kw", [dict(seed=2, n=300, S=4, zipf=True), dict(seed=10, n=700, S=9, R=32)],
+                         ids=["zipf-r16", "uniform-r32"])
+def test_relabelled_slots_give_the_same_bits(kw, path):
+    """Relabelling the pool (slot s becomes perm[s], its adapter and scale
+    moving with it) changes which segment comes first but no row's
+    arithmetic: the output is bitwise the same."""
+    c = small_case(**kw)
+    perm = np.random.default_rng(kw["seed"] + 50).permutation(c.num_slots)
+    act = active(c)
+    slot2 = np.where(act, perm[np.where(act, c.slot, 0)], c.slot).astype(np.int32)
+    a2, b2, s2 = (np.empty_like(v) for v in (c.a_pool, c.b_pool, c.scale))
+    a2[perm], b2[perm], s2[perm] = c.a_pool, c.b_pool, c.scale
+    print(f"relabel {kw} path={path}", flush=True)
+    ref = fused_bits(c, c.slot, c.a_pool, c.b_pool, c.scale, c.x, c.y)
+    got = fused_bits(c, slot2, a2, b2, s2, c.x, c.y)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("kw", [dict(seed=2, n=300, S=4, zipf=True), dict(seed=11, n=500, S=30, zipf=True)],
+                         ids=["long-segments", "many-slots"])
+def test_row_permutation_gives_the_same_bits(kw, path):
+    """Permuting the rows (x, y and slot together) permutes the output: each
+    row's result depends only on its own inputs and its segment's length."""
+    c = small_case(**kw)
+    p = np.random.default_rng(kw["seed"] + 60).permutation(c.n)
+    print(f"row permutation {kw} path={path}", flush=True)
+    ref = fused_bits(c, c.slot, c.a_pool, c.b_pool, c.scale, c.x, c.y)
+    got = fused_bits(c, c.slot[p].copy(), c.a_pool, c.b_pool, c.scale, c.x[p].copy(), c.y[p].copy())
+    assert np.array_equal(got, ref[p])
