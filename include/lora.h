@@ -31,8 +31,13 @@
  *    workspace's counters return to zero after every call; the fused and
  *    MoE workspaces keep a count of the calls completed on them (a control
  *    word at a library-defined offset), which tags the partial results of
- *    the next call, and stay valid for calls of any shape that fits them.  Calls that share a
- *    workspace must be ordered (same stream).
+ *    the next call, and stay valid for calls of any shape that fits them.
+ *    Calls that share a workspace must be ordered (same stream).
+ *  - Inside a fused call, units that wait for other units' results do so
+ *    with bounded polls.  Such a wait can only run out when calls sharing a
+ *    workspace overlap; the kernel then still finishes (the rows concerned
+ *    get undefined values) and sets an error word to 1, which the library
+ *    never clears: for lora_delta_fused it is the first int32 of ws.
  *
  * Layouts (metrale docs, LoraPair and LoraRoute; the slices follow vLLM's
  * add_shrink / add_expand, one A and one block of B rows per output slice):
