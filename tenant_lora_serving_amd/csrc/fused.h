@@ -1285,9 +1285,9 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
 }
 
 // ============================================================ host side
-static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-static int tile_bound_of(int n, int S) {
+inline int tile_bound_of(int n, int S) {
     if (n <= 0) return 0;
     const long long a = (n + kTileRows - 1) / kTileRows + (long long)(n < S ? n : S);
     return (int)(a < n ? a : n);
