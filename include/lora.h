@@ -95,7 +95,9 @@ enum {
  *                                     n_segments_with_at_least_16_rows,
  *                                     n_tiles, 0, 0, 0}
  *   tiles        [lora_meta_max_tiles(n,S) * LORA_TILE_WORDS]
- *       Each segment is cut into tiles of at most 16 consecutive sorted rows.
+ *       Each segment is cut into tiles of 16 consecutive sorted rows, the
+ *       last one ragged; when n <= 1024, a segment of 9..15 rows is cut into
+ *       two tiles of ceil(rows/2) and floor(rows/2) rows (run in parallel).
  *       Record t (32 int32): [0] slot, [1] first sorted position, [2] rows in
  *       the tile (0 marks an unused record), [3] rows in the whole segment,
  *       [4] segment index, [5] the tile's index within its segment,
@@ -111,7 +113,8 @@ typedef struct {
 } lora_meta_t;
 
 /* Number of tile records the tiles array must hold for n rows and S slots:
- * min(n, ceil(n/16) + min(n, S)). */
+ * with g = min(n, S), min(n, ceil(n/16) + g) when n > 1024, else
+ * min(n, ceil(n/16) + g + min(g, floor(n/9)), ceil(n/8) + g). */
 int32_t lora_meta_max_tiles(int32_t n, int32_t num_slots);
 
 /* Workspace bytes lora_meta_build needs for n rows and S slots. */

@@ -36,11 +36,7 @@ int mfma_min_rows() {
     return v;
 }
 
-int tile_bound(int n, int S) {
-    if (n <= 0) return 0;
-    const long long a = (n + LORA_TILE_ROWS - 1) / LORA_TILE_ROWS + (long long)(n < S ? n : S);
-    return (int)(a < n ? a : n);
-}
+int tile_bound(int n, int S) { return tl::tile_bound_of(n, S); }
 
 size_t meta_ws_bytes(int n, int S) {
     (void)S;

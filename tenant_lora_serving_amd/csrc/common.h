@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace tl {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -13,8 +15,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kTileRows = 16;    // rows per tile record (the MFMA M dimension)
-constexpr int kTileWords = 32;   // int32 words per tile record
 // tile record fields
 constexpr int kRecSlot = 0, kRecPos = 1, kRecRows = 2, kRecSegRows = 3, kRecSeg = 4, kRecSegTile = 5,
               kRecRowIds = 8;

@@ -1176,8 +1176,9 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
             // has nothing to do
             if (WM != 0 && h.mseg >= fa.mfma_min && n_rr <= 64) {
                 const int jt = __builtin_amdgcn_readlane(h.rec, kRecSegTile);
-                if (jt & 1) return;
-                if (h.mseg > kTileRows * (jt + 1)) {
+                // (segments under 16 rows, cut in two tiles, are never paired)
+                if ((jt & 1) && h.mseg >= kTileRows) return;
+                if (!(jt & 1) && h.mseg > kTileRows * (jt + 1)) {
                     const Hdr h1 = load_hdr(fa.tiles, t + 1);
                     uint64_t *fl0 = fa.flags + (int64_t)t * kFlagWords, *fl1 = fl0 + kFlagWords;
                     int old = 0;
@@ -1248,8 +1249,8 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
         // (at rank 64 the second tile's registers would spill)
         if (WM != 0 && NRS == 1 && h.mseg >= fa.mfma_min) {
             const int jt = __builtin_amdgcn_readlane(h.rec, kRecSegTile);
-            if (jt & 1) return;
-            if (h.mseg > kTileRows * (jt + 1)) {
+            if ((jt & 1) && h.mseg >= kTileRows) return;
+            if (!(jt & 1) && h.mseg > kTileRows * (jt + 1)) {
                 const Hdr h1 = load_hdr(fa.tiles, t + 1);
                 const float sc = op.scale_of(h.slot);
                 const XaSrc xs0{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P,
@@ -1287,11 +1288,6 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
 // ============================================================ host side
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-inline int tile_bound_of(int n, int S) {
-    if (n <= 0) return 0;
-    const long long a = (n + kTileRows - 1) / kTileRows + (long long)(n < S ? n : S);
-    return (int)(a < n ? a : n);
-}
 
 static int rpl_of(int n_rr) { return n_rr >= 64 ? 4 : (n_rr + 15) / 16; }
 static int nrs_of(int R) { return R <= 32 ? 1 : (R <= 64 ? 2 : 4); }

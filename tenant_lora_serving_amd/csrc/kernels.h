@@ -11,6 +11,37 @@ namespace tl {
 constexpr int kMaxSlices = 8;
 constexpr int kMaxRank = 128;
 constexpr int kMetaMaxSlotsMulti = 8192;  // slot limit when n spans several 1024-row chunks
+constexpr int kTileRows = 16;             // rows per tile record (the MFMA M dimension)
+constexpr int kTileWords = 32;            // int32 words per tile record
+
+// Tiles of a segment of t rows in a batch of n rows: 16-row tiles, the last
+// one ragged, except that in batches of at most 1024 rows (decode-sized) a
+// segment of 9..15 rows is cut into two tiles of ceil(t/2) and floor(t/2)
+// rows.  Such a segment takes the vector-ALU path at the default MFMA
+// threshold, whose work grows with a tile's rows, and in a small batch it is
+// on the critical path; two tiles run in parallel.  (In large batches the
+// extra tile would re-read the adapter for no gain.)  Tile pairing (two
+// 16-row tiles in one unit) applies to segments of at least 16 rows only.
+constexpr int kSplitMaxRows = 1024;
+__host__ __device__ inline bool seg_is_split(int t, int n) { return n <= kSplitMaxRows && t > 8 && t < kTileRows; }
+__host__ __device__ inline int seg_tiles(int t, int n) {
+    return seg_is_split(t, n) ? 2 : (t + kTileRows - 1) / kTileRows;
+}
+__host__ __device__ inline int seg_tile_rows(int t, int n) { return seg_is_split(t, n) ? (t + 1) / 2 : kTileRows; }
+// Upper bound of the tile count of n rows in at most S segments: a segment
+// has at most t/16 + 1 tiles, plus one when it is split (a split segment has
+// at least 9 rows), and at most t/8 + 1 tiles in any case; never more than n.
+__host__ __device__ inline int tile_bound_of(int n, int S) {
+    if (n <= 0) return 0;
+    const long long segs = n < S ? n : S;
+    long long m = (n + kTileRows - 1) / kTileRows + segs;
+    if (n <= kSplitMaxRows) {
+        const long long split = segs < n / 9 ? segs : n / 9;
+        const long long b = (n + 7) / 8 + segs;
+        m = m + split < b ? m + split : b;
+    }
+    return (int)(m < n ? m : n);
+}
 
 struct MetaOut {
     int32_t *sorted_rows;

@@ -137,7 +137,8 @@ __device__ __forceinline__ void write_tile_header(int32_t *rec, int slot, int po
 // scatter of every chunk (only < 0) or of chunk `only` alone, which needs
 // the [chunk][slot] table.  Workgroup `only == 0` (or the single assembler)
 // writes the segment arrays and the counts.
-__device__ void meta_assemble(int S, int n_chunks, MetaOut out, MetaWs ws, MetaShared &sh, int *dyn, int only) {
+__device__ void meta_assemble(int n, int S, int n_chunks, MetaOut out, MetaWs ws, MetaShared &sh, int *dyn,
+                              int only) {
     const int tid = threadIdx.x;
     int *start = dyn, *segidx = dyn + S, *tileoff = dyn + 2 * S, *rc = dyn + 3 * S;
     // With a [chunk][slot] table in LDS, every chunk's rows are placed at once:
@@ -192,7 +193,7 @@ __device__ void meta_assemble(int S, int n_chunks, MetaOut out, MetaWs ws, MetaS
     int lng = 0;
     for (int s = s0; s < s1; ++s) {
         const int v = rc[s];
-        loc = loc + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
+        loc = loc + Int3{v, v > 0, seg_tiles(v, n)};
         lng += v >= kTileRows;
     }
     Int3 tot;
@@ -208,7 +209,7 @@ __device__ void meta_assemble(int S, int n_chunks, MetaOut out, MetaWs ws, MetaS
             out.seg_offsets[run.b] = run.a;
             out.seg_slot[run.b] = s;
         }
-        run = run + Int3{v, v > 0, (v + kTileRows - 1) / kTileRows};
+        run = run + Int3{v, v > 0, seg_tiles(v, n)};
         rc[s] = 0;
     }
     __syncthreads();
@@ -246,12 +247,12 @@ __device__ void meta_assemble(int S, int n_chunks, MetaOut out, MetaWs ws, MetaS
                 const int dest = start[k2] + o;
                 const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
                 out.sorted_rows[dest] = row;
-                const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
+                const int per = seg_tile_rows(seg_rows, n);
+                const int t = tileoff[k2] + o / per, j = o % per;
                 int32_t *rec = out.tiles + (int64_t)t * kTileWords;
                 rec[kRecRowIds + j] = row;
                 if (j == 0)
-                    write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
-                                      o / kTileRows);
+                    write_tile_header(rec, (int)k2, dest, min(per, seg_rows - o), seg_rows, segidx[k2], o / per);
             }
         }
     }
@@ -268,12 +269,12 @@ __device__ void meta_assemble(int S, int n_chunks, MetaOut out, MetaWs ws, MetaS
             const int dest = start[k2] + o;
             const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
             out.sorted_rows[dest] = row;
-            const int t = tileoff[k2] + o / kTileRows, j = o % kTileRows;
+            const int per = seg_tile_rows(seg_rows, n);
+            const int t = tileoff[k2] + o / per, j = o % per;
             int32_t *rec = out.tiles + (int64_t)t * kTileWords;
             rec[kRecRowIds + j] = row;
             if (j == 0)
-                write_tile_header(rec, (int)k2, dest, min(kTileRows, seg_rows - o), seg_rows, segidx[k2],
-                                      o / kTileRows);
+                write_tile_header(rec, (int)k2, dest, min(per, seg_rows - o), seg_rows, segidx[k2], o / per);
         }
         __syncthreads();
         if (a2 && off2 == 0) rc[k2] += len2;
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
         const int n_long = __syncthreads_count(seg_lead && len >= kTileRows);
         int n_tiles;
         const int tile_x =
-            block_excl_scan<kMT>(seg_lead ? (len + kTileRows - 1) / kTileRows : 0, sh.scan, n_tiles);
+            block_excl_scan<kMT>(seg_lead ? seg_tiles(len, n) : 0, sh.scan, n_tiles);
         if (seg_lead) sh.run_tile[run_id] = tile_x;
         const int n_seg = __syncthreads_count(seg_lead);
         if (act) {
@@ -330,10 +331,11 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
                 out.seg_offsets[run_id] = tid;
                 out.seg_slot[run_id] = (int)key;
             }
-            const int t = sh.run_tile[run_id] + off / kTileRows, j = off % kTileRows;
+            const int per = seg_tile_rows(len, n);
+            const int t = sh.run_tile[run_id] + off / per, j = off % per;
             int32_t *rec = out.tiles + (int64_t)t * kTileWords;
             rec[kRecRowIds + j] = val;
-            if (j == 0) write_tile_header(rec, (int)key, tid, min(kTileRows, len - off), len, run_id, off / kTileRows);
+            if (j == 0) write_tile_header(rec, (int)key, tid, min(per, len - off), len, run_id, off / per);
         }
         if (tid == 0) {
             out.seg_offsets[n_seg] = n_active;
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
     if (!sh.flag_last) return;
     __threadfence();
 
-    meta_assemble(S, n_chunks, out, ws, sh, dyn, -1);
+    meta_assemble(n, S, n_chunks, out, ws, sh, dyn, -1);
     if (tid == 0) {
         store_relaxed(&ws.ctl[0], 0);
         store_relaxed(&ws.ctl[1], 0);
@@ -374,10 +376,10 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
 
 // Second launch of a split build: workgroup c places chunk c.  The invalid
 // count is read (and cleared for the next call) by workgroup 0 alone.
-__global__ __launch_bounds__(kMT) void meta_assemble_kernel(int S, int n_chunks, MetaOut out, MetaWs ws) {
+__global__ __launch_bounds__(kMT) void meta_assemble_kernel(int n, int S, int n_chunks, MetaOut out, MetaWs ws) {
     __shared__ MetaShared sh;
     extern __shared__ int dyn[];
-    meta_assemble(S, n_chunks, out, ws, sh, dyn, blockIdx.x);
+    meta_assemble(n, S, n_chunks, out, ws, sh, dyn, blockIdx.x);
     if (blockIdx.x == 0 && threadIdx.x == 0) store_relaxed(&ws.ctl[1], 0);
 }
 
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
 #pragma unroll
                 for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
             }
-            const Int3 v = {t, t > 0, (t + kTileRows - 1) / kTileRows};
+            const Int3 v = {t, t > 0, seg_tiles(t, n)};
             const Int3 inc = wave_incl_scan3(v);
             const Int3 run = {inc.a - v.a, inc.b - v.b, inc.c - v.c};
             if (k < S) {
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
             int t = 0;
 #pragma unroll
             for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
-            loc = loc + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+            loc = loc + Int3{t, t > 0, seg_tiles(t, n)};
             if (t >= kTileRows) atomicAdd(&n_long, 1);
         }
         Int3 run = block_excl_scan3<NT>(loc, scan3, tot);
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
                 out.seg_offsets[run.b] = run.a;
                 out.seg_slot[run.b] = k;
             }
-            run = run + Int3{t, t > 0, (t + kTileRows - 1) / kTileRows};
+            run = run + Int3{t, t > 0, seg_tiles(t, n)};
         }
         __syncthreads();
     }
@@ -517,10 +519,11 @@ __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, M
         const int len = (key + 1 < S ? start[key + 1] : tot.a) - st;
         const int q = pos - st;
         out.sorted_rows[pos] = tid;
-        const int t = tile_off[key] + q / kTileRows, j = q % kTileRows;
+        const int per = seg_tile_rows(len, n);
+        const int t = tile_off[key] + q / per, j = q % per;
         int32_t *rec = out.tiles + (int64_t)t * kTileWords;
         rec[kRecRowIds + j] = tid;
-        if (j == 0) write_tile_header(rec, key, pos, min(kTileRows, len - q), len, seg_idx[key], q / kTileRows);
+        if (j == 0) write_tile_header(rec, key, pos, min(per, len - q), len, seg_idx[key], q / per);
     }
     if (tid == 0) {
         out.seg_offsets[tot.b] = tot.a;
@@ -587,7 +590,7 @@ static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hip
     if (dyn > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_assemble_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    hipLaunchKernelGGL(meta_assemble_kernel, dim3(chunks), dim3(kMT), dyn, st, S, chunks, out, ws);
+    hipLaunchKernelGGL(meta_assemble_kernel, dim3(chunks), dim3(kMT), dyn, st, n, S, chunks, out, ws);
     return hipGetLastError();
 }
 

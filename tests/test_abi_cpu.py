@@ -45,9 +45,17 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_tile_bound_and_workspace_sizes(L):
     assert L.lora_meta_max_tiles(0, 4) == 0
-    assert L.lora_meta_max_tiles(8, 4) == 5          # ceil(8/16) + min(8, 4)
-    assert L.lora_meta_max_tiles(256, 32) == 48
+    assert L.lora_meta_max_tiles(8, 4) == 5          # ceil(8/16) + min(8, 4) + 0 split segments
+    assert L.lora_meta_max_tiles(256, 32) == 64       # min(16 + 32 + 28, 32 + 32): 9..15-row segments split
+    assert L.lora_meta_max_tiles(6947, 16) == 451     # 435 + 16: no split past 1024 rows
     assert L.lora_meta_max_tiles(1024, 1024) == 1024  # capped at n
+    # the bound holds for the worst partitions: every segment split (9 or 15 rows),
+    # every segment one row, one long segment, and past 1024 rows (no split)
+    for n, S, lens in [(9 * 40, 40, [9] * 40), (15 * 33, 33, [15] * 33), (50, 50, [1] * 50),
+                       (5000, 1, [5000]), (16 * 7 + 9 * 5, 12, [16] * 7 + [9] * 5),
+                       (9 * 113, 113, [9] * 113), (9 * 200, 200, [9] * 200)]:
+        tiles = sum(2 if (n <= 1024 and 8 < t < 16) else -(-t // 16) for t in lens)
+        assert tiles <= L.lora_meta_max_tiles(n, S), (n, S, tiles)
     assert L.lora_meta_workspace_bytes(1024, 8) == 0  # one chunk needs none
     assert L.lora_meta_workspace_bytes(1025, 8) > 0
     assert L.lora_meta_workspace_bytes(5000, 9000) == 0  # unsupported -> 0
