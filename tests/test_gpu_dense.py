@@ -299,3 +299,24 @@ def test_row_permutation_gives_the_same_bits(kw, path):
     ref = fused_bits(c, c.slot, c.a_pool, c.b_pool, c.scale, c.x, c.y)
     got = fused_bits(c, c.slot[p].copy(), c.a_pool, c.b_pool, c.scale, c.x[p].copy(), c.y[p].copy())
     assert np.array_equal(got, ref[p])
+
+
+def test_wide_call_with_split_segments(path):
+    """A batch under 1024 rows whose expand units are wide (16384 output
+    columns): its 9..15-row segments are cut into two tiles while the longer
+    segments' tiles are paired in the shrink and the expand; on the MFMA-only
+    path the cut segments' second tiles run on their own."""
+    rng = np.random.default_rng(77)
+    lens = list(rng.integers(9, 16, size=14)) + list(rng.integers(16, 60, size=8)) + [1, 3, 8]
+    slot = np.concatenate([np.full(m, s, np.int32) for s, m in enumerate(lens)])
+    slot = slot[rng.permutation(slot.size)]
+    c = I.make_dense(78, n=slot.size, k_in=264, slice_sizes=(8192, 8192), num_slots=len(lens), max_rank=16,
+                     rank_choices=[8, 16], slot=slot, scale_num=32.0)
+    print(f"wide split n={c.n} segments={len(lens)} path={path}", flush=True)
+    dv = Dev(c)
+    meta = dv.meta
+    n_tiles = int(meta.counts.cpu()[4])
+    assert n_tiles == sum(2 if 8 < m < 16 else -(-m // 16) for m in lens)
+    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, meta, dv.y)
+    torch.cuda.synchronize()
+    check_y(dv, h16(dv.y), np.arange(c.n), f"wide split {path}")
