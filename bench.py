@@ -170,17 +170,12 @@ def secondary(args):
         E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
         if w == "moe_shared":
             mats = [d16(c.a_shared), d16(c.b_fused)]
-            ta = torch.tensor([mats[0].data_ptr() + e * L * R * H * 2 for e in range(E)], dtype=torch.int64)
-            tb = torch.tensor([mats[1].data_ptr() + e * L * 2 * I_ * R * 2 for e in range(E)], dtype=torch.int64)
-            sb, a_el, b_el = 2 * I_ * R, R * H, 2 * I_ * R
+            (ta, _), (tb, sb) = B.fill_w_ptr(mats[0]), B.fill_w_ptr(mats[1])
+            a_el, b_el = R * H, 2 * I_ * R
         else:
             mats = [d16(m) for m in (c.a_gate, c.a_up, c.b_gate, c.b_up)]
-            ta = torch.tensor([[mats[i].data_ptr() + e * L * R * H * 2 for e in range(E)] for i in (0, 1)],
-                              dtype=torch.int64)
-            tb = torch.tensor([[mats[i].data_ptr() + e * L * I_ * R * 2 for e in range(E)] for i in (2, 3)],
-                              dtype=torch.int64)
-            sb, a_el, b_el = I_ * R, 2 * R * H, 2 * I_ * R
-        ta, tb = ta.cuda(), tb.cuda()
+            (ta, _), (tb, sb) = B.fill_w_ptr(mats[0], mats[1]), B.fill_w_ptr(mats[2], mats[3])
+            a_el, b_el = 2 * R * H, 2 * I_ * R
         nbytes = moe_bytes(c.topk_ids, c.lora_ids, L, E, a_el, b_el, H * 2, 2 * I_ * 2, True)
         rows, copies = c.T, 1
         x, tk, lo = d16(c.x), torch.from_numpy(c.topk_ids).cuda(), torch.from_numpy(c.lora_ids).cuda()
@@ -196,8 +191,7 @@ def secondary(args):
         c = I.moe_w2()
         E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
         mats = [d16(c.a_down), d16(c.b_down)]
-        ta = torch.tensor([mats[0].data_ptr() + e * L * R * I_ * 2 for e in range(E)], dtype=torch.int64).cuda()
-        tb = torch.tensor([mats[1].data_ptr() + e * L * H * R * 2 for e in range(E)], dtype=torch.int64).cuda()
+        (ta, _), (tb, _) = B.fill_w_ptr(mats[0]), B.fill_w_ptr(mats[1])
         nbytes = moe_bytes(c.topk_ids, c.lora_ids, L, E, R * I_, H * R, I_ * 2, H * 4, False)
         rows, copies = c.T, 1
         x2, y = d16(c.x2), d16(c.y)

@@ -24,20 +24,31 @@
  *    launch).  Pointers must stay valid until the stream reaches the call.
  *  - The caller owns every buffer, including metadata and workspaces.  The
  *    library keeps no pointer after a call returns and holds no state
- *    besides the MFMA row threshold (lora_set_mfma_min_rows).
+ *    besides the MFMA row threshold, which is per calling thread
+ *    (lora_set_mfma_min_rows).
  *  - Every check that can run on the host runs before any launch and
  *    returns an error code; nothing is enqueued then.
  *  - Workspaces must be zero-filled before their first use.  The meta
- *    workspace's counters return to zero after every call; the fused and
- *    MoE workspaces keep a count of the calls completed on them (a control
- *    word at a library-defined offset), which tags the partial results of
- *    the next call, and stay valid for calls of any shape that fits them.
+ *    workspace's counters return to zero after every call.  The fused and
+ *    MoE workspaces hold a control line (below) whose tag of the last
+ *    completed call tags the partial results of the next one; they stay
+ *    valid for calls of any shape that fits them, for 2^31 - 2 calls
+ *    (then the tags start over: zero-fill the workspace again before that).
  *    Calls that share a workspace must be ordered (same stream).
  *  - Inside a fused call, units that wait for other units' results do so
  *    with bounded polls.  Such a wait can only run out when calls sharing a
  *    workspace overlap; the kernel then still finishes (the rows concerned
- *    get undefined values) and sets an error word to 1, which the library
- *    never clears: for lora_delta_fused it is the first int32 of ws.
+ *    get undefined values) and sets the control line's error word to 1,
+ *    which the library never clears.
+ *
+ * Control line (int32 words, at a fixed byte offset of the workspace:
+ * LORA_FUSED_CTL_OFFSET for lora_delta_fused, LORA_MOE_CTL_OFFSET for
+ * moe_lora_gemm1_delta and moe_lora_w2_delta, whatever the call's shape):
+ *    [0] error word: 0, or 1 once a bounded wait has given up
+ *    [1] tag of the last completed call (0 before the first; tags run
+ *        0x80000001, 0x80000002, ..., so the low 31 bits count the calls)
+ *    [2] tiles finished by a running call: 0 between calls
+ * Read it after the stream has reached the call.
  *
  * Layouts (metrale docs, LoraPair and LoraRoute; the slices follow vLLM's
  * add_shrink / add_expand, one A and one block of B rows per output slice):
@@ -75,6 +86,10 @@ enum {
     LORA_EWORKSPACE = -3,   /* workspace or metadata buffer too small */
     LORA_ELAUNCH = -4       /* the HIP runtime refused a launch */
 };
+
+/* Byte offsets of the control line in the fused and MoE workspaces. */
+#define LORA_FUSED_CTL_OFFSET 0
+#define LORA_MOE_CTL_OFFSET 128
 
 /* Rows per tile of the per-segment work lists built by lora_meta_build. */
 #define LORA_TILE_ROWS 16
@@ -216,7 +231,9 @@ size_t moe_lora_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts,
  *       out[t][j][:] = scale * B @ (A @ x[t])
  * l < 0 gives a zero row.  l >= num_loras or e outside [0, num_experts) gives
  * a zero row and is counted: after the call the first 16 bytes of ws hold
- * counts {n_active_pairs, n_segments, n_invalid_pairs, n_long_segments}.
+ * counts {n_active_pairs, n_segments, n_invalid_pairs, n_long_segments}
+ * (the whole pair metadata is in ws too: moe_lora_meta_layout).  The
+ * control line is at byte LORA_MOE_CTL_OFFSET.
  * The delta is unweighted and kept per pair (it is added before the gated
  * activation).  out is [T][top_k][2*inter] bf16, every element written.
  * With T = 0 only the counts are written, and x, topk_ids, lora_ids and out
@@ -269,12 +286,26 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I,
                       int32_t rank, int32_t H, float scale, uint16_t *y, int64_t ldy,
                       int32_t reuse_routing, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Where a MoE call (gemm1 or w2) keeps the pair metadata it builds in ws,
+ * as byte offsets into ws (offsets [host], 5 entries): counts (8 int32),
+ * sorted_rows, seg_offsets, seg_slot, tiles -- the arrays of lora_meta_t for
+ * n = T * top_k rows (pairs p = t * top_k + j) and S = num_loras *
+ * num_experts slots, with key l * num_experts + e (vLLM punica_base.py,
+ * moe_lora_align_block_size: pairs grouped by (adapter, expert); FlashInfer
+ * bgmv_moe_gemm1_lora_delta: topk_ids, lora_ids).  The offsets depend on
+ * (T, top_k, num_experts, num_loras) only.  LORA_EINVAL for bad sizes.
+ */
+int moe_lora_meta_layout(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras,
+                         size_t *offsets);
+
 /* Segments with at least this many rows take the MFMA path, shorter ones the
- * vector-ALU path (default 16; the environment variable LORA_MFMA_MIN_ROWS,
- * read at the first call, overrides the default).  The setter is the one
- * piece of process-wide state: it takes effect for calls enqueued after it
- * returns; values below 1 are clamped to 1.  Both paths compute the same
- * result to within the tolerance of the fp32 accumulation. */
+ * vector-ALU path.  The default is 16 (the environment variable
+ * LORA_MFMA_MIN_ROWS, read once, replaces it).  The setter overrides it for
+ * the calling thread only (other threads keep theirs), for calls that
+ * thread enqueues after it returns; rows <= 0 drops the override.  Both
+ * paths compute the same result to within the tolerance of the fp32
+ * accumulation. */
 int32_t lora_mfma_min_rows(void);
 void lora_set_mfma_min_rows(int32_t rows);
 

@@ -3,7 +3,6 @@
 // allocates, frees or synchronizes; every check runs before any launch.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdlib>
 
 #include "../../include/lora.h"
@@ -19,22 +18,22 @@ constexpr int kMaxSlots = 1 << 20;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-std::atomic<int> g_mfma_min{-1};
-
-int mfma_min_rows() {
-    int v = g_mfma_min.load(std::memory_order_relaxed);
-    if (v < 0) {
-        int d = 16;
+// The MFMA row threshold: a process-wide default (16, or LORA_MFMA_MIN_ROWS
+// read once), and a per-thread override that only the calling thread sees,
+// so one caller's setting never changes another thread's arithmetic path.
+int default_mfma_min() {
+    static const int d = [] {
         if (const char *e = std::getenv("LORA_MFMA_MIN_ROWS")) {
             const int x = std::atoi(e);
-            if (x > 0) d = x;
+            if (x > 0) return x;
         }
-        int expected = -1;
-        g_mfma_min.compare_exchange_strong(expected, d);
-        v = g_mfma_min.load(std::memory_order_relaxed);
-    }
-    return v;
+        return 16;
+    }();
+    return d;
 }
+thread_local int t_mfma_min = 0;  // 0: the default
+
+int mfma_min_rows() { return t_mfma_min > 0 ? t_mfma_min : default_mfma_min(); }
 
 int tile_bound(int n, int S) { return tl::tile_bound_of(n, S); }
 
@@ -221,19 +220,27 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, co
         tl::launch_fused(d, meta.tiles, meta.counts, plan, ws, mfma_min_rows(), static_cast<hipStream_t>(stream)));
 }
 
-// MoE workspace: [counts 8 | sorted_rows n | seg_offsets cap+1 | seg_slot cap | tiles] [meta ws] [fused ws]
+// MoE workspace: a fixed 256-byte header (counts, 8 int32 at byte 0; the
+// fused control line at byte LORA_MOE_CTL_OFFSET), then [sorted_rows n |
+// seg_offsets cap+1 | seg_slot cap | tiles] [meta ws] [fused flags and
+// partials].  The header never moves, so the control line's call tag
+// survives calls of any shape; the pair metadata's offsets depend only on
+// (T, top_k, E, L), so a w2 call can reuse the routing a gemm1 call built.
 namespace {
 struct MoeLayout {
-    size_t counts, sorted, segoff, segslot, tiles, meta_ws, fused, total;
+    size_t counts, ctl, sorted, segoff, segslot, tiles, meta_ws, fused, total;
     tl::FusedPlan plan;
 };
+static_assert(LORA_MOE_CTL_OFFSET >= 8 * sizeof(int32_t) && LORA_MOE_CTL_OFFSET + 64 <= 256 &&
+                  LORA_MOE_CTL_OFFSET % 64 == 0,
+              "the control line sits in the header, clear of the counts");
 MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int k_in, int n_sh) {
     MoeLayout m{};
     const int n = T * top_k, S = L * E, cap = n < S ? n : S;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    size_t o = 0;
-    m.counts = o;
-    o = up(o + 8 * sizeof(int32_t));
+    m.counts = 0;
+    m.ctl = LORA_MOE_CTL_OFFSET;
+    size_t o = 256;
     m.sorted = o;
     o = up(o + (size_t)n * sizeof(int32_t));
     m.segoff = o;
@@ -291,7 +298,8 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
     if (n == 0) return LORA_OK;
     tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
                    lora_ids, num_experts, num_loras, rank, inter, scale, out};
-    return launched(tl::launch_moe_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused, mfma_min_rows(), st));
+    return launched(tl::launch_moe_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused,
+                                         reinterpret_cast<int *>(b + lay.ctl), mfma_min_rows(), st));
 }
 
 size_t moe_lora_w2_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras, int32_t rank,
@@ -337,12 +345,26 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, con
     tl::MoeW2Shape m{x2, ldx, T, I, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, top_k, topk_weights,
                      num_experts, num_loras, rank, H, scale, y, ldy};
     return launched(
-        tl::launch_moe_w2_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused, mfma_min_rows(), st));
+        tl::launch_moe_w2_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused,
+                                reinterpret_cast<int *>(b + lay.ctl), mfma_min_rows(), st));
+}
+
+int moe_lora_meta_layout(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras, size_t *offsets) {
+    if (!offsets || T < 0 || top_k < 1 || num_experts < 1 || num_loras < 1) return LORA_EINVAL;
+    if ((long long)T * top_k > kMaxRows || (long long)num_experts * num_loras > kMaxSlots) return LORA_EINVAL;
+    // the metadata part of the layout does not depend on rank, width or form
+    const MoeLayout lay = moe_layout(T, top_k, num_experts, num_loras, 8, 8, 1);
+    offsets[0] = lay.counts;
+    offsets[1] = lay.sorted;
+    offsets[2] = lay.segoff;
+    offsets[3] = lay.segslot;
+    offsets[4] = lay.tiles;
+    return LORA_OK;
 }
 
 int32_t lora_mfma_min_rows(void) { return mfma_min_rows(); }
 
-void lora_set_mfma_min_rows(int32_t rows) { g_mfma_min.store(rows < 1 ? 1 : rows, std::memory_order_relaxed); }
+void lora_set_mfma_min_rows(int32_t rows) { t_mfma_min = rows > 0 ? rows : 0; }
 
 const char *lora_status_string(int status) {
     switch (status) {

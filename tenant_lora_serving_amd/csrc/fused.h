@@ -70,8 +70,18 @@ constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its unit
 constexpr int kFlagWords = 64;      // 64-bit words per tile: piece flags, then the finished-consumer count
 // control line of the workspace
 constexpr int kCtlError = 0;  // set when a bounded wait gave up
-constexpr int kCtlGen = 1;    // completed calls on this workspace
+constexpr int kCtlGen = 1;    // tag of the last completed call on this workspace (0: none yet)
 constexpr int kCtlDone = 2;   // finished tiles of the running call
+
+// Call tags have the top bit set and never equal 0xFFFFFFFF: they run
+// 0x80000001, 0x80000002, ... 0xFFFFFFFE and start over.  Whatever else a
+// workspace may hold where a later call keeps its flags and partials -- zero
+// fill, or the int32 metadata a MoE call builds in the same workspace (row
+// ids, positions, slots, counts: all in [0, 2^31)) -- can therefore never
+// read as the current call's tag, and neither can an earlier call's tag.
+__device__ __forceinline__ uint32_t next_tag(uint32_t last) {
+    return (last >= 0x80000001u && last < 0xFFFFFFFEu) ? last + 1u : 0x80000001u;
+}
 
 // ============================================================ tile record, per wave
 // Lane i holds word (i mod 32) of the record; the scalar fields are read
@@ -1164,7 +1174,7 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
     if (un.kind == kUnitShrink || un.kind == kUnitExpand) {
         const int t = un.t;
         if (t >= fa.tile_bound) return;
-        const uint32_t tag = (uint32_t)load_relaxed(fa.ctl + kCtlGen) + 1u;
+        const uint32_t tag = next_tag((uint32_t)load_relaxed(fa.ctl + kCtlGen));
         if (un.kind == kUnitShrink) {
             const int p = un.sub;
             const Hdr h = load_hdr(fa.tiles, t);
@@ -1319,8 +1329,8 @@ static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, bool mfma_le
 // its tiles are expected on the MFMA path (selects expand mode 2 over 1).
 template <class Op>
 static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                                  int C, int EC, void *ws, int mfma_min, bool mfma_lean, int add_inputs,
-                                  ZeroFill zf, int zero_units, hipStream_t st) {
+                                  int C, int EC, void *ws, int *ctl, int mfma_min, bool mfma_lean,
+                                  int add_inputs, ZeroFill zf, int zero_units, hipStream_t st) {
     char *w = static_cast<char *>(ws);
     FusedArgs fa{};
     fa.tiles = tiles;
@@ -1341,7 +1351,7 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     fa.P = (steps + ks - 1) / ks;
     fa.C = C;
     fa.EC = EC;
-    fa.ctl = reinterpret_cast<int *>(w);
+    fa.ctl = ctl;
     fa.flags = reinterpret_cast<uint64_t *>(w + 256);
     fa.part = reinterpret_cast<uint64_t *>(w + plan.flag_bytes);
     fa.mfma_min = mfma_min;

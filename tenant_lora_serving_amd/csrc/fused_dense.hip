@@ -41,7 +41,8 @@ hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t
     const int EC = expand_width(d.slice_off, d.num_slices, plan.tile_bound);
     const int C = chunks_of(d.slice_off, d.num_slices, EC);
     const bool lean = (long long)d.n >= (long long)mfma_min * d.num_slots;
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, lean, 1,
+    // the control line is the first 256 bytes of the fused workspace
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, static_cast<int *>(ws), mfma_min, lean, 1,
                            ZeroFill{nullptr, nullptr, 1, 1, 1, 0}, 0, st);
 }
 

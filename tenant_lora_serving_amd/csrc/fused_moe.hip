@@ -5,7 +5,7 @@
 namespace tl {
 
 hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                            void *ws, int mfma_min, hipStream_t st) {
+                            void *ws, int *ctl, int mfma_min, hipStream_t st) {
     MoeOp op{};
     op.x = m.x;
     op.ldx = m.ldx;
@@ -30,7 +30,7 @@ hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32
     const int EC = expand_width(off, 2, plan.tile_bound);
     const int C = chunks_of(off, 2, EC);
     const bool lean = (long long)n_pairs >= (long long)mfma_min * m.E * m.L;
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, lean, 0, zf, zero_units, st);
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, ctl, mfma_min, lean, 0, zf, zero_units, st);
 }
 
 }  // namespace tl

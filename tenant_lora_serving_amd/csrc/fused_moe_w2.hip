@@ -5,7 +5,7 @@
 namespace tl {
 
 hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const int32_t *tiles, const int32_t *counts,
-                               const FusedPlan &plan, void *ws, int mfma_min, hipStream_t st) {
+                               const FusedPlan &plan, void *ws, int *ctl, int mfma_min, hipStream_t st) {
     MoeW2Op op{};
     op.x = m.x2;
     op.ldx = m.ldx;
@@ -28,7 +28,7 @@ hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const int32_t *tiles, const 
     const int EC = expand_width(off, 1, plan.tile_bound);
     const int C = chunks_of(off, 1, EC);
     const bool lean = (long long)m.T * m.top_k >= (long long)mfma_min * m.E * m.L;
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, mfma_min, lean, 1, zf, 0, st);
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, ctl, mfma_min, lean, 1, zf, 0, st);
 }
 
 }  // namespace tl

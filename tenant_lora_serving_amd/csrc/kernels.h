@@ -124,7 +124,7 @@ struct MoeShape {
     uint16_t *out;
 };
 hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                            void *ws, int mfma_min, hipStream_t st);
+                            void *ws, int *ctl, int mfma_min, hipStream_t st);
 
 // Routed-MoE down projection: x2 [n_pairs][I] (ldx), y [n_pairs][H] (ldy) added to.
 struct MoeW2Shape {
@@ -143,6 +143,6 @@ struct MoeW2Shape {
     int64_t ldy;
 };
 hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const int32_t *tiles, const int32_t *counts,
-                               const FusedPlan &plan, void *ws, int mfma_min, hipStream_t st);
+                               const FusedPlan &plan, void *ws, int *ctl, int mfma_min, hipStream_t st);
 
 }  // namespace tl

@@ -366,3 +366,47 @@ def router_fold(seed: int = 8) -> ExpertFoldCase:
 
 
 CONFIGS = {1: tiny_bgmv, 2: decode_bgmv, 3: prefill_sgmv, 4: no_reuse, 5: moe_gemm1}
+
+
+# ---------------------------------------------------------------- save / load
+_CASE_TYPES = {cls.__name__: cls for cls in (DenseCase, MoeCase, MoeW2Case, ExpertFoldCase)}
+
+
+def save_case(case, path: str) -> None:
+    """Write a case to an .npz file: its arrays as arrays, every other field
+    (sizes, name, slice sizes, the meta dict) as one JSON string.  Nothing in
+    the file needs pickle to read back."""
+    import dataclasses
+    import json
+    arrays, plain = {}, {}
+    for f in dataclasses.fields(case):
+        v = getattr(case, f.name)
+        if isinstance(v, np.ndarray):
+            arrays[f.name] = v
+        elif isinstance(v, dict):      # DenseCase.meta: arrays (sequence lengths, slots)
+            plain[f.name] = {}
+            for k, e in v.items():
+                arrays[f"{f.name}.{k}"] = np.asarray(e)
+        else:
+            plain[f.name] = list(v) if isinstance(v, tuple) else v
+    np.savez(path, __case__=np.array(json.dumps({"type": type(case).__name__, "fields": plain})), **arrays)
+
+
+def load_case(path: str):
+    """Read a case written by save_case (numpy's loader with pickle disabled)."""
+    import json
+    with np.load(path, allow_pickle=False) as z:
+        head = json.loads(str(z["__case__"]))
+        cls = _CASE_TYPES[head["type"]]
+        kw = dict(head["fields"])
+        for k in z.files:
+            if k == "__case__":
+                continue
+            if "." in k:
+                d, e = k.split(".", 1)
+                kw.setdefault(d, {})[e] = np.ascontiguousarray(z[k])
+            else:
+                kw[k] = np.ascontiguousarray(z[k])
+    if "slice_sizes" in kw:
+        kw["slice_sizes"] = tuple(kw["slice_sizes"])
+    return cls(**kw)

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "liblora.so")
 
 TILE_ROWS = 16
 TILE_WORDS = 32
+FUSED_CTL_OFFSET = 0      # byte offset of the control line in a lora_delta_fused workspace
+MOE_CTL_OFFSET = 128      # ... in a moe_lora_gemm1_delta / moe_lora_w2_delta workspace
 
 _c_i32, _c_i64, _c_sz, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                      ctypes.c_void_p, ctypes.c_float)
@@ -79,6 +81,8 @@ def lib():
         L.moe_lora_w2_delta.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i64,
                                         _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
                                         _c_f, _c_p, _c_i64, _c_i32, _c_p, _c_sz, _c_p]
+        L.moe_lora_meta_layout.restype = ctypes.c_int
+        L.moe_lora_meta_layout.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]
         L.lora_mfma_min_rows.restype = _c_i32
         L.lora_mfma_min_rows.argtypes = []
         L.lora_set_mfma_min_rows.restype = None
@@ -93,13 +97,39 @@ EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build
             "lora_meta_from_offsets", "lora_shrink",
             "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused",
             "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "moe_lora_w2_workspace_bytes",
-            "moe_lora_w2_delta", "lora_mfma_min_rows",
+            "moe_lora_w2_delta", "moe_lora_meta_layout", "lora_mfma_min_rows",
             "lora_set_mfma_min_rows", "lora_status_string"]
 
 
 def _check(fn: str, status: int):
     if status != 0:
         raise LoraError(fn, status, lib().lora_status_string(status).decode())
+
+
+@dataclass
+class WsStatus:
+    """A fused or MoE workspace's control line."""
+    error: int       # 1 once a bounded wait gave up (never cleared by the library)
+    calls: int       # calls completed on the workspace (low 31 bits of the last tag)
+    running: int     # tiles counted by an unfinished call: 0 between calls
+
+    @property
+    def ok(self) -> bool:
+        return self.error == 0 and self.running == 0
+
+
+def ws_status(ws: torch.Tensor, moe: bool = False) -> WsStatus:
+    """Read a workspace's control line (synchronizes with the device)."""
+    o = MOE_CTL_OFFSET if moe else FUSED_CTL_OFFSET
+    err, tag, run = ws[o:o + 12].view(torch.int32).cpu().tolist()
+    return WsStatus(err, tag & 0x7FFFFFFF, run)
+
+
+def _check_ws(fn: str, ws: torch.Tensor, moe: bool, stream):
+    (stream or torch.cuda.current_stream()).synchronize()
+    st = ws_status(ws, moe)
+    if not st.ok:
+        raise LoraError(fn, -100, f"workspace control line reports {st}")
 
 
 def _stream(stream=None) -> int:
@@ -126,6 +156,8 @@ def _rows_ld(t: torch.Tensor, name: str):
 
 
 def set_mfma_min_rows(rows: int):
+    """Override the MFMA row threshold for the calling thread (rows <= 0: back
+    to the default)."""
     lib().lora_set_mfma_min_rows(int(rows))
 
 
@@ -251,8 +283,9 @@ def fused_workspace(n: int, num_slots: int, num_slices: int, max_rank: int, k_in
 def lora_delta_fused(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor,
                      scale: torch.Tensor, slice_sizes, meta: LoraMeta, y: torch.Tensor,
                      offset_start: int = 0, ws: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
-    """y[i, window] += (scale[s] * x[i] @ A_s^T) @ B_s^T for active rows, in place."""
+                     stream=None, check: bool = False) -> torch.Tensor:
+    """y[i, window] += (scale[s] * x[i] @ A_s^T) @ B_s^T for active rows, in place.
+    check: synchronize afterwards and raise if the workspace's error word is set."""
     _pool_dims(a_pool, b_pool)
     S, Lsl, R, k_in = a_pool.shape
     if len(slice_sizes) != Lsl or sum(slice_sizes) != b_pool.shape[1]:
@@ -271,6 +304,8 @@ def lora_delta_fused(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor
                                 yp, ldy, int(offset_start), _dev(ws, "ws", torch.uint8),
                                 ws.numel(), _stream(stream))
     _check("lora_delta_fused", st)
+    if check:
+        _check_ws("lora_delta_fused", ws, False, stream)
     return y
 
 
@@ -285,7 +320,8 @@ def moe_lora_gemm1_delta(hidden_states: torch.Tensor, w_ptr_a: torch.Tensor, lor
                          w_ptr_b: torch.Tensor, lora_stride_b: int, topk_ids: torch.Tensor,
                          lora_ids: torch.Tensor, rank: int, intermediate_size: int, *,
                          num_loras: int, scale: float = 1.0, out: torch.Tensor | None = None,
-                         ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                         ws: torch.Tensor | None = None, stream=None,
+                         check: bool = False) -> torch.Tensor:
     """[T, top_k, 2I] gate/up delta per routed pair.  A 2-D [2, E] pointer
     table selects the regular form, a 1-D [E] table the shared-A form."""
     shared = w_ptr_a.dim() == 1
@@ -309,6 +345,8 @@ def moe_lora_gemm1_delta(hidden_states: torch.Tensor, w_ptr_a: torch.Tensor, lor
         E, int(num_loras), int(rank), int(intermediate_size), float(scale),
         _dev(out, "out", torch.bfloat16), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     _check("moe_lora_gemm1_delta", st)
+    if check:
+        _check_ws("moe_lora_gemm1_delta", ws, True, stream)
     return out
 
 
@@ -332,7 +370,7 @@ def moe_lora_w2_delta(x2: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: in
                       lora_ids: torch.Tensor, rank: int, y: torch.Tensor, *, num_loras: int,
                       topk_weights: torch.Tensor | None = None, scale: float = 1.0,
                       ws: torch.Tensor | None = None, reuse_routing: bool = False,
-                      stream=None) -> torch.Tensor:
+                      stream=None, check: bool = False) -> torch.Tensor:
     """Add the routed down-projection delta to y ([T*top_k, H] or [T, top_k, H])
     in place; x2 holds the pairs' activated gemm1 outputs, [T*top_k, I].
     reuse_routing: ws holds the pair metadata of this routing from the
@@ -362,12 +400,52 @@ def moe_lora_w2_delta(x2: torch.Tensor, w_ptr_a: torch.Tensor, lora_stride_a: in
         E, int(num_loras), int(rank), H, float(scale), yp, ldy, 1 if reuse_routing else 0,
         _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     _check("moe_lora_w2_delta", st)
+    if check:
+        _check_ws("moe_lora_w2_delta", ws, True, stream)
     return y
 
 
 def moe_counts(ws: torch.Tensor) -> torch.Tensor:
     """{n_active_pairs, n_segments, n_invalid_pairs, n_long_segments} of the last MoE call."""
     return ws[:16].view(torch.int32)
+
+
+def moe_meta_view(ws: torch.Tensor, T: int, top_k: int, num_experts: int, num_loras: int) -> LoraMeta:
+    """The pair metadata the last MoE call built in ws, as views of ws (for n =
+    T * top_k pairs and S = num_loras * num_experts (adapter, expert) keys)."""
+    off = (_c_sz * 5)()
+    _check("moe_lora_meta_layout", lib().moe_lora_meta_layout(T, top_k, num_experts, num_loras, off))
+    n, S = T * top_k, num_experts * num_loras
+    cap = min(n, S)
+    tb = int(lib().lora_meta_max_tiles(n, S))
+
+    def view(i, count):
+        return ws[off[i]:off[i] + 4 * count].view(torch.int32)
+    return LoraMeta(n, S, view(1, n), view(2, cap + 1), view(3, cap), view(0, 8),
+                    view(4, tb * TILE_WORDS), ws[:0])
+
+
+def fill_w_ptr(*banks: torch.Tensor):
+    """Pointer table and adapter stride over expert-major LoRA banks, the form
+    bgmv_moe_gemm1_lora_delta's w_ptr_a / w_ptr_b take.  Each bank is a
+    contiguous [num_experts, num_loras, rows, cols] bf16 device tensor; entry
+    [s][e] is the address of bank s's block for expert e, and adapter l's
+    matrix starts l * stride elements past it, stride = rows * cols.  One bank
+    gives the 1-D [num_experts] table (one shared A, or the fused [2I, rank] B),
+    two give [2, num_experts] (gate, up).  Returns (table on the banks' device,
+    stride).  The banks must outlive every call that uses the table."""
+    if not banks or len(banks) > 2:
+        raise ValueError("fill_w_ptr takes one bank (shared / fused form) or two (gate, up)")
+    shapes = {tuple(b.shape) for b in banks}
+    if len(shapes) != 1 or banks[0].dim() != 4:
+        raise ValueError("banks must all be [num_experts, num_loras, rows, cols]")
+    for i, b in enumerate(banks):
+        _dev(b, f"bank {i}", torch.bfloat16)
+    E, L, r, c = banks[0].shape
+    block = L * r * c * banks[0].element_size()
+    tab = [[b.data_ptr() + e * block for e in range(E)] for b in banks]
+    t = torch.tensor(tab if len(banks) == 2 else tab[0], dtype=torch.int64)
+    return t.to(banks[0].device), r * c
 
 
 # ---------------------------------------------------------------- expert-sorted and router folds

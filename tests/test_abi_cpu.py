@@ -183,3 +183,44 @@ def test_moe_w2_validation(L):
 def test_status_strings(L):
     for s in (OK, EINVAL, EUNSUP, EWS, -4, 99):
         assert isinstance(L.lora_status_string(s), bytes)
+
+
+def test_moe_meta_layout(L):
+    off = (ctypes.c_size_t * 5)()
+    assert L.moe_lora_meta_layout(2048, 8, 64, 8, off) == OK
+    n, S = 2048 * 8, 64 * 8
+    up = lambda v: (v + 255) // 256 * 256   # noqa: E731
+    # counts at byte 0; the header line (counts, control line) is 256 bytes
+    assert list(off) == [0, 256, 256 + up(4 * n), 256 + up(4 * n) + up(4 * (min(n, S) + 1)),
+                         256 + up(4 * n) + up(4 * (min(n, S) + 1)) + up(4 * min(n, S))]
+    assert B.MOE_CTL_OFFSET + 12 <= 256 and B.MOE_CTL_OFFSET >= 32   # clear of the 8 counts
+    # the tiles fit every MoE workspace of that routing, gemm1 (either form) or w2
+    tiles_end = off[4] + 4 * 32 * L.lora_meta_max_tiles(n, S)
+    assert tiles_end <= L.moe_lora_workspace_bytes(2048, 8, 64, 8, 16, 4096)
+    assert tiles_end <= L.moe_lora_w2_workspace_bytes(2048, 8, 64, 8, 8, 8)
+    assert L.moe_lora_meta_layout(-1, 8, 64, 8, off) == EINVAL
+    assert L.moe_lora_meta_layout(16, 0, 64, 8, off) == EINVAL
+    assert L.moe_lora_meta_layout(16, 8, 64, 8, None) == EINVAL
+
+
+def test_mfma_threshold_is_per_thread(L):
+    import threading
+    default = L.lora_mfma_min_rows()
+    seen = {}
+
+    def other():
+        seen["before"] = L.lora_mfma_min_rows()
+        L.lora_set_mfma_min_rows(3)
+        seen["after"] = L.lora_mfma_min_rows()
+
+    L.lora_set_mfma_min_rows(7)
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    try:
+        assert L.lora_mfma_min_rows() == 7          # the other thread's setting is not seen here
+        assert seen == {"before": default, "after": 3}
+        L.lora_set_mfma_min_rows(0)
+        assert L.lora_mfma_min_rows() == default    # 0 drops the override
+    finally:
+        L.lora_set_mfma_min_rows(0)

@@ -2,7 +2,9 @@
 fp64 oracle, on both compute paths (vector ALU for short segments, MFMA for
 segments with at least `mfma_min_rows` rows), plus the bitwise invariants:
 rows without an active slot and columns outside the slice windows untouched,
-zero scale leaves y unchanged, run-to-run bitwise determinism."""
+zero scale leaves y unchanged, run-to-run bitwise determinism.  Every row of
+every full-size workload is compared; after every fused call the workspace's
+control line shows no bounded wait gave up."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ import torch
 from oracle import oracle as O
 from tenant_lora_serving_amd import inputs as I
 from tenant_lora_serving_amd import lora as B
-from gpu_util import assert_close, bf64, d16, d32, h16
+from gpu_util import assert_close, assert_close_chunked, assert_ws_ok, bf64, d16, d32, h16
 
 pytestmark = pytest.mark.gpu
 
@@ -48,28 +50,44 @@ class Dev:
         self.y_host = yh
         self.y = d16(yh)
         self.meta = B.lora_meta_build(self.slot, c.num_slots)
+        self.ws = B.fused_workspace(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in)
+
+    def fused(self, ws=None, scale=None):
+        """lora_delta_fused on this case; the control line is checked afterwards."""
+        c = self.c
+        ws = self.ws if ws is None else ws
+        B.lora_delta_fused(self.x, self.a, self.b, self.scale if scale is None else scale, c.slice_sizes,
+                           self.meta, self.y, offset_start=self.offset_start, ws=ws)
+        assert_ws_ok(ws)
 
 
 def active(c):
     return (c.slot >= 0) & (c.slot < c.num_slots)
 
 
-def check_y(dv: Dev, y_gpu_bits: np.ndarray, rows: np.ndarray, what: str, add_inputs=True, xa=None):
+def check_y(dv: Dev, y_gpu_bits: np.ndarray, rows: np.ndarray | None, what: str, add_inputs=True, xa=None,
+            chunk: int = 256):
+    """Every listed row (default: all rows) within tolerance of the oracle
+    inside the window, bitwise unchanged outside it and on inactive rows."""
     c = dv.c
-    if xa is None:
-        orc = O.fused_rows(c.x, c.k_in, c.a_pool, c.b_pool, c.scale, c.num_slots, c.slice_sizes,
-                           c.max_rank, c.slot, rows, dv.y_host, dv.offset_start)
-    else:
-        orc = O.expand_rows(xa, c.b_pool, c.num_slots, c.slice_sizes, c.max_rank, c.slot, rows,
-                            dv.y_host, dv.offset_start, add_inputs)
-    gpu = bf64(y_gpu_bits[rows])
+    rows = np.arange(c.n) if rows is None else np.asarray(rows)
     w0, w1 = dv.offset_start, dv.offset_start + c.n_out
-    worst = assert_close(gpu[:, w0:w1], orc[:, w0:w1], what)
     # outside the window and on inactive rows: bitwise unchanged
     assert np.array_equal(y_gpu_bits[rows][:, :w0], dv.y_host[rows][:, :w0])
     assert np.array_equal(y_gpu_bits[rows][:, w1:], dv.y_host[rows][:, w1:])
-    off = ~active(c)[rows]
-    assert np.array_equal(y_gpu_bits[rows][off], dv.y_host[rows][off])
+    off = rows[~active(c)[rows]]
+    assert np.array_equal(y_gpu_bits[off], dv.y_host[off])
+    worst = 0.0
+    for c0 in range(0, rows.size, chunk):
+        sel = rows[c0:c0 + chunk]
+        if xa is None:
+            orc = O.fused_rows(c.x, c.k_in, c.a_pool, c.b_pool, c.scale, c.num_slots, c.slice_sizes,
+                               c.max_rank, c.slot, sel, dv.y_host, dv.offset_start)
+        else:
+            orc = O.expand_rows(xa[c0:c0 + chunk], c.b_pool, c.num_slots, c.slice_sizes, c.max_rank, c.slot,
+                                sel, dv.y_host, dv.offset_start, add_inputs)
+        gpu = bf64(y_gpu_bits[sel])
+        worst = max(worst, assert_close(gpu[:, w0:w1], orc[:, w0:w1], f"{what} rows [{c0}:{c0 + sel.size}]"))
     return worst
 
 
@@ -106,10 +124,8 @@ def test_fused_small(kw, path):
     c = small_case(**kw)
     print(f"fused small {kw} path={path}", flush=True)
     dv = Dev(c, ldy_pad=16, offset_start=8)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y,
-                       offset_start=dv.offset_start)
-    torch.cuda.synchronize()
-    check_y(dv, h16(dv.y), np.arange(c.n), f"fused {kw} {path}")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"fused {kw} {path}")
 
 
 @pytest.mark.parametrize("kw", SMALL[:5], ids=[f"s{k['seed']}" for k in SMALL[:5]])
@@ -139,9 +155,8 @@ def test_shrink_then_expand_small(kw, path):
 def test_fused_tiny_config(path):
     c = I.tiny_bgmv()
     dv = Dev(c)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
-    torch.cuda.synchronize()
-    check_y(dv, h16(dv.y), np.arange(c.n), f"tiny {path}")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"tiny {path}")
 
 
 @pytest.fixture(scope="module")
@@ -153,9 +168,8 @@ def test_fused_decode_full(decode_case, path):
     c = decode_case
     print(f"decode full path={path}", flush=True)
     dv = Dev(c)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
-    torch.cuda.synchronize()
-    check_y(dv, h16(dv.y), np.arange(c.n), f"decode {path}")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"decode {path}")
 
 
 def test_fused_decode_deterministic_and_ws_state(decode_case):
@@ -163,30 +177,27 @@ def test_fused_decode_deterministic_and_ws_state(decode_case):
     outs = []
     for _ in range(3):
         dv = Dev(c)
-        ws = B.fused_workspace(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in)
-        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y, ws=ws)
-        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y, ws=ws)
-        torch.cuda.synchronize()
+        dv.fused()
+        dv.fused()
         outs.append(h16(dv.y))
         # control line: no bounded wait gave up, two completed calls, no consumer left counted
-        ctl = ws[:16].view(torch.int32).cpu().tolist()
-        assert ctl[:3] == [0, 2, 0], ctl
+        assert_ws_ok(dv.ws, calls=2)
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
 
 
 def test_fused_workspace_reused_across_shapes(decode_case):
-    """One workspace serves calls of different shapes in turn: partials left by
-    an earlier call (another layout of tiles and pieces) are never taken for
-    the current call's."""
-    big = decode_case
-    small = small_case(11, n=40, k_in=1032, slices=(64, 32), S=5, R=24)
-    ws = B.fused_workspace(big.n, big.num_slots, big.num_slices, 32, big.k_in)
-    for case in (big, small, big, small, small, big):
+    """One workspace serves calls of different shapes in turn, each with its
+    own routing and inputs: partials left by an earlier call (another layout
+    of tiles and pieces) are never taken for the current call's."""
+    cases = [decode_case, small_case(11, n=40, k_in=1032, slices=(64, 32), S=5, R=24),
+             I.decode_bgmv(seed=21), small_case(12, n=40, k_in=1032, slices=(64, 32), S=5, R=24),
+             small_case(13, n=33, k_in=1032, slices=(64, 32), S=7, R=24), I.decode_bgmv(seed=22)]
+    ws = B.fused_workspace(decode_case.n, decode_case.num_slots, decode_case.num_slices, 32, decode_case.k_in)
+    for i, case in enumerate(cases):
         dv = Dev(case)
-        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, case.slice_sizes, dv.meta, dv.y, ws=ws)
-        torch.cuda.synchronize()
-        check_y(dv, h16(dv.y), np.arange(case.n), f"reuse n={case.n}")
-    assert ws[:16].view(torch.int32).cpu().tolist()[:3] == [0, 6, 0]
+        dv.fused(ws=ws)
+        assert_ws_ok(ws, calls=i + 1)
+        check_y(dv, h16(dv.y), None, f"reuse call {i} n={case.n}")
 
 
 def test_fused_workspace_reused_across_layouts(decode_case):
@@ -195,19 +206,17 @@ def test_fused_workspace_reused_across_layouts(decode_case):
     call kept partials of another layout, and every result is still right."""
     few_tiles_big_partials = small_case(12, n=40, k_in=4096, slices=(64, 32), S=3, R=64)
     many_tiles_multi_step = small_case(13, n=5000, k_in=4096, slices=(4096,), S=4, R=16, neg=0.05)
-    cases = [decode_case, few_tiles_big_partials, decode_case, many_tiles_multi_step,
-             few_tiles_big_partials, decode_case]
+    cases = [decode_case, few_tiles_big_partials, I.decode_bgmv(seed=23), many_tiles_multi_step,
+             small_case(14, n=40, k_in=4096, slices=(64, 32), S=3, R=64), I.decode_bgmv(seed=24)]
     need = max(int(B.lib().lora_fused_workspace_bytes(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in))
                for c in cases)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for i, case in enumerate(cases):
         print(f"layout reuse call {i}: n={case.n} k_in={case.k_in} R={case.max_rank}", flush=True)
         dv = Dev(case)
-        B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, case.slice_sizes, dv.meta, dv.y, ws=ws)
-        torch.cuda.synchronize()
-        rows = np.arange(case.n) if case.n <= 512 else np.arange(case.n)[::17]
-        check_y(dv, h16(dv.y), rows, f"layout reuse {i}")
-    assert ws[:16].view(torch.int32).cpu().tolist()[:3] == [0, len(cases), 0]
+        dv.fused(ws=ws)
+        assert_ws_ok(ws, calls=i + 1)
+        check_y(dv, h16(dv.y), None, f"layout reuse {i}")
 
 
 def test_fused_k_beyond_one_flag_block(path):
@@ -215,16 +224,14 @@ def test_fused_k_beyond_one_flag_block(path):
     # unit takes two steps even in a decode-sized call
     c = small_case(14, n=24, k_in=65 * 512 + 8, slices=(48,), S=3, R=16)
     dv = Dev(c)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
-    torch.cuda.synchronize()
-    check_y(dv, h16(dv.y), np.arange(c.n), f"k_in={c.k_in} {path}")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"k_in={c.k_in} {path}")
 
 
 def test_zero_scale_is_bitwise_noop(decode_case):
     c = decode_case
     dv = Dev(c)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale * 0, c.slice_sizes, dv.meta, dv.y)
-    torch.cuda.synchronize()
+    dv.fused(scale=dv.scale * 0)
     assert np.array_equal(h16(dv.y), dv.y_host)
 
 
@@ -235,38 +242,31 @@ def test_shrink_expand_decode_full(decode_case):
     B.lora_shrink(dv.x, dv.a, dv.scale, dv.meta, xa)
     B.lora_expand(xa, dv.b, c.slice_sizes, dv.meta, dv.y)
     torch.cuda.synchronize()
-    check_y(dv, h16(dv.y), np.arange(c.n), "decode split")
+    check_y(dv, h16(dv.y), None, "decode split")
 
 
 def test_fused_no_reuse_full():
     c = I.no_reuse()
     print("no-reuse full", flush=True)
     dv = Dev(c)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
-    torch.cuda.synchronize()
-    rows = np.random.default_rng(0).choice(c.n, size=96, replace=False)
-    check_y(dv, h16(dv.y), rows, "no-reuse")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, "no-reuse")
 
 
 def test_fused_prefill_full():
     c = I.prefill_sgmv()
     print(f"prefill full n={c.n}", flush=True)
     dv = Dev(c)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, dv.meta, dv.y)
-    torch.cuda.synchronize()
-    y = h16(dv.y)
-    rng = np.random.default_rng(0)
-    # sampled rows: segment boundaries, tile tails and random rows
-    starts = np.concatenate([[0], np.cumsum(c.meta["seq_lens"])])
-    rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1, rng.choice(c.n, 40, replace=False)]))
-    check_y(dv, y, rows, "prefill")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, "prefill", chunk=128)
 
 
 def fused_bits(c: I.DenseCase, slot, a_pool, b_pool, scale, x, y):
     meta = B.lora_meta_build(d32(slot), c.num_slots)
     yd = d16(y)
-    B.lora_delta_fused(d16(x), d16(a_pool), d16(b_pool), d32(scale), c.slice_sizes, meta, yd)
-    torch.cuda.synchronize()
+    ws = B.fused_workspace(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in)
+    B.lora_delta_fused(d16(x), d16(a_pool), d16(b_pool), d32(scale), c.slice_sizes, meta, yd, ws=ws)
+    assert_ws_ok(ws, calls=1)
     return h16(yd)
 
 
@@ -317,6 +317,5 @@ def test_wide_call_with_split_segments(path):
     meta = dv.meta
     n_tiles = int(meta.counts.cpu()[4])
     assert n_tiles == sum(2 if 8 < m < 16 else -(-m // 16) for m in lens)
-    B.lora_delta_fused(dv.x, dv.a, dv.b, dv.scale, c.slice_sizes, meta, dv.y)
-    torch.cuda.synchronize()
-    check_y(dv, h16(dv.y), np.arange(c.n), f"wide split {path}")
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"wide split {path}")

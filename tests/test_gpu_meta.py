@@ -55,7 +55,7 @@ def assert_meta_matches(meta, slot: np.ndarray, S: int):
         assert rec[:6].tolist() == [s, p, k, m, g, jt], (t, rec[:6])
         assert rec[8:8 + k].tolist() == rid
     for t in range(len(exp), bound):
-        assert tiles[t][2] == 0
+        assert not tiles[t][:8].any(), (t, tiles[t][:8])   # unused records: zero header
     # the workspace counters are back to zero
     if meta.ws.numel() >= 8:
         assert meta.ws[:8].view(torch.int32).cpu().tolist() == [0, 0]

@@ -1,7 +1,8 @@
 """GPU parity of moe_lora_gemm1_delta (regular and shared-A forms) against the
-fp64 oracle: per-(token, slot) gate/up deltas, zero rows for unadapted and
-invalid pairs (bitwise), the pair counts, and shared-A == regular when the
-adapters share A."""
+fp64 oracle: per-(token, slot) gate/up deltas on every pair, zero rows for
+unadapted and invalid pairs (bitwise), the pair metadata the call builds in
+its workspace (bit for bit), the workspace control line after every call,
+and shared-A == regular when the adapters share A."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,8 @@ import torch
 from oracle import oracle as O
 from tenant_lora_serving_amd import inputs as I
 from tenant_lora_serving_amd import lora as B
-from gpu_util import assert_close, bf64, d16, d32, h16
+from gpu_util import assert_close, assert_close_chunked, assert_ws_ok, bf64, d16, d32, h16
+from test_gpu_meta import assert_meta_matches
 
 pytestmark = pytest.mark.gpu
 
@@ -25,22 +27,23 @@ def path(request):
 
 
 def device_tables(c: I.MoeCase, shared: bool):
-    """Device banks and FlashInfer-style pointer tables ([2, E] or [E])."""
-    E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
+    """Device banks and FlashInfer-style pointer tables ([2, E] or [E]) from fill_w_ptr."""
     if shared:
         A, Bm = d16(c.a_shared), d16(c.b_fused)
-        ta = torch.tensor([A.data_ptr() + e * L * R * H * 2 for e in range(E)], dtype=torch.int64)
-        tb = torch.tensor([Bm.data_ptr() + e * L * 2 * I_ * R * 2 for e in range(E)], dtype=torch.int64)
-        return (A, Bm), ta.cuda(), R * H, tb.cuda(), 2 * I_ * R
+        (ta, sa), (tb, sb) = B.fill_w_ptr(A), B.fill_w_ptr(Bm)
+        assert (sa, sb) == (c.R * c.H, 2 * c.I * c.R)
+        return (A, Bm), ta, sa, tb, sb
     Ag, Au, Bg, Bu = d16(c.a_gate), d16(c.a_up), d16(c.b_gate), d16(c.b_up)
-    ta = torch.tensor([[M.data_ptr() + e * L * R * H * 2 for e in range(E)] for M in (Ag, Au)],
-                      dtype=torch.int64)
-    tb = torch.tensor([[M.data_ptr() + e * L * I_ * R * 2 for e in range(E)] for M in (Bg, Bu)],
-                      dtype=torch.int64)
-    return (Ag, Au, Bg, Bu), ta.cuda(), R * H, tb.cuda(), I_ * R
+    (ta, sa), (tb, sb) = B.fill_w_ptr(Ag, Au), B.fill_w_ptr(Bg, Bu)
+    assert ta.shape == (2, c.E) and (sa, sb) == (c.R * c.H, c.I * c.R)
+    return (Ag, Au, Bg, Bu), ta, sa, tb, sb
 
 
-def run_moe(c: I.MoeCase, shared: bool, ws=None):
+SENTINEL = 0x40E0   # bf16 bits of 7.0, the fill of `out` before the call
+
+
+def run_moe(c: I.MoeCase, shared: bool, ws=None, calls=None):
+    """One call; returns (out rows [T*top_k, 2I] as bf16 bits, counts, ws)."""
     keep, ta, sa, tb, sb = device_tables(c, shared)
     x = d16(c.x)
     if ws is None:
@@ -48,26 +51,35 @@ def run_moe(c: I.MoeCase, shared: bool, ws=None):
     out = torch.full((c.T, c.top_k, 2 * c.I), 7.0, dtype=torch.bfloat16, device="cuda")
     B.moe_lora_gemm1_delta(x, ta, sa, tb, sb, d32(c.topk_ids), d32(c.lora_ids), c.R, c.I,
                            num_loras=c.L, scale=c.scale, out=out, ws=ws)
-    torch.cuda.synchronize()
+    assert_ws_ok(ws, moe=True, calls=calls)
     del keep
-    return h16(out).reshape(c.T * c.top_k, 2 * c.I), B.moe_counts(ws).cpu().numpy()
+    return h16(out).reshape(c.T * c.top_k, 2 * c.I), B.moe_counts(ws).cpu().numpy(), ws
 
 
-def check_moe(c: I.MoeCase, shared: bool, sample=None, what=""):
+def check_pair_meta(c, ws):
+    """The pair metadata the call built in its workspace equals the oracle's
+    metadata of the (adapter, expert) keys, bit for bit."""
+    keys = O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L)
+    assert_meta_matches(B.moe_meta_view(ws, c.T, c.top_k, c.E, c.L), keys, c.E * c.L)
+
+
+def check_moe(c: I.MoeCase, shared: bool, what="", ws=None, calls=None):
+    """Every pair against the oracle, zero rows bitwise, counts and pair
+    metadata bit-exact, no pair left holding the pre-call fill."""
     print(f"moe case T={c.T} E={c.E} L={c.L} shared={shared} {what}", flush=True)
-    out, counts = run_moe(c, shared)
+    out, counts, ws = run_moe(c, shared, ws, calls)
     n = c.T * c.top_k
     lora = np.repeat(c.lora_ids, c.top_k)
     ex = c.topk_ids.reshape(-1)
     valid = (lora >= 0) & (lora < c.L) & (ex >= 0) & (ex < c.E)
     assert not out[~valid].any(), "pairs without a valid (adapter, expert) must be zero rows"
+    assert not (out[valid] == SENTINEL).all(axis=1).any(), "a routed pair's row was never written"
     keys = O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L)
     _, _, _, ocnt = O.meta_build(keys, c.E * c.L)
     assert counts.tolist() == ocnt.tolist()
-    pairs = np.arange(n) if sample is None else np.unique(np.concatenate([
-        np.flatnonzero(valid)[:: max(1, valid.sum() // sample)], np.flatnonzero(~valid)[:8]]))
-    orc = O.case_moe_pairs(c, shared, pairs)
-    return assert_close(bf64(out[pairs]), orc, f"moe shared={shared} {what}")
+    check_pair_meta(c, ws)
+    return assert_close_chunked(out, lambda p: O.case_moe_pairs(c, shared, p), np.arange(n),
+                                f"moe shared={shared} {what}", chunk=2048)
 
 
 def small_moe(seed, **kw):
@@ -101,8 +113,8 @@ def test_moe_shared_equals_regular_when_a_shared():
     c.a_up[:] = c.a_shared
     c.b_gate[:] = c.b_fused[:, :, :c.I]
     c.b_up[:] = c.b_fused[:, :, c.I:]
-    o_reg, _ = run_moe(c, False)
-    o_sh, _ = run_moe(c, True)
+    o_reg, _, _ = run_moe(c, False)
+    o_sh, _, _ = run_moe(c, True)
     assert_close(bf64(o_reg), bf64(o_sh), "shared vs regular")
 
 
@@ -113,17 +125,43 @@ def moe_case():
 
 @pytest.mark.parametrize("shared", [False, True])
 def test_moe_config_full(moe_case, shared):
-    check_moe(moe_case, shared, sample=400, what="config")
+    check_moe(moe_case, shared, what="config")
 
 
 def test_moe_deterministic(moe_case):
     ws = B.moe_workspace(moe_case.T, moe_case.top_k, moe_case.E, moe_case.L, moe_case.R, moe_case.H)
-    a, _ = run_moe(moe_case, False, ws)
-    b, _ = run_moe(moe_case, False, ws)
+    a, _, _ = run_moe(moe_case, False, ws, calls=1)
+    b, _, _ = run_moe(moe_case, False, ws, calls=2)
     assert np.array_equal(a, b)
 
 
 def test_moe_no_pairs():
     c = small_moe(9, T=0)
-    out, counts = run_moe(c, False)
+    out, counts, _ = run_moe(c, False)
     assert out.size == 0 and counts.tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_moe_pair_metadata_small_split(seed):
+    """At most 1024 pairs: (adapter, expert) segments of 9..15 pairs are cut
+    into two tiles; invalid adapter and expert ids are counted."""
+    c = small_moe(seed, T=60, E=5, top_k=3, L=3)
+    assert c.T * c.top_k <= 1024
+    keys = O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L)
+    lens = np.bincount(keys[(keys >= 0) & (keys < c.E * c.L)], minlength=c.E * c.L)
+    assert ((lens > 8) & (lens < 16)).any(), "the case must hold a segment that is cut in two"
+    check_moe(c, False, what=f"split seed={seed}")
+
+
+def test_moe_workspace_reused_across_shapes(moe_case):
+    """One workspace, calls of different T in turn, each with its own tokens
+    and routing: big, small, big, big.  The control line stays at one place
+    whatever the shape, so every call gets a fresh tag and no call takes an
+    earlier call's partials; each call matches the oracle on every pair."""
+    c = moe_case
+    small = I.make_moe(31, T=70, H=c.H, E=c.E, top_k=c.top_k, I=c.I, R=c.R, L=c.L)
+    big2 = I.make_moe(32, T=c.T, H=c.H, E=c.E, top_k=c.top_k, I=c.I, R=c.R, L=c.L)
+    big3 = I.make_moe(33, T=c.T, H=c.H, E=c.E, top_k=c.top_k, I=c.I, R=c.R, L=c.L)
+    ws = B.moe_workspace(c.T, c.top_k, c.E, c.L, c.R, c.H)
+    for i, case in enumerate([c, small, big2, big3]):
+        check_moe(case, False, what=f"reuse call {i}", ws=ws, calls=i + 1)

@@ -11,7 +11,8 @@ import torch
 from oracle import oracle as O
 from tenant_lora_serving_amd import inputs as I
 from tenant_lora_serving_amd import lora as B
-from gpu_util import assert_close, bf64, d16, d32, h16
+from gpu_util import assert_close, assert_close_chunked, assert_ws_ok, bf64, d16, d32, h16
+from test_gpu_moe import check_pair_meta
 
 pytestmark = pytest.mark.gpu
 
@@ -27,16 +28,16 @@ def path(request):
 
 
 def device_tables(c: I.MoeW2Case):
-    """Device banks and [E] pointer tables: adapter l of expert e starts
-    l * stride elements past entry e."""
-    E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
+    """Device banks and [E] pointer tables from fill_w_ptr: adapter l of expert
+    e starts l * stride elements past entry e."""
     A, Bm = d16(c.a_down), d16(c.b_down)
-    ta = torch.tensor([A.data_ptr() + e * L * R * I_ * 2 for e in range(E)], dtype=torch.int64)
-    tb = torch.tensor([Bm.data_ptr() + e * L * H * R * 2 for e in range(E)], dtype=torch.int64)
-    return (A, Bm), ta.cuda(), R * I_, tb.cuda(), H * R
+    (ta, sa), (tb, sb) = B.fill_w_ptr(A), B.fill_w_ptr(Bm)
+    assert (sa, sb) == (c.R * c.I, c.H * c.R)
+    return (A, Bm), ta, sa, tb, sb
 
 
-def run_w2(c: I.MoeW2Case, weighted: bool, ws=None):
+def run_w2(c: I.MoeW2Case, weighted: bool, ws=None, calls=None):
+    """One call; returns (y rows as bf16 bits, counts, ws)."""
     keep, ta, sa, tb, sb = device_tables(c)
     y = d16(c.y)
     wt = d32(c.topk_weights) if weighted else None
@@ -44,15 +45,17 @@ def run_w2(c: I.MoeW2Case, weighted: bool, ws=None):
         ws = B.moe_w2_workspace(c.T, c.top_k, c.E, c.L, c.R, c.I)
     B.moe_lora_w2_delta(d16(c.x2), ta, sa, tb, sb, d32(c.topk_ids), d32(c.lora_ids), c.R, y,
                         num_loras=c.L, topk_weights=wt, scale=c.scale, ws=ws)
-    torch.cuda.synchronize()
+    assert_ws_ok(ws, moe=True, calls=calls)
     del keep
-    return h16(y), B.moe_counts(ws).cpu().numpy()
+    return h16(y), B.moe_counts(ws).cpu().numpy(), ws
 
 
-def check_w2(c: I.MoeW2Case, weighted: bool, sample=None, what=""):
+def check_w2(c: I.MoeW2Case, weighted: bool, what="", ws=None, calls=None):
+    """Every routed pair against the oracle, unrouted rows bitwise, counts
+    and pair metadata bit-exact."""
     print(f"moe w2 case T={c.T} E={c.E} L={c.L} I={c.I} H={c.H} R={c.R} weighted={weighted} {what}",
           flush=True)
-    out, counts = run_w2(c, weighted)
+    out, counts, ws = run_w2(c, weighted, ws, calls)
     lora = np.repeat(c.lora_ids, c.top_k)
     ex = c.topk_ids.reshape(-1)
     valid = (lora >= 0) & (lora < c.L) & (ex >= 0) & (ex < c.E)
@@ -60,11 +63,9 @@ def check_w2(c: I.MoeW2Case, weighted: bool, sample=None, what=""):
     keys = O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L)
     _, _, _, ocnt = O.meta_build(keys, c.E * c.L)
     assert counts.tolist() == ocnt.tolist()
-    pairs = np.flatnonzero(valid)
-    if sample is not None:
-        pairs = pairs[:: max(1, len(pairs) // sample)]
-    orc = O.case_moe_w2_pairs(c, pairs, weighted)
-    return assert_close(bf64(out[pairs]), orc, f"moe w2 weighted={weighted} {what}")
+    check_pair_meta(c, ws)
+    return assert_close_chunked(out, lambda p: O.case_moe_w2_pairs(c, p, weighted), np.flatnonzero(valid),
+                                f"moe w2 weighted={weighted} {what}", chunk=2048)
 
 
 def small_w2(seed, **kw):
@@ -96,12 +97,12 @@ def test_w2_wide_columns(path):
     # 8000 pairs over 16 keys: about 516 tiles, so the expand units widen to
     # 1024 columns (two 512-column batches, the last unit ragged)
     c = small_w2(4, T=4000, E=4, top_k=2, I=264, H=2056, R=16, L=4, neg_frac=0.05)
-    check_w2(c, True, sample=300, what=f"wide {path}")
+    check_w2(c, True, what=f"wide {path}")
 
 
 def test_w2_no_pairs():
     c = small_w2(5, T=0)
-    out, counts = run_w2(c, True)
+    out, counts, _ = run_w2(c, True)
     assert out.size == 0 and counts.tolist() == [0, 0, 0, 0]
 
 
@@ -109,22 +110,23 @@ def test_w2_single_expert_top1_equals_dense_fused():
     c = small_w2(6, T=130, E=1, top_k=1, L=4, I=520, H=520, R=16, neg_frac=0.2)
     c.lora_ids[c.lora_ids >= c.L] = -1
     c.topk_ids[:] = 0
-    out, _ = run_w2(c, False)
+    out, _, _ = run_w2(c, False)
     a_pool = d16(np.ascontiguousarray(c.a_down[0][:, None]))   # [L, 1, R, I]
     b_pool = d16(np.ascontiguousarray(c.b_down[0]))            # [L, H, R]
     y = d16(c.y)
     meta = B.lora_meta_build(d32(c.lora_ids), c.L)
+    ws = B.fused_workspace(c.T, c.L, 1, c.R, c.I)
     B.lora_delta_fused(d16(c.x2), a_pool, b_pool, torch.full((c.L,), c.scale, device="cuda"), (c.H,),
-                       meta, y)
-    torch.cuda.synchronize()
+                       meta, y, ws=ws)
+    assert_ws_ok(ws, calls=1)
     assert np.array_equal(out, h16(y))
 
 
 def test_w2_unit_weights_equal_unweighted():
     c = small_w2(7, T=200, E=3)
     c.topk_weights[:] = 1.0
-    a, _ = run_w2(c, True)
-    b, _ = run_w2(c, False)
+    a, _, _ = run_w2(c, True)
+    b, _, _ = run_w2(c, False)
     assert np.array_equal(a, b)
 
 
@@ -134,21 +136,28 @@ def w2_case():
 
 
 def test_w2_config_full(w2_case):
-    check_w2(w2_case, True, sample=400, what="config")
+    check_w2(w2_case, True, what="config")
 
 
-def test_w2_deterministic_and_ws_reuse(w2_case):
+def test_w2_deterministic(w2_case):
     c = w2_case
     ws = B.moe_w2_workspace(c.T, c.top_k, c.E, c.L, c.R, c.I)
-    a, _ = run_w2(c, True, ws)
-    small = small_w2(8, T=70, E=c.E, top_k=c.top_k, L=c.L, I=c.I, R=c.R, H=520)
-    check_small = run_w2(small, True, ws)[0]
-    b, _ = run_w2(c, True, ws)
+    a, _, _ = run_w2(c, True, ws, calls=1)
+    b, _, _ = run_w2(c, True, ws, calls=2)
     assert np.array_equal(a, b)
-    lora = np.repeat(small.lora_ids, small.top_k)
-    ex = small.topk_ids.reshape(-1)
-    valid = np.flatnonzero((lora >= 0) & (lora < small.L) & (ex >= 0) & (ex < small.E))
-    assert_close(bf64(check_small[valid]), O.case_moe_w2_pairs(small, valid, True), "small on shared ws")
+
+
+def test_w2_workspace_reused_across_shapes(w2_case):
+    """One workspace, calls of different T in turn, each with its own inputs
+    and routing (big, small, big, big): each matches the oracle on every
+    routed pair, and the control line counts every call with no error."""
+    c = w2_case
+    small = small_w2(8, T=70, E=c.E, top_k=c.top_k, L=c.L, I=c.I, R=c.R, H=c.H)
+    big2 = I.make_moe_w2(34, T=c.T, H=c.H, E=c.E, top_k=c.top_k, I=c.I, R=c.R, L=c.L)
+    big3 = I.make_moe_w2(35, T=c.T, H=c.H, E=c.E, top_k=c.top_k, I=c.I, R=c.R, L=c.L)
+    ws = B.moe_w2_workspace(c.T, c.top_k, c.E, c.L, c.R, c.I)
+    for i, case in enumerate([c, small, big2, big3]):
+        check_w2(case, True, what=f"reuse call {i}", ws=ws, calls=i + 1)
 
 
 def test_w2_reuses_the_gemm1_routing():
@@ -164,18 +173,16 @@ def test_w2_reuses_the_gemm1_routing():
     ws = torch.zeros(max(n1, n2), dtype=torch.uint8, device="cuda")
     # gemm1 on the shared workspace builds the routing
     Ag, Au, Bg, Bu = d16(g.a_gate), d16(g.a_up), d16(g.b_gate), d16(g.b_up)
-    ta = torch.tensor([[M.data_ptr() + e * g.L * g.R * g.H * 2 for e in range(g.E)] for M in (Ag, Au)],
-                      dtype=torch.int64).cuda()
-    tb = torch.tensor([[M.data_ptr() + e * g.L * g.I * g.R * 2 for e in range(g.E)] for M in (Bg, Bu)],
-                      dtype=torch.int64).cuda()
-    B.moe_lora_gemm1_delta(d16(g.x), ta, g.R * g.H, tb, g.I * g.R, d32(g.topk_ids), d32(g.lora_ids), g.R,
+    (ta, sa1), (tb, sb1) = B.fill_w_ptr(Ag, Au), B.fill_w_ptr(Bg, Bu)
+    B.moe_lora_gemm1_delta(d16(g.x), ta, sa1, tb, sb1, d32(g.topk_ids), d32(g.lora_ids), g.R,
                            g.I, num_loras=g.L, ws=ws)
+    assert_ws_ok(ws, moe=True, calls=1)
     keep, wa, sa, wb, sb = device_tables(c)
     y_reuse = d16(c.y)
     B.moe_lora_w2_delta(d16(c.x2), wa, sa, wb, sb, d32(c.topk_ids), d32(c.lora_ids), c.R, y_reuse,
                         num_loras=c.L, topk_weights=d32(c.topk_weights), scale=c.scale, ws=ws,
                         reuse_routing=True)
-    torch.cuda.synchronize()
-    fresh, _ = run_w2(c, True)
+    assert_ws_ok(ws, moe=True, calls=2)
+    fresh, _, _ = run_w2(c, True)
     assert np.array_equal(h16(y_reuse), fresh)
     del keep

@@ -9,7 +9,7 @@ import torch
 from oracle import oracle as O
 from tenant_lora_serving_amd import inputs as I
 from tenant_lora_serving_amd import lora as B
-from gpu_util import assert_close, bf64, d16, d32, h16
+from gpu_util import assert_close, assert_close_chunked, assert_ws_ok, bf64, d16, d32, h16
 
 pytestmark = pytest.mark.gpu
 
@@ -25,13 +25,13 @@ def test_logits_full_vocab(logits_case):
     c = logits_case
     print(f"logits n={c.n} vocab={c.n_out}", flush=True)
     y = d16(c.y)
-    B.add_lora_logits(y, d16(c.x), d16(c.a_pool), d16(c.b_pool), d32(c.scale), d32(c.slot))
-    torch.cuda.synchronize()
+    ws = B.fused_workspace(c.n, c.num_slots, 1, c.max_rank, c.k_in)
+    B.add_lora_logits(y, d16(c.x), d16(c.a_pool), d16(c.b_pool), d32(c.scale), d32(c.slot), ws=ws)
+    assert_ws_ok(ws, calls=1)
     out = h16(y)
     act = (c.slot >= 0) & (c.slot < c.num_slots)
     assert np.array_equal(out[~act], c.y[~act])
-    rows = np.flatnonzero(act)[::4]
-    assert_close(bf64(out[rows]), O.case_fused_rows(c, rows), "logits")
+    assert_close_chunked(out, lambda r: O.case_fused_rows(c, r), np.flatnonzero(act), "logits", chunk=32)
 
 
 def test_logits_small_ragged():
@@ -39,8 +39,9 @@ def test_logits_small_ragged():
     c = I.make_dense(42, n=37, k_in=264, slice_sizes=(32008,), num_slots=5, max_rank=8,
                      slot_kind="uniform_neg")
     y = d16(c.y)
-    B.add_lora_logits(y, d16(c.x), d16(c.a_pool), d16(c.b_pool), d32(c.scale), d32(c.slot))
-    torch.cuda.synchronize()
+    ws = B.fused_workspace(c.n, c.num_slots, 1, c.max_rank, c.k_in)
+    B.add_lora_logits(y, d16(c.x), d16(c.a_pool), d16(c.b_pool), d32(c.scale), d32(c.slot), ws=ws)
+    assert_ws_ok(ws, calls=1)
     assert_close(bf64(h16(y)), O.case_fused_rows(c, np.arange(c.n)), "logits small")
 
 
