@@ -84,7 +84,8 @@ enum {
     LORA_EINVAL = -1,       /* bad pointer, size, alignment or leading dimension */
     LORA_EUNSUPPORTED = -2, /* a shape outside the limits above */
     LORA_EWORKSPACE = -3,   /* workspace or metadata buffer too small */
-    LORA_ELAUNCH = -4       /* the HIP runtime refused a launch */
+    LORA_ELAUNCH = -4,      /* the HIP runtime refused a launch */
+    LORA_ESCRATCH = -5      /* lora_delta_fused_noalloc: the call does not fit the fixed buffer */
 };
 
 /* Byte offsets of the control line in the fused and MoE workspaces. */
@@ -212,6 +213,35 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in,
                      int32_t num_slots, int32_t num_slices, const int32_t *slice_sizes,
                      int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
                      int32_t offset_start, void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the fixed device buffer behind lora_delta_fused_noalloc. */
+#define LORA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * lora_delta_fused without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, result and errors as
+ * lora_delta_fused, whose kernels it runs; the workspace is instead a fixed
+ * buffer of LORA_NOALLOC_SCRATCH_BYTES in device memory that the library
+ * holds on each GPU it runs on until the process ends (zero when loaded).
+ * Nothing is allocated or freed.  Calls whose workspace (as
+ * lora_fused_workspace_bytes gives it) exceeds the buffer return
+ * LORA_ESCRATCH before anything is enqueued; decode-sized batches fit (256
+ * rows, 32 slots, three slices, rank 16, k_in 4096 need about 3 MB).  The
+ * buffer used is the current device's, so `stream` must belong to the
+ * current device (LORA_EINVAL otherwise); the first call on a device
+ * resolves the buffer's address, so make it outside graph capture.  Every
+ * call on one GPU shares that GPU's buffer, and each call finds it as the
+ * last one left it (the control line's call tags keep calls apart, so
+ * nothing is cleared between calls): calls on one GPU must be ordered (one
+ * stream, or streams joined by events); calls that overlap race and give
+ * undefined rows.
+ */
+int lora_delta_fused_noalloc(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in,
+                             const uint16_t *a_pool, const uint16_t *b_pool, const float *scale,
+                             int32_t num_slots, int32_t num_slices, const int32_t *slice_sizes,
+                             int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
+                             int32_t offset_start, void *stream);
 
 /* Workspace bytes moe_lora_gemm1_delta needs. */
 size_t moe_lora_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts,

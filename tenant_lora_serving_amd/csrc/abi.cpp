@@ -194,10 +194,16 @@ size_t lora_fused_workspace_bytes(int32_t n, int32_t num_slots, int32_t num_slic
     return tl::fused_plan(n, num_slots, num_slices, max_rank, k_in, 8).total_bytes;
 }
 
-int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
-                     const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
-                     const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
-                     int32_t offset_start, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused call with its workspace given (ws != null) or, for the
+// allocation-free variant (ws == null), the library's fixed device buffer.
+int fused_call(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
+               const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
+               const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
+               int32_t offset_start, void *ws, size_t ws_bytes, bool own_scratch, void *stream) {
     tl::DenseShape d{};
     if (int rc = dense_shape(d, n, k_in, num_slots, num_slices, slice_sizes, max_rank)) return rc;
     if (int rc = check_x(x, ldx, k_in)) return rc;
@@ -206,8 +212,21 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, co
         return LORA_EINVAL;
     const tl::FusedPlan plan =
         tl::fused_plan(n, num_slots, num_slices, max_rank, k_in, d.slice_off[num_slices]);
-    if (!ws || ws_bytes < plan.total_bytes || !aligned16(ws)) return LORA_EWORKSPACE;
-    if (n == 0) return LORA_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (own_scratch) {
+        if (plan.total_bytes > (size_t)LORA_NOALLOC_SCRATCH_BYTES) return LORA_ESCRATCH;
+        if (n == 0) return LORA_OK;
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return LORA_ELAUNCH;
+        if (st) {  // the buffer resolved is the current device's: the stream must run there
+            hipDevice_t sd = -1;
+            if (hipStreamGetDevice(st, &sd) != hipSuccess || sd != dev) return LORA_EINVAL;
+        }
+        if (tl::noalloc_scratch(dev, &ws) != hipSuccess) return LORA_ELAUNCH;
+    } else {
+        if (!ws || ws_bytes < plan.total_bytes || !aligned16(ws)) return LORA_EWORKSPACE;
+        if (n == 0) return LORA_OK;
+    }
     d.x = x;
     d.ldx = ldx;
     d.a_pool = a_pool;
@@ -216,8 +235,27 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, co
     d.y = y;
     d.ldy = ldy;
     d.offset_start = offset_start;
-    return launched(
-        tl::launch_fused(d, meta.tiles, meta.counts, plan, ws, mfma_min_rows(), static_cast<hipStream_t>(stream)));
+    return launched(tl::launch_fused(d, meta.tiles, meta.counts, plan, ws, mfma_min_rows(), st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
+                     const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
+                     const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
+                     int32_t offset_start, void *ws, size_t ws_bytes, void *stream) {
+    return fused_call(x, ldx, n, k_in, a_pool, b_pool, scale, num_slots, num_slices, slice_sizes, max_rank, meta,
+                      y, ldy, offset_start, ws, ws_bytes, false, stream);
+}
+
+int lora_delta_fused_noalloc(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
+                             const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
+                             const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y,
+                             int64_t ldy, int32_t offset_start, void *stream) {
+    return fused_call(x, ldx, n, k_in, a_pool, b_pool, scale, num_slots, num_slices, slice_sizes, max_rank, meta,
+                      y, ldy, offset_start, nullptr, 0, true, stream);
 }
 
 // MoE workspace: a fixed 256-byte header (counts, 8 int32 at byte 0; the
@@ -373,6 +411,7 @@ const char *lora_status_string(int status) {
     case LORA_EUNSUPPORTED: return "unsupported shape";
     case LORA_EWORKSPACE: return "workspace missing, misaligned or too small";
     case LORA_ELAUNCH: return "kernel launch failed";
+    case LORA_ESCRATCH: return "the call needs more workspace than the library's fixed device buffer holds";
     default: return "unknown status";
     }
 }

@@ -100,6 +100,11 @@ hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *ti
 hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
                         void *ws, int mfma_min, hipStream_t st);
 
+// Address of the library's fixed device buffer (LORA_NOALLOC_SCRATCH_BYTES)
+// on `device`, which must be the current device; resolved on the first call
+// per device, then cached.
+hipError_t noalloc_scratch(int device, void **ptr);
+
 // MoE pairs whose (adapter, expert) is not valid get a zero output row.
 struct ZeroFill {
     const int32_t *topk;

@@ -69,6 +69,10 @@ def lib():
         L.lora_delta_fused.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                        _c_p, _c_i32, _MetaStruct, _c_p, _c_i64, _c_i32, _c_p, _c_sz,
                                        _c_p]
+        L.lora_delta_fused_noalloc.restype = ctypes.c_int
+        L.lora_delta_fused_noalloc.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32,
+                                               _c_i32, _c_p, _c_i32, _MetaStruct, _c_p, _c_i64, _c_i32,
+                                               _c_p]
         L.moe_lora_workspace_bytes.restype = _c_sz
         L.moe_lora_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]
         L.moe_lora_gemm1_delta.restype = ctypes.c_int
@@ -95,7 +99,7 @@ def lib():
 
 EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build",
             "lora_meta_from_offsets", "lora_shrink",
-            "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused",
+            "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused", "lora_delta_fused_noalloc",
             "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "moe_lora_w2_workspace_bytes",
             "moe_lora_w2_delta", "moe_lora_meta_layout", "lora_mfma_min_rows",
             "lora_set_mfma_min_rows", "lora_status_string"]
@@ -306,6 +310,33 @@ def lora_delta_fused(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor
     _check("lora_delta_fused", st)
     if check:
         _check_ws("lora_delta_fused", ws, False, stream)
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # the fixed device buffer behind lora_delta_fused_noalloc
+
+
+def lora_delta_fused_noalloc(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor,
+                             scale: torch.Tensor, slice_sizes, meta: LoraMeta, y: torch.Tensor,
+                             offset_start: int = 0, stream=None) -> torch.Tensor:
+    """lora_delta_fused on the library's own fixed device buffer: no workspace
+    argument, nothing allocated (for callers that cannot allocate).  Calls
+    whose workspace would exceed the buffer raise (status -5)."""
+    _pool_dims(a_pool, b_pool)
+    S, Lsl, R, k_in = a_pool.shape
+    if len(slice_sizes) != Lsl or sum(slice_sizes) != b_pool.shape[1]:
+        raise ValueError("slice sizes do not match the pools")
+    xp, ldx = _rows_ld(x, "x")
+    yp, ldy = _rows_ld(y, "y")
+    n = x.shape[0]
+    if y.shape[0] != n:
+        raise ValueError("x and y row counts differ")
+    ss = (ctypes.c_int32 * Lsl)(*[int(v) for v in slice_sizes])
+    st = lib().lora_delta_fused_noalloc(xp, ldx, n, k_in, _dev(a_pool, "a_pool", torch.bfloat16),
+                                        _dev(b_pool, "b_pool", torch.bfloat16),
+                                        _dev(scale, "scale", torch.float32), S, Lsl, ss, R, meta.struct(),
+                                        yp, ldy, int(offset_start), _stream(stream))
+    _check("lora_delta_fused_noalloc", st)
     return y
 
 

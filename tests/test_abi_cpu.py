@@ -224,3 +224,22 @@ def test_mfma_threshold_is_per_thread(L):
         assert L.lora_mfma_min_rows() == default    # 0 drops the override
     finally:
         L.lora_set_mfma_min_rows(0)
+
+
+def test_noalloc_rejects_oversize_before_any_launch(L):
+    m = _meta()
+    ss = (ctypes.c_int32 * 1)(1024)
+    # 4096 rows, rank 64, k_in 4096: the workspace would exceed the fixed buffer
+    need = L.lora_fused_workspace_bytes(4096, 16, 1, 64, 4096)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    args = [0x1000, 4096, 4096, 4096, 0x2000, 0x3000, 0x4000, 16, 1, ss, 64, m, 0x5000, 1024, 0, None]
+    assert L.lora_delta_fused_noalloc(*args) == -5
+    assert L.lora_status_string(-5) != L.lora_status_string(99)
+    # the same argument checks as lora_delta_fused come first
+    bad = list(args)
+    bad[3] = 4100
+    assert L.lora_delta_fused_noalloc(*bad) == EINVAL
+    zero = list(args)
+    zero[2] = 0
+    zero[10] = 16
+    assert L.lora_delta_fused_noalloc(*zero) == OK   # nothing to do: no device touched
