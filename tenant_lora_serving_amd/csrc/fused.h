@@ -106,6 +106,14 @@ __device__ __forceinline__ int hdr_row(const Hdr &h, int j) {
 }
 
 // ============================================================ shrink units
+// Piece 0's unit zeroes its tile's consumer count with an exchange issued
+// before the unit's loads, and the count must be zero before the tile's first
+// flag is raised.  Using the exchange's result (xo) right after the x tile is
+// staged -- where the loads issued after the exchange are awaited anyway --
+// makes the wave wait for that exchange there and for nothing else later; in
+// particular the flag store does not wait for the unit's partial stores.
+__device__ __forceinline__ void exchange_done(int xo) { asm volatile("" : : "v"(xo)); }
+
 // x rows 0..15 (zero past m), k in [k0, k1), into xs[j * kXS + k - k0]: wave w
 // loads rows w, w+4, w+8, w+12, one coalesced 1 KB row segment each.
 template <class Op>
@@ -132,7 +140,7 @@ __device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpre
 // rb + 4w + rl + 16i (i < RPL) at k = k0 + 128s + 8kl (s < 4).
 template <int RPL, class Op>
 __device__ __forceinline__ void shrink_valu_1(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
-                                            uint64_t *pu, uint32_t tag) {
+                                            uint64_t *pu, uint32_t tag, int xo) {
     const int lane = lane_id(), w = wave_id();
     const int rl = lane >> 4, kl = lane & 15;
     const int n_rr = op.n_rr(), m = h.m;
@@ -156,6 +164,7 @@ __device__ __forceinline__ void shrink_valu_1(const Op &op, const Hdr &h, int k0
         store_x(xv, xs);
         __syncthreads();
     }
+    exchange_done(xo);
     for (int rb = 0; rb < n_rr; rb += 16 * RPL) {
         if (rb > 0) load_a(rb);
         float sv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -202,7 +211,7 @@ __device__ __forceinline__ void shrink_valu_1(const Op &op, const Hdr &h, int k0
 // D[tile row][rank row] = x[16 x 32k] . A^T over 16 steps of 32 k.
 template <class Op>
 __device__ __forceinline__ void shrink_mfma_1(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
-                                            uint64_t *pu, uint32_t tag) {
+                                            uint64_t *pu, uint32_t tag, int xo) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
     const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
@@ -223,11 +232,22 @@ __device__ __forceinline__ void shrink_mfma_1(const Op &op, const Hdr &h, int k0
         store_x(xv, xs);
         __syncthreads();
     }
+    exchange_done(xo);
     for (int g = w; g < G; g += 4) {
         if (g != w) load_a(g);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // x fragments read from LDS four steps at a time: with all sixteen
+        // hoisted ahead of the MFMAs (64 more registers next to the 64 of A in
+        // flight) the kernel would not fit four waves per SIMD
 #pragma unroll
-        for (int s = 0; s < 16; ++s) acc = mfma_16x16x32(lds16(xs + col * kXS + 32 * s + 8 * kq), av[s], acc);
+        for (int s0 = 0; s0 < 16; s0 += 4) {
+            u32x4_t xf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xf[s] = lds16(xs + col * kXS + 32 * (s0 + s) + 8 * kq);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(xf[s], av[s0 + s], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // lane holds D[4kq + i][col]: tile rows 4kq..4kq+3 of rank row rr
         const int rr = 16 * g + col;
         if (rr < n_rr) {
@@ -243,7 +263,7 @@ __device__ __forceinline__ void shrink_mfma_1(const Op &op, const Hdr &h, int k0
 // of the steps added up before they are stored.
 template <int RPL, class Op>
 __device__ __forceinline__ void shrink_valu_n(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
-                                            uint64_t *pu, uint32_t tag) {
+                                            uint64_t *pu, uint32_t tag, int xo) {
     const int lane = lane_id(), w = wave_id();
     const int rl = lane >> 4, kl = lane & 15;
     const int n_rr = op.n_rr(), m = h.m;
@@ -274,6 +294,7 @@ __device__ __forceinline__ void shrink_valu_n(const Op &op, const Hdr &h, int k0
         for (int ks = k0; ks < k1; ks += kKP) {
             const int ke = min(k1, ks + kKP);
             stage(rb, ks, ke, rb > 0 || ks > k0);
+            exchange_done(xo);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 if (4 * b < m) {
@@ -319,7 +340,7 @@ __device__ __forceinline__ void shrink_valu_n(const Op &op, const Hdr &h, int k0
 // D[tile row][rank row] = x[16 x 32k] . A^T over 16 steps of 32 k.
 template <class Op>
 __device__ __forceinline__ void shrink_mfma_n(const Op &op, const Hdr &h, int k0, int k1, uint16_t *xs,
-                                            uint64_t *pu, uint32_t tag) {
+                                            uint64_t *pu, uint32_t tag, int xo) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
     const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
@@ -360,6 +381,7 @@ __device__ __forceinline__ void shrink_mfma_n(const Op &op, const Hdr &h, int k0
         for (int ks = k0; ks < k1; ks += kKP) {
             const int ke = min(k1, ks + kKP);
             stage(g0, ks, ke, ps > 0 || ks > k0);
+            exchange_done(xo);
             if (g0 < G) {
 #pragma unroll
                 for (int s = 0; s < 16; ++s)
@@ -383,7 +405,8 @@ __device__ __forceinline__ void shrink_mfma_n(const Op &op, const Hdr &h, int k0
 // rank-row group w (at most 4 groups).
 template <class Op>
 __device__ __forceinline__ void shrink_mfma_pair(const Op &op, const Hdr &h0, const Hdr &h1, int k0, int k1,
-                                                 uint16_t *xs, uint64_t *pu0, uint64_t *pu1, uint32_t tag) {
+                                                 uint16_t *xs, uint64_t *pu0, uint64_t *pu1, uint32_t tag,
+                                                 int xo) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
     const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
@@ -406,6 +429,7 @@ __device__ __forceinline__ void shrink_mfma_pair(const Op &op, const Hdr &h0, co
         store_x(xv0, xs);
         store_x(xv1, xs1);
         __syncthreads();
+        exchange_done(xo);
         if (w < G) {
 #pragma unroll
             for (int s2 = 0; s2 < 16; ++s2) {
@@ -786,7 +810,7 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
                                             const XaSrc &xs, char *lds) {
     constexpr bool WIDE = WM != 0, PREFETCH = WM == 1;
     const int lane = lane_id(), w = wave_id();
-    const int R = op.R, m = h.m;
+    const int R = Op::kRank ? Op::kRank : op.R, m = h.m;
     const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
     const bool tr = PREFETCH && xs.coalesce_b && R <= 32;
     const uint16_t *bp = nullptr;
@@ -905,7 +929,7 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
                                             const XaSrc &xs, char *lds) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
-    const int R = op.R;
+    const int R = Op::kRank ? Op::kRank : op.R;
     const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
     // D comes out as row = col, columns 16ct + 4kq .. +4; y is read and
     // written row-major (rows 4j + lane/16, 8 bytes per lane) and the two
@@ -1158,8 +1182,16 @@ struct FusedArgs {
 
 // Modes 0 and 2 ask for three waves per SIMD: their registers fit without
 // spills up to rank 64 (mode 1 holds a second batch's B and y and gets two).
+// Mode 0 at a compile-time rank fits four (at most 126 registers), so a
+// decode-sized call's units are all resident from the start.
+template <int WM, int NRS, class Op>
+constexpr int fused_min_waves() {
+    return (WM == 0 && Op::kRank != 0) ? 4 : ((WM != 1 && NRS <= 2) ? 3 : 1);
+}
+
 template <int RPL, int NRS, int WM, class Op>
-__global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kernel(Op op, FusedArgs fa, ZeroFill zf) {
+__global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_kernel(Op op, FusedArgs fa,
+                                                                                     ZeroFill zf) {
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
     constexpr int kLdsShrink = (WM != 0 ? 2 : 1) * kTileRows * kXS * 2;  // wide modes stage tile pairs
     constexpr int kLdsStage = WM == 1 ? 4 * kBStage * 2 : 0, kLdsTile = 4 * kTileRows * kDtStride * 4;
@@ -1196,12 +1228,10 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
                         old = xchg_relaxed(reinterpret_cast<int *>((threadIdx.x == 0 ? fl0 : fl1) + kFlagWords - 1), 0);
                     shrink_mfma_pair(op, h, h1, k0p, k1p, reinterpret_cast<uint16_t *>(lds),
                                      fa.part + ((int64_t)t * P + p) * n_rr * 16,
-                                     fa.part + ((int64_t)(t + 1) * P + p) * n_rr * 16, tag);
+                                     fa.part + ((int64_t)(t + 1) * P + p) * n_rr * 16, tag, old);
                     __syncthreads();
-                    if (threadIdx.x < 2) {
-                        asm volatile("" : : "v"(old) : "memory");  // the exchange has returned
+                    if (threadIdx.x < 2)  // (the exchanges have returned: exchange_done)
                         store_word64((threadIdx.x == 0 ? fl0 : fl1) + p, ((uint64_t)tag << 32) | tag);
-                    }
                     return;
                 }
             }
@@ -1218,22 +1248,22 @@ __global__ __launch_bounds__(kFT, (WM != 1 && NRS <= 2) ? 3 : 1) void fused_kern
             // units of several k steps exist only in the wide modes
             if (h.mseg >= fa.mfma_min) {
                 if (WM != 0 && fa.KS > 1)
-                    shrink_mfma_n(op, h, k0, k1, xs, pu, tag);
+                    shrink_mfma_n(op, h, k0, k1, xs, pu, tag, old);
                 else
-                    shrink_mfma_1(op, h, k0, k1, xs, pu, tag);
+                    shrink_mfma_1(op, h, k0, k1, xs, pu, tag, old);
             } else {
                 if (WM != 0 && fa.KS > 1)
-                    shrink_valu_n<RPL>(op, h, k0, k1, xs, pu, tag);
+                    shrink_valu_n<RPL>(op, h, k0, k1, xs, pu, tag, old);
                 else
-                    shrink_valu_1<RPL>(op, h, k0, k1, xs, pu, tag);
+                    shrink_valu_1<RPL>(op, h, k0, k1, xs, pu, tag, old);
             }
             // raise the flag after every wave has issued its stores (the tags,
-            // not this order, are what make the hand-off correct)
+            // not this order, are what make the hand-off correct); the stores
+            // are not awaited: a consumer that sees the flag before a partial
+            // word re-reads that word until its tag is the call's.  The
+            // exchange has returned (exchange_done).
             __syncthreads();
-            if (threadIdx.x == 0) {
-                asm volatile("" : : "v"(old) : "memory");  // the exchange has returned
-                store_word64(fl + p, ((uint64_t)tag << 32) | tag);
-            }
+            if (threadIdx.x == 0) store_word64(fl + p, ((uint64_t)tag << 32) | tag);
             return;
         }
         const int cc = un.sub;
@@ -1306,22 +1336,32 @@ template <int RPL, int NRS, class Op>
 static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, bool mfma_lean, long long grid, ZeroFill zf,
                                  hipStream_t st) {
     const dim3 g((unsigned)grid), b(kFT);
-    if (fa.EC <= kEB && fa.KS == 1)
+    if constexpr (Op::kRank != 0) {
+        // compile-time ranks serve mode 0 only (the caller checks narrow_call)
         hipLaunchKernelGGL((fused_kernel<RPL, NRS, 0, Op>), g, b, 0, st, op, fa, zf);
-    else if (!mfma_lean)
-        hipLaunchKernelGGL((fused_kernel<RPL, NRS, 1, Op>), g, b, 0, st, op, fa, zf);
-    else
-        hipLaunchKernelGGL((fused_kernel<RPL, NRS, 2, Op>), g, b, 0, st, op, fa, zf);
+    } else {
+        if (fa.EC <= kEB && fa.KS == 1)
+            hipLaunchKernelGGL((fused_kernel<RPL, NRS, 0, Op>), g, b, 0, st, op, fa, zf);
+        else if (!mfma_lean)
+            hipLaunchKernelGGL((fused_kernel<RPL, NRS, 1, Op>), g, b, 0, st, op, fa, zf);
+        else
+            hipLaunchKernelGGL((fused_kernel<RPL, NRS, 2, Op>), g, b, 0, st, op, fa, zf);
+    }
     return hipGetLastError();
 }
 
 template <int RPL, class Op>
 static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, bool mfma_lean, long long grid, ZeroFill zf,
                                  hipStream_t st) {
-    switch (nrs_of(op.R)) {
-    case 1: return launch_fused_t<RPL, 1>(op, fa, mfma_lean, grid, zf, st);
-    case 2: return launch_fused_t<RPL, 2>(op, fa, mfma_lean, grid, zf, st);
-    default: return launch_fused_t<RPL, 4>(op, fa, mfma_lean, grid, zf, st);
+    if constexpr (Op::kRank != 0) {
+        return launch_fused_t<RPL, (Op::kRank <= 32 ? 1 : (Op::kRank <= 64 ? 2 : 4))>(op, fa, mfma_lean, grid, zf,
+                                                                                     st);
+    } else {
+        switch (nrs_of(op.R)) {
+        case 1: return launch_fused_t<RPL, 1>(op, fa, mfma_lean, grid, zf, st);
+        case 2: return launch_fused_t<RPL, 2>(op, fa, mfma_lean, grid, zf, st);
+        default: return launch_fused_t<RPL, 4>(op, fa, mfma_lean, grid, zf, st);
+        }
     }
 }
 
@@ -1369,6 +1409,13 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     case 3: return launch_fused_r<3>(op, fa, mfma_lean, grid, zf, st);
     default: return launch_fused_r<4>(op, fa, mfma_lean, grid, zf, st);
     }
+}
+
+// Mode 0 (one 512-column batch per expand unit, one 512-k step per shrink
+// unit): what launch_fused_op picks for these expand units and this k_in.
+static bool narrow_call(int k_in, int EC) {
+    const int steps = (k_in + kKP - 1) / kKP;
+    return EC <= kEB && steps <= kFlagWords - 1;
 }
 
 static int chunks_of(const int *off, int n_windows, int EC) {

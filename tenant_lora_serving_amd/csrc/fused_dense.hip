@@ -41,9 +41,15 @@ hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t
     const int EC = expand_width(d.slice_off, d.num_slices, plan.tile_bound);
     const int C = chunks_of(d.slice_off, d.num_slices, EC);
     const bool lean = (long long)d.n >= (long long)mfma_min * d.num_slots;
+    const ZeroFill nz{nullptr, nullptr, 1, 1, 1, 0};
     // the control line is the first 256 bytes of the fused workspace
-    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, static_cast<int *>(ws), mfma_min, lean, 1,
-                           ZeroFill{nullptr, nullptr, 1, 1, 1, 0}, 0, st);
+    int *ctl = static_cast<int *>(ws);
+    if (d.R == 16 && narrow_call(d.k_in, EC)) {
+        DenseOpR<16> o16;
+        static_cast<DenseOp &>(o16) = op;
+        return launch_fused_op(o16, tiles, counts, plan, C, EC, ws, ctl, mfma_min, lean, 1, nz, 0, st);
+    }
+    return launch_fused_op(op, tiles, counts, plan, C, EC, ws, ctl, mfma_min, lean, 1, nz, 0, st);
 }
 
 }  // namespace tl

@@ -27,6 +27,7 @@ struct DenseOp {
     int k_in, R, n_sh, n_out, col0, n_sl;
     int off[kMaxSlices + 1];
     static constexpr bool kRowWeights = false;
+    static constexpr int kRank = 0;  // R is a runtime value
 
     __device__ int n_rr() const { return n_sh * R; }
     __device__ int n_xs() const { return n_sl; }
@@ -54,6 +55,20 @@ struct DenseOp {
     __device__ float row_weight(int) const { return 1.f; }
 };
 
+// The dense delta at a rank fixed at compile time (R == RK): decode-sized
+// calls at a common rank, where the fixed rank lets the kernel fit four
+// waves per SIMD.  Same layout and arithmetic as DenseOp.
+template <int RK>
+struct DenseOpR : DenseOp {
+    static constexpr int kRank = RK;
+
+    __device__ int n_rr() const { return n_sh * RK; }
+    __device__ const uint16_t *arow(int slot, int rr) const {
+        return a_pool + ((int64_t)slot * n_sh * RK + rr) * k_in;
+    }
+    __device__ const uint16_t *brow(int slot, int c) const { return b_pool + ((int64_t)slot * n_out + c) * RK; }
+};
+
 // Routed MoE gemm1 (FlashInfer bgmv_moe_gemm1_lora_delta): key = l*E + e,
 // rows are (token, slot) pairs; output window 0 is gate, window 1 is up.
 struct MoeOp {
@@ -68,6 +83,7 @@ struct MoeOp {
     float sc;
     int k_in, R, n_sh, n_out, E, inter, shared;
     static constexpr bool kRowWeights = false;
+    static constexpr int kRank = 0;
 
     __device__ int n_rr() const { return n_sh * R; }
     __device__ int n_xs() const { return 2; }
@@ -112,6 +128,7 @@ struct MoeW2Op {
     float sc;
     int k_in, R, n_sh, n_out, E;
     static constexpr bool kRowWeights = true;
+    static constexpr int kRank = 0;
 
     __device__ int n_rr() const { return R; }
     __device__ int n_xs() const { return 1; }
