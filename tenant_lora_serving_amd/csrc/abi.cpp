@@ -336,8 +336,8 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
     if (n == 0) return LORA_OK;
     tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
                    lora_ids, num_experts, num_loras, rank, inter, scale, out};
-    return launched(tl::launch_moe_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused,
-                                         reinterpret_cast<int *>(b + lay.ctl), mfma_min_rows(), st));
+    return launched(tl::launch_moe_delta(m, mo, lay.plan, b + lay.fused, reinterpret_cast<int *>(b + lay.ctl),
+                                         mfma_min_rows(), st));
 }
 
 size_t moe_lora_w2_workspace_bytes(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras, int32_t rank,

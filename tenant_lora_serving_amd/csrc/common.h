@@ -71,6 +71,25 @@ __device__ __forceinline__ u32x4_t ld16_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
 }
 
+// ---------------------------------------------------------------- buffer addressing
+// A buffer resource spans [base, base + bytes), bytes < 2^31.  A buffer load
+// at an offset outside it returns zero and a store there is dropped, so a
+// masked access is a select of its offset rather than a branch around it
+// (which would also keep the compiler from counting the loads in flight).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufWord3 = 0x00020000;   // descriptor word 3 on gfx9: 32-bit data format
+constexpr uint32_t kOob = 0x80000000u;  // an offset past the end of every resource made here
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- DPP lane sums
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -161,6 +180,21 @@ __device__ __forceinline__ Int3 block_excl_scan3(Int3 v, Int3 *scratch, Int3 &to
     total = scratch[NW];
     __syncthreads();
     return r;
+}
+
+// ---------------------------------------------------------------- workspace control line
+constexpr int kCtlError = 0;  // set when a bounded wait gave up
+constexpr int kCtlGen = 1;    // tag of the last completed call on this workspace (0: none yet)
+constexpr int kCtlDone = 2;   // finished tiles of the running call
+
+// Call tags have the top bit set and never equal 0xFFFFFFFF: they run
+// 0x80000001, 0x80000002, ... 0xFFFFFFFE and start over.  Whatever else a
+// workspace may hold where a later call keeps its flags and partials -- zero
+// fill, or the int32 metadata a MoE call builds in the same workspace (row
+// ids, positions, slots, counts: all in [0, 2^31)) -- can therefore never
+// read as the current call's tag, and neither can an earlier call's tag.
+__device__ __forceinline__ uint32_t next_tag(uint32_t last) {
+    return (last >= 0x80000001u && last < 0xFFFFFFFEu) ? last + 1u : 0x80000001u;
 }
 
 // ---------------------------------------------------------------- device-scope sync

@@ -68,20 +68,6 @@ constexpr int kDtStride = 68;  // fp32 row stride of a wave's 16 x 64 output til
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its units take several k steps
 constexpr int kFlagWords = 64;      // 64-bit words per tile: piece flags, then the finished-consumer count
-// control line of the workspace
-constexpr int kCtlError = 0;  // set when a bounded wait gave up
-constexpr int kCtlGen = 1;    // tag of the last completed call on this workspace (0: none yet)
-constexpr int kCtlDone = 2;   // finished tiles of the running call
-
-// Call tags have the top bit set and never equal 0xFFFFFFFF: they run
-// 0x80000001, 0x80000002, ... 0xFFFFFFFE and start over.  Whatever else a
-// workspace may hold where a later call keeps its flags and partials -- zero
-// fill, or the int32 metadata a MoE call builds in the same workspace (row
-// ids, positions, slots, counts: all in [0, 2^31)) -- can therefore never
-// read as the current call's tag, and neither can an earlier call's tag.
-__device__ __forceinline__ uint32_t next_tag(uint32_t last) {
-    return (last >= 0x80000001u && last < 0xFFFFFFFEu) ? last + 1u : 0x80000001u;
-}
 
 // ============================================================ tile record, per wave
 // Lane i holds word (i mod 32) of the record; the scalar fields are read

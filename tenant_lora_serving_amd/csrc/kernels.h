@@ -128,8 +128,8 @@ struct MoeShape {
     float scale;
     uint16_t *out;
 };
-hipError_t launch_moe_delta(const MoeShape &m, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                            void *ws, int *ctl, int mfma_min, hipStream_t st);
+hipError_t launch_moe_delta(const MoeShape &m, const MetaOut &meta, const FusedPlan &plan, void *ws, int *ctl,
+                            int mfma_min, hipStream_t st);
 
 // Routed-MoE down projection: x2 [n_pairs][I] (ldx), y [n_pairs][H] (ldy) added to.
 struct MoeW2Shape {

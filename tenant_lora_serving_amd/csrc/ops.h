@@ -108,6 +108,59 @@ struct MoeOp {
     __device__ uint16_t *yrow(int pair) const { return out + (int64_t)pair * n_out; }
     __device__ float scale_of(int) const { return sc; }
     __device__ float row_weight(int) const { return 1.f; }
+
+    // The (adapter, expert) matrices of one key, resolved once: table reads
+    // inside a load loop would each be followed by a wait for every load in
+    // flight (the next load's address depends on them).
+    struct Bases {
+        const uint16_t *a[2];
+        const uint16_t *b[2];
+    };
+    __device__ Bases bases(int key) const {
+        const int l = key / E, e = key - l * E;
+        Bases bs;
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            const int ia = shared ? e : sg * E + e;
+            bs.a[sg] = reinterpret_cast<const uint16_t *>(wa[ia]) + (int64_t)l * lsa;
+            bs.b[sg] = reinterpret_cast<const uint16_t *>(wb[ia]) + (int64_t)l * lsb;
+        }
+        return bs;
+    }
+    // rank row rr of the resolved key (rows R.. belong to the up slice)
+    __device__ const uint16_t *arow_b(const Bases &bs, int rr) const {
+        const int sg = rr >= R ? 1 : 0;
+        return bs.a[sg] + (int64_t)(rr - sg * R) * k_in;
+    }
+    // output column c of the resolved key (gate columns 0..I, up I..2I)
+    __device__ const uint16_t *brow_b(const Bases &bs, int c) const {
+        if (shared) return bs.b[0] + (int64_t)c * R;
+        const int sg = c >= inter ? 1 : 0;
+        return bs.b[sg] + (int64_t)(c - sg * inter) * R;
+    }
+
+    // Buffer resources and byte offsets (all extents below 2^31 bytes; the
+    // launcher checks): x rows of n_rows pairs, slice sg of a key's A and B,
+    // the output rows.
+    __device__ rsrc_t x_rsrc(int n_rows) const {
+        return make_rsrc(x, (uint32_t)((int64_t)(n_rows / top_k) * ldx * 2));
+    }
+    __device__ uint32_t x_off(int pair, int k) const {
+        return (uint32_t)(((int64_t)(pair / top_k) * ldx + k) * 2);
+    }
+    __device__ rsrc_t a_rsrc(const Bases &bs, int sg) const {
+        return make_rsrc(bs.a[shared ? 0 : sg], (uint32_t)(R * k_in * 2));
+    }
+    __device__ uint32_t a_off(int r, int k) const { return (uint32_t)((r * k_in + k) * 2); }
+    // window l's B: its own matrix (regular) or rows l*I.. of the fused one
+    __device__ rsrc_t b_rsrc(const Bases &bs, int l) const {
+        return shared ? make_rsrc(bs.b[0], (uint32_t)(2 * inter * R * 2)) : make_rsrc(bs.b[l], (uint32_t)(inter * R * 2));
+    }
+    __device__ uint32_t b_off(int l, int cw, int rk) const {
+        return (uint32_t)(((shared ? l * inter + cw : cw) * R + rk) * 2);
+    }
+    __device__ rsrc_t y_rsrc(int n_rows) const { return make_rsrc(out, (uint32_t)((int64_t)n_rows * n_out * 2)); }
+    __device__ uint32_t y_off(int pair, int col) const { return (uint32_t)(((int64_t)pair * n_out + col) * 2); }
 };
 
 // Routed MoE down projection (vLLM punica_base.py, add_lora_w2): rows are

@@ -1,0 +1,300 @@
+// segment.h -- the routed-MoE gemm1 delta with one workgroup per segment
+// group, for gfx950: shrink and expand of up to 64 pairs of one (adapter,
+// expert) segment in the same workgroup, with no hand-off between
+// workgroups.
+//
+// Semantics (FlashInfer bgmv_moe_gemm1_lora_delta, description and
+// parameters): for every routed pair (t, j) with adapter l and expert e,
+//   out[t][j] = scale * concat(B_gate (A_gate x[t]), B_up (A_up x[t]))
+// (shared-A form: scale * B_fused (A x[t])); pairs are grouped into
+// segments of one (l, e) by the pair metadata (its 16-pair tile records).
+//
+// A segment of the MoE workloads holds a few tens of pairs, so the whole
+// segment fits one workgroup: unit u takes the first 64 pairs of segment u
+// of the pair metadata (sorted_rows[seg_offsets[u] ..]).  Consecutive units,
+// which the hardware hands to the 8 XCDs in turn, are segments of similar
+// size, so every XCD gets its share.  A longer segment's further groups of 64
+// pairs are taken by the units launched after those, one per tile record: the
+// unit of a tile that starts such a group (index 4, 8, ... in its segment)
+// takes that group; every other tile unit returns at once.  In the unit:
+//   shrink  wave w owns tile w's 16 rows (the MFMA M dimension) and every
+//           rank group of 16 rank rows; k runs in stages of 256 with two
+//           stages of loads in flight: each wave's x fragments (the gathered
+//           token rows, loaded in the MFMA operand layout) and the stage's A
+//           rows (loaded coalesced by all threads, 512 contiguous bytes per
+//           row, and handed to every wave through a padded LDS buffer).
+//   xa      scale * the fp32 accumulators, split into bf16 hi + lo terms in
+//           LDS (the bf16 MFMA sees hi + lo = xa to 2^-16 relative).
+//   expand  the 2I output columns in chunks of 64 (four 16-column MFMA
+//           tiles), chunk q on wave q mod 4, B rows read directly in the
+//           operand layout one chunk ahead; each chunk's 16 x 64 block per
+//           tile goes through the wave's LDS tile so that out rows are
+//           written 128 contiguous bytes at a time.
+// Ranks up to 16 fit hi and lo in one 32-wide MFMA k block (lanes of k
+// quarters 0 .. R/8 - 1 carry hi, the next R/8 quarters lo, and the B
+// operand repeats its R ranks); rank 32 takes two MFMAs (hi, then lo).
+// Pairs without a valid (adapter, expert) get zero rows from the zero units
+// after the tile units.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+#include "ops.h"
+
+namespace tl {
+
+constexpr int kSegTiles = 4;              // tiles (of 16 pairs) per segment unit
+constexpr int kSegK = 256;                // k per pipeline stage
+constexpr int kSegAStride = kSegK * 2 + 16;  // bytes per staged A row (padded: conflict-free operand reads)
+constexpr int kSegDt = 68;                // fp32 row stride of a wave's 16 x 64 output tile
+
+struct SegArgs {
+    const int32_t *tiles;
+    int tile_bound;
+    const int32_t *sorted_rows;
+    const int32_t *seg_offsets;
+    const int32_t *seg_slot;
+    const int32_t *counts;  // counts[1]: segments
+    int n_units;            // units before the zero units: the most segments the call can have
+    int n_rows;             // pairs of the call (the metadata's n)
+    int *ctl;               // the workspace's control line (its call tag is advanced)
+};
+
+// bytes of a row of the LDS xa block: for each of nx blocks, hi[R] then lo[R] (bf16), + 16 pad
+__host__ __device__ constexpr int seg_xa_stride(int nx, int R) { return nx * 4 * R + 16; }
+
+template <int G, int RK>
+constexpr int seg_lds_bytes() {
+    constexpr int shrink = 2 * 16 * G * kSegAStride;
+    constexpr int expand = kSegTiles * 16 * seg_xa_stride(2, RK) + 4 * 16 * kSegDt * 4;
+    return shrink > expand ? shrink : expand;
+}
+
+// G: rank groups of 16 rank rows (n_rr <= 16 G); RK: the rank (8, 16 or 32).
+template <int G, int RK, class Op>
+__global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, ZeroFill zf) {
+    static_assert(RK == 8 || RK == 16 || RK == 32, "segment units take ranks 8, 16 and 32");
+    __shared__ __align__(16) char lds[seg_lds_bytes<G, RK>()];
+    const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+    const int c = lane & 15, kq = lane >> 4;
+
+    if ((int)blockIdx.x >= sa.n_units + sa.tile_bound) {
+        // zero rows of pairs that get no delta
+        const int pair = ((int)blockIdx.x - sa.n_units - sa.tile_bound) * 16 + (tid >> 4);
+        if (pair >= zf.n_pairs) return;
+        const int l = zf.lora[pair / zf.top_k], ex = zf.topk[pair];
+        if (l >= 0 && l < zf.L && ex >= 0 && ex < zf.E) return;
+        uint16_t *o = op.yrow(pair);
+        for (int cc = (tid & 15) * 8; cc < op.n_out; cc += 128) st16(o + cc, zero4());
+        return;
+    }
+    if (blockIdx.x == 0 && tid == 0)  // the call's tag, for later calls that share the workspace
+        store_relaxed(sa.ctl + kCtlGen, (int)next_tag((uint32_t)load_relaxed(sa.ctl + kCtlGen)));
+
+    // ---- the unit's group: key, first sorted position, pairs
+    const int u = blockIdx.x;
+    int slot, g_start, mg;
+    if (u < sa.n_units) {
+        if (u >= __builtin_amdgcn_readfirstlane(sa.counts[1])) return;
+        g_start = __builtin_amdgcn_readfirstlane(sa.seg_offsets[u]);
+        mg = min(kSegTiles * 16, __builtin_amdgcn_readfirstlane(sa.seg_offsets[u + 1]) - g_start);
+        slot = __builtin_amdgcn_readfirstlane(sa.seg_slot[u]);
+    } else {
+        const int rec = sa.tiles[(int64_t)(u - sa.n_units) * kTileWords + (lane & 31)];
+        const int jt = __builtin_amdgcn_readlane(rec, kRecSegTile);
+        if (__builtin_amdgcn_readlane(rec, kRecRows) == 0 || jt == 0 || jt % kSegTiles) return;
+        // (such a segment is longer than 64 pairs, so its tiles hold 16 pairs each)
+        slot = __builtin_amdgcn_readlane(rec, kRecSlot);
+        g_start = __builtin_amdgcn_readlane(rec, kRecPos);
+        mg = min(kSegTiles * 16, __builtin_amdgcn_readlane(rec, kRecSegRows) - 16 * jt);
+    }
+    const int K = op.k_in, n_rr = op.n_rr();
+    const auto bs = op.bases(slot);
+    const rsrc_t rx = op.x_rsrc(sa.n_rows), ra0 = op.a_rsrc(bs, 0), ra1 = op.a_rsrc(bs, 1);
+    const int NS = (K + kSegK - 1) / kSegK;
+    const int nt = (mg + 15) / 16;  // the group's tiles of 16 pairs
+    // pair ids: lane holds row (lane & 15) of each tile
+    int pid[kSegTiles];
+#pragma unroll
+    for (int i = 0; i < kSegTiles; ++i) {
+        const int j = 16 * i + c;
+        pid[i] = j < mg ? sa.sorted_rows[g_start + j] : 0;
+    }
+    int mt[kSegTiles];
+#pragma unroll
+    for (int i = 0; i < kSegTiles; ++i) mt[i] = min(16, max(0, mg - 16 * i));
+    // wave w's x row for lane c: tile w, row c (offset past the buffer when absent)
+    int myrow = pid[0];
+#pragma unroll
+    for (int i = 1; i < kSegTiles; ++i) myrow = w == i ? pid[i] : myrow;
+    const bool xrow_ok = 16 * w + c < mg;
+    const uint32_t xo = xrow_ok ? op.x_off(myrow, 0) : kOob;
+
+    // ---- shrink: PD stages of loads in flight (two units per CU leave room
+    // for the registers: at most two waves per SIMD are needed)
+    constexpr int AQ = 2 * G;  // 16-byte A chunks per thread per stage (16 G rows x 512 bytes)
+    constexpr int PD = 2;
+    u32x4_t xr[PD][8], ar[PD][AQ];
+    f32x4_t acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int s, u32x4_t (&xv)[8], u32x4_t (&av)[AQ]) {
+        const int k0 = s * kSegK;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int k = k0 + 32 * ks + 8 * kq;
+            xv[ks] = buf_ld16(rx, k < K ? xo + 2 * k : kOob);
+        }
+        // thread chunk i covers rank rows 8i .. 8i + 7 (one slice: R is a multiple of 8)
+#pragma unroll
+        for (int i = 0; i < AQ; ++i) {
+            const int q = tid + 256 * i, row = q >> 5, k = k0 + 8 * (q & 31);
+            const int sg = (8 * i) / RK;
+            const bool ok = row < n_rr && k < K;
+            av[i] = buf_ld16(sg == 0 ? ra0 : ra1, ok ? op.a_off(row - sg * RK, k) : kOob);
+        }
+    };
+    auto stage = [&](int s, int b, const u32x4_t (&xv)[8], const u32x4_t (&av)[AQ]) {
+        char *abuf = lds + b * 16 * G * kSegAStride;
+        // (every wave finished the compute of stage s - 2, which read this
+        // buffer, before the barrier of stage s - 1)
+#pragma unroll
+        for (int i = 0; i < AQ; ++i) {
+            const int q = tid + 256 * i;
+            st16(abuf + (q >> 5) * kSegAStride + 16 * (q & 31), av[i]);
+        }
+        __syncthreads();
+        if (w < nt) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    acc[g] = mfma_16x16x32(xv[ks], ld16(abuf + (16 * g + c) * kSegAStride + 64 * ks + 16 * kq),
+                                           acc[g]);
+        }
+    };
+    // stage s lives in register slot s % PD and LDS buffer s % 2; the loads of
+    // stage s + PD - 1 go into the slot stage s - 1 has just freed, before
+    // stage s is computed
+#pragma unroll
+    for (int b = 0; b < PD - 1; ++b)
+        if (b < NS) issue(b, xr[b], ar[b]);
+    for (int s0 = 0; s0 < NS; s0 += PD) {
+#pragma unroll
+        for (int b = 0; b < PD; ++b) {
+            const int s = s0 + b;
+            if (s < NS) {
+                if (s + PD - 1 < NS) issue(s + PD - 1, xr[(b + PD - 1) % PD], ar[(b + PD - 1) % PD]);
+                stage(s, s & 1, xr[b], ar[b]);
+            }
+        }
+    }
+
+    // ---- xa = scale * acc as bf16 hi + lo, [row][block][hi R | lo R]
+    constexpr int NX = 2;  // blocks of the LDS row (the shared form uses one)
+    constexpr int XS = seg_xa_stride(NX, RK);
+    __syncthreads();  // every wave is done with the A buffers, which xa and the tiles reuse
+    const float sc = op.scale_of(slot);
+    if (w < nt) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int rr = 16 * g + c;
+            if (rr < n_rr) {
+                const int xb = rr / RK, r = rr - xb * RK;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * w + 4 * kq + i;
+                    const float x = acc[g][i] * sc;
+                    const float hi = bf16_round(x);
+                    uint16_t *xl = reinterpret_cast<uint16_t *>(lds + row * XS) + xb * 2 * RK;
+                    xl[r] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+                    xl[RK + r] = __builtin_bit_cast(uint16_t, (__bf16)(x - hi));
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- expand: chunks of 64 columns of each window, chunk q on wave q % 4
+    float *dt = reinterpret_cast<float *>(lds + kSegTiles * 16 * XS) + w * 16 * kSegDt;
+    const int n_win = op.n_xs();
+    const int W = op.xoff(1) - op.xoff(0);  // window width (I)
+    const int cpw = (W + 63) / 64;          // chunks per window
+    const int n_chunks = n_win * cpw;
+    // the xa operands of every tile for each window block: RK <= 16 packs hi and lo in one k block
+    constexpr int QH = RK / 8;  // k quarters of one term
+    auto xa_op = [&](int rt, int xb, bool lo_term) -> u32x4_t {
+        const uint16_t *xl = reinterpret_cast<const uint16_t *>(lds + (16 * rt + c) * XS) + xb * 2 * RK;
+        if constexpr (RK <= 16) {
+            (void)lo_term;
+            if (kq < QH) return ld16(xl + 8 * kq);
+            if (kq < 2 * QH) return ld16(xl + RK + 8 * (kq - QH));
+            return zero4();
+        } else {
+            return ld16(xl + (lo_term ? RK : 0) + 8 * kq);
+        }
+    };
+    const rsrc_t rb0 = op.b_rsrc(bs, 0), rb1 = op.b_rsrc(bs, 1), ry = op.y_rsrc(sa.n_rows);
+    auto load_b = [&](int q, u32x4_t (&bv)[4]) {
+        const int l = min(q, n_chunks - 1) / cpw, cw0 = 64 * (q - l * cpw);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int cw = cw0 + 16 * ct + c;  // column within window l
+            const int rk = RK <= 16 ? 8 * (kq % QH) : 8 * kq;
+            bv[ct] = buf_ld16(l == 0 ? rb0 : rb1, (q < n_chunks && cw < W) ? op.b_off(l, cw, rk) : kOob);
+        }
+    };
+    // the wave's chunks q = w + 4 j; PB chunks of B in flight (the shrink's
+    // registers are free now)
+    constexpr int PB = 2;
+    u32x4_t bq[PB][4];
+#pragma unroll
+    for (int b = 0; b < PB; ++b) load_b(w + 4 * b, bq[b]);
+    for (int j0 = 0; w + 4 * j0 < n_chunks; j0 += PB) {
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+        const int q = w + 4 * (j0 + b);
+        if (q >= n_chunks) break;
+        u32x4_t cur[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) cur[ct] = bq[b][ct];
+        load_b(q + 4 * PB, bq[b]);  // refill the slot: the chunk PB ahead
+        const int l = q / cpw, col0 = op.xoff(l) + 64 * (q - l * cpw), c1 = op.xoff(l + 1);
+        const int xb = op.xblk(l);
+#pragma unroll
+        for (int rt = 0; rt < kSegTiles; ++rt) {
+            if (rt >= nt) break;
+            f32x4_t d[4];
+            const u32x4_t h0 = xa_op(rt, xb, false);
+            u32x4_t h1 = zero4();
+            if constexpr (RK > 16) h1 = xa_op(rt, xb, true);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                d[ct] = mfma_16x16x32(cur[ct], h0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                if constexpr (RK > 16) d[ct] = mfma_16x16x32(cur[ct], h1, d[ct]);
+            }
+            // lane (c, kq) holds out row c, columns 16 ct + 4 kq .. + 4: through
+            // the wave's tile to rows of 64 columns, 16 lanes x 8 bytes each
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                *reinterpret_cast<f32x4_t *>(dt + c * kSegDt + 16 * ct + 4 * kq) = d[ct];
+            __builtin_amdgcn_wave_barrier();
+            const int rt_pid = rt == 0 ? pid[0] : rt == 1 ? pid[1] : rt == 2 ? pid[2] : pid[3];
+            const int mrt = rt == 0 ? mt[0] : rt == 1 ? mt[1] : rt == 2 ? mt[2] : mt[3];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 4 * j + kq;
+                const f32x4_t o = *reinterpret_cast<const f32x4_t *>(dt + row * kSegDt + 4 * c);
+                const int pr = __shfl(rt_pid, row, kWave);
+                const int col = col0 + 4 * c;
+                buf_st8(ry, (row < mrt && col < c1) ? op.y_off(pr, col) : kOob,
+                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])));
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        }
+    }
+}
+
+}  // namespace tl

@@ -165,3 +165,17 @@ def test_moe_workspace_reused_across_shapes(moe_case):
     ws = B.moe_workspace(c.T, c.top_k, c.E, c.L, c.R, c.H)
     for i, case in enumerate([c, small, big2, big3]):
         check_moe(case, False, what=f"reuse call {i}", ws=ws, calls=i + 1)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_moe_segments_longer_than_64_pairs(shared):
+    """A hot expert: its (adapter, expert) segments run past 64 pairs (their
+    later groups of 64 are taken by further units) while the call averages
+    well under 64 pairs per key, the regime of one workgroup per segment."""
+    c = small_moe(23, T=300, E=8, top_k=2, L=2, H=520, I=72)
+    c.topk_ids[:200, 0] = 0                      # 200 tokens route to expert 0 first
+    c.topk_ids[:200, 1] = np.where(c.topk_ids[:200, 1] == 0, 1, c.topk_ids[:200, 1])
+    keys = O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L)
+    lens = np.bincount(keys[(keys >= 0) & (keys < c.E * c.L)], minlength=c.E * c.L)
+    assert lens.max() > 64 and (keys >= 0).sum() <= 64 * c.E * c.L
+    check_moe(c, shared, what="long segments")
