@@ -19,10 +19,11 @@
 // takes that group; every other tile unit returns at once.  In the unit:
 //   shrink  wave w owns tile w's 16 rows (the MFMA M dimension) and every
 //           rank group of 16 rank rows; k runs in stages of 256 with two
-//           stages of loads in flight: each wave's x fragments (the gathered
-//           token rows, loaded in the MFMA operand layout) and the stage's A
-//           rows (loaded coalesced by all threads, 512 contiguous bytes per
-//           row, and handed to every wave through a padded LDS buffer).
+//           stages of loads in flight in registers: the stage's gathered x
+//           rows and A rows, each loaded coalesced (32 threads per 512-byte
+//           row slice; a load in the MFMA operand layout would touch 16 rows,
+//           so 16 half-used cache lines, per 16 lanes) and handed to the
+//           waves through a padded LDS stage.
 //   xa      scale * the fp32 accumulators, split into bf16 hi + lo terms in
 //           LDS (the bf16 MFMA sees hi + lo = xa to 2^-16 relative).
 //   expand  the 2I output columns in chunks of 64 (four 16-column MFMA
@@ -65,7 +66,7 @@ __host__ __device__ constexpr int seg_xa_stride(int nx, int R) { return nx * 4 *
 
 template <int G, int RK>
 constexpr int seg_lds_bytes() {
-    constexpr int shrink = 2 * 16 * G * kSegAStride;
+    constexpr int shrink = (64 + 16 * G) * kSegAStride;  // one stage of x rows and A rows
     constexpr int expand = kSegTiles * 16 * seg_xa_stride(2, RK) + 4 * 16 * kSegDt * 4;
     return shrink > expand ? shrink : expand;
 }
@@ -123,71 +124,71 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
     int mt[kSegTiles];
 #pragma unroll
     for (int i = 0; i < kSegTiles; ++i) mt[i] = min(16, max(0, mg - 16 * i));
-    // wave w's x row for lane c: tile w, row c (offset past the buffer when absent)
-    int myrow = pid[0];
-#pragma unroll
-    for (int i = 1; i < kSegTiles; ++i) myrow = w == i ? pid[i] : myrow;
-    const bool xrow_ok = 16 * w + c < mg;
-    const uint32_t xo = xrow_ok ? op.x_off(myrow, 0) : kOob;
-
-    // ---- shrink: PD stages of loads in flight (two units per CU leave room
-    // for the registers: at most two waves per SIMD are needed)
+    // ---- shrink.  Stage s covers k in [256 s, 256 s + 256): its x rows (64
+    // at most, 512 bytes each) and its 16 G A rows are loaded coalesced, 32
+    // threads per row, two stages ahead into registers; each stage is written
+    // to the LDS stage (padded rows: the operand reads are free of bank
+    // conflicts) and every wave takes its MFMA operands from there.
     constexpr int AQ = 2 * G;  // 16-byte A chunks per thread per stage (16 G rows x 512 bytes)
-    constexpr int PD = 2;
-    u32x4_t xr[PD][8], ar[PD][AQ];
+    constexpr int XQ = 8;      // 16-byte x chunks per thread per stage (64 rows x 512 bytes)
+    char *xbuf = lds, *abuf = lds + 64 * kSegAStride;
+    // byte offset of this thread's x row of chunk i (row (tid >> 5) + 8 i), or past the buffer
+    uint32_t xo[XQ];
+#pragma unroll
+    for (int i = 0; i < XQ; ++i) {
+        const int row = (tid >> 5) + 8 * i;
+        xo[i] = row < mg ? op.x_off(sa.sorted_rows[g_start + row], 0) : kOob;
+    }
+    u32x4_t xr[2][XQ], ar[2][AQ];
     f32x4_t acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int s, u32x4_t (&xv)[8], u32x4_t (&av)[AQ]) {
-        const int k0 = s * kSegK;
+    auto issue = [&](int s, u32x4_t (&xv)[XQ], u32x4_t (&av)[AQ]) {
+        const int k = s * kSegK + 8 * (tid & 31);
+        const bool kok = k < K;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int k = k0 + 32 * ks + 8 * kq;
-            xv[ks] = buf_ld16(rx, k < K ? xo + 2 * k : kOob);
-        }
+        for (int i = 0; i < XQ; ++i) xv[i] = buf_ld16(rx, kok ? xo[i] + 2 * k : kOob);
         // thread chunk i covers rank rows 8i .. 8i + 7 (one slice: R is a multiple of 8)
 #pragma unroll
         for (int i = 0; i < AQ; ++i) {
-            const int q = tid + 256 * i, row = q >> 5, k = k0 + 8 * (q & 31);
+            const int row = (tid >> 5) + 8 * i;
             const int sg = (8 * i) / RK;
-            const bool ok = row < n_rr && k < K;
-            av[i] = buf_ld16(sg == 0 ? ra0 : ra1, ok ? op.a_off(row - sg * RK, k) : kOob);
+            av[i] = buf_ld16(sg == 0 ? ra0 : ra1, (row < n_rr && kok) ? op.a_off(row - sg * RK, k) : kOob);
         }
     };
-    auto stage = [&](int s, int b, const u32x4_t (&xv)[8], const u32x4_t (&av)[AQ]) {
-        char *abuf = lds + b * 16 * G * kSegAStride;
-        // (every wave finished the compute of stage s - 2, which read this
-        // buffer, before the barrier of stage s - 1)
+    auto stage = [&](const u32x4_t (&xv)[XQ], const u32x4_t (&av)[AQ]) {
+        __syncthreads();  // every wave has computed the previous stage
+        const int off = (tid >> 5) * kSegAStride + 16 * (tid & 31);
 #pragma unroll
-        for (int i = 0; i < AQ; ++i) {
-            const int q = tid + 256 * i;
-            st16(abuf + (q >> 5) * kSegAStride + 16 * (q & 31), av[i]);
-        }
+        for (int i = 0; i < XQ; ++i) st16(xbuf + off + 8 * i * kSegAStride, xv[i]);
+#pragma unroll
+        for (int i = 0; i < AQ; ++i) st16(abuf + off + 8 * i * kSegAStride, av[i]);
         __syncthreads();
+    };
+    auto compute = [&]() {
         if (w < nt) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4_t xf = ld16(xbuf + (16 * w + c) * kSegAStride + 64 * ks + 16 * kq);
 #pragma unroll
                 for (int g = 0; g < G; ++g)
-                    acc[g] = mfma_16x16x32(xv[ks], ld16(abuf + (16 * g + c) * kSegAStride + 64 * ks + 16 * kq),
-                                           acc[g]);
+                    acc[g] = mfma_16x16x32(xf, ld16(abuf + (16 * g + c) * kSegAStride + 64 * ks + 16 * kq), acc[g]);
+            }
         }
     };
-    // stage s lives in register slot s % PD and LDS buffer s % 2; the loads of
-    // stage s + PD - 1 go into the slot stage s - 1 has just freed, before
-    // stage s is computed
-#pragma unroll
-    for (int b = 0; b < PD - 1; ++b)
-        if (b < NS) issue(b, xr[b], ar[b]);
-    for (int s0 = 0; s0 < NS; s0 += PD) {
-#pragma unroll
-        for (int b = 0; b < PD; ++b) {
-            const int s = s0 + b;
-            if (s < NS) {
-                if (s + PD - 1 < NS) issue(s + PD - 1, xr[(b + PD - 1) % PD], ar[(b + PD - 1) % PD]);
-                stage(s, s & 1, xr[b], ar[b]);
-            }
+    // stage s lives in register slot s % 2 until it is written to LDS; the
+    // loads of stage s + 2 then refill that slot while stage s computes
+    issue(0, xr[0], ar[0]);
+    if (NS > 1) issue(1, xr[1], ar[1]);
+    for (int s = 0; s < NS; s += 2) {
+        stage(xr[0], ar[0]);
+        if (s + 2 < NS) issue(s + 2, xr[0], ar[0]);
+        compute();
+        if (s + 1 < NS) {
+            stage(xr[1], ar[1]);
+            if (s + 3 < NS) issue(s + 3, xr[1], ar[1]);
+            compute();
         }
     }
 
