@@ -383,8 +383,8 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, con
     tl::MoeW2Shape m{x2, ldx, T, I, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, top_k, topk_weights,
                      num_experts, num_loras, rank, H, scale, y, ldy};
     return launched(
-        tl::launch_moe_w2_delta(m, mo.tiles, mo.counts, lay.plan, b + lay.fused,
-                                reinterpret_cast<int *>(b + lay.ctl), mfma_min_rows(), st));
+        tl::launch_moe_w2_delta(m, mo, lay.plan, b + lay.fused, reinterpret_cast<int *>(b + lay.ctl),
+                                mfma_min_rows(), st));
 }
 
 int moe_lora_meta_layout(int32_t T, int32_t top_k, int32_t num_experts, int32_t num_loras, size_t *offsets) {

@@ -85,6 +85,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t off) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, off, 0, 0);

@@ -147,7 +147,7 @@ struct MoeW2Shape {
     uint16_t *y;
     int64_t ldy;
 };
-hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const int32_t *tiles, const int32_t *counts,
-                               const FusedPlan &plan, void *ws, int *ctl, int mfma_min, hipStream_t st);
+hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const MetaOut &meta, const FusedPlan &plan, void *ws, int *ctl,
+                               int mfma_min, hipStream_t st);
 
 }  // namespace tl

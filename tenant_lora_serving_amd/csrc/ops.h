@@ -83,6 +83,7 @@ struct MoeOp {
     float sc;
     int k_in, R, n_sh, n_out, E, inter, shared;
     static constexpr bool kRowWeights = false;
+    static constexpr bool kAddInputs = false;  // out is written, not added to
     static constexpr int kRank = 0;
 
     __device__ int n_rr() const { return n_sh * R; }
@@ -200,6 +201,29 @@ struct MoeW2Op {
     __device__ uint16_t *yrow(int pair) const { return y + (int64_t)pair * ldy; }
     __device__ float scale_of(int) const { return sc; }
     __device__ float row_weight(int pair) const { return wt ? wt[pair] : 1.f; }
+
+    static constexpr bool kAddInputs = true;  // y is added to in place
+    // The key's matrices resolved once (see MoeOp::Bases); one slice.
+    struct Bases {
+        const uint16_t *a[1];
+        const uint16_t *b[1];
+    };
+    __device__ Bases bases(int key) const {
+        const int l = key / E, e = key - l * E;
+        Bases bs;
+        bs.a[0] = reinterpret_cast<const uint16_t *>(wa[e]) + (int64_t)l * lsa;
+        bs.b[0] = reinterpret_cast<const uint16_t *>(wb[e]) + (int64_t)l * lsb;
+        return bs;
+    }
+    // buffer resources and byte offsets (extents below 2^31 bytes, checked by the launcher)
+    __device__ rsrc_t x_rsrc(int n_rows) const { return make_rsrc(x, (uint32_t)((int64_t)n_rows * ldx * 2)); }
+    __device__ uint32_t x_off(int pair, int k) const { return (uint32_t)(((int64_t)pair * ldx + k) * 2); }
+    __device__ rsrc_t a_rsrc(const Bases &bs, int) const { return make_rsrc(bs.a[0], (uint32_t)(R * k_in * 2)); }
+    __device__ uint32_t a_off(int r, int k) const { return (uint32_t)((r * k_in + k) * 2); }
+    __device__ rsrc_t b_rsrc(const Bases &bs, int) const { return make_rsrc(bs.b[0], (uint32_t)(n_out * R * 2)); }
+    __device__ uint32_t b_off(int, int cw, int rk) const { return (uint32_t)((cw * R + rk) * 2); }
+    __device__ rsrc_t y_rsrc(int n_rows) const { return make_rsrc(y, (uint32_t)((int64_t)n_rows * ldy * 2)); }
+    __device__ uint32_t y_off(int pair, int col) const { return (uint32_t)(((int64_t)pair * ldy + col) * 2); }
 };
 
 }  // namespace tl

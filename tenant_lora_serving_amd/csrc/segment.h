@@ -1,13 +1,15 @@
-// segment.h -- the routed-MoE gemm1 delta with one workgroup per segment
+// segment.h -- the routed-MoE LoRA deltas with one workgroup per segment
 // group, for gfx950: shrink and expand of up to 64 pairs of one (adapter,
 // expert) segment in the same workgroup, with no hand-off between
 // workgroups.
 //
-// Semantics (FlashInfer bgmv_moe_gemm1_lora_delta, description and
-// parameters): for every routed pair (t, j) with adapter l and expert e,
+// Semantics: for every routed pair (t, j) with adapter l and expert e,
+//  gemm1 (FlashInfer bgmv_moe_gemm1_lora_delta, description and parameters):
 //   out[t][j] = scale * concat(B_gate (A_gate x[t]), B_up (A_up x[t]))
-// (shared-A form: scale * B_fused (A x[t])); pairs are grouped into
-// segments of one (l, e) by the pair metadata (its 16-pair tile records).
+//   (shared-A form: scale * B_fused (A x[t]));
+//  w2 (vLLM punica_base.py, add_lora_w2): y[p] += w[p] * scale * B (A x2[p]),
+//   p = t * top_k + j, w the router weight (or 1).
+// Pairs are grouped into segments of one (l, e) by the pair metadata.
 //
 // A segment of the MoE workloads holds a few tens of pairs, so the whole
 // segment fits one workgroup: unit u takes the first 64 pairs of segment u
@@ -30,7 +32,8 @@
 //           tiles), chunk q on wave q mod 4, B rows read directly in the
 //           operand layout one chunk ahead; each chunk's 16 x 64 block per
 //           tile goes through the wave's LDS tile so that out rows are
-//           written 128 contiguous bytes at a time.
+//           written 128 contiguous bytes at a time (w2: y rows are read
+//           the same way, their loads issued before the chunk's MFMAs).
 // Ranks up to 16 fit hi and lo in one 32-wide MFMA k block (lanes of k
 // quarters 0 .. R/8 - 1 carry hi, the next R/8 quarters lo, and the B
 // operand repeats its R ranks); rank 32 takes two MFMAs (hi, then lo).
@@ -198,6 +201,18 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
     __syncthreads();  // every wave is done with the A buffers, which xa and the tiles reuse
     const float sc = op.scale_of(slot);
     if (w < nt) {
+        // router weights of the wave's rows 4 kq + i (w2)
+        float rw[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (Op::kRowWeights) {
+            int mypid = pid[0];
+#pragma unroll
+            for (int i = 1; i < kSegTiles; ++i) mypid = w == i ? pid[i] : mypid;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pr = __shfl(mypid, 4 * kq + i, kWave);
+                rw[i] = 16 * w + 4 * kq + i < mg ? op.row_weight(pr) : 0.f;
+            }
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int rr = 16 * g + c;
@@ -206,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * w + 4 * kq + i;
-                    const float x = acc[g][i] * sc;
+                    const float x = acc[g][i] * sc * rw[i];
                     const float hi = bf16_round(x);
                     uint16_t *xl = reinterpret_cast<uint16_t *>(lds + row * XS) + xb * 2 * RK;
                     xl[r] = __builtin_bit_cast(uint16_t, (__bf16)hi);
@@ -266,6 +281,19 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
 #pragma unroll
         for (int rt = 0; rt < kSegTiles; ++rt) {
             if (rt >= nt) break;
+            const int rt_pid = rt == 0 ? pid[0] : rt == 1 ? pid[1] : rt == 2 ? pid[2] : pid[3];
+            const int mrt = rt == 0 ? mt[0] : rt == 1 ? mt[1] : rt == 2 ? mt[2] : mt[3];
+            // this row tile's out rows 4 j + kq, columns col0 + 4c .. + 4 (w2: their y, read first)
+            uint32_t yoff[4];
+            uint2 yv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 4 * j + kq, col = col0 + 4 * c;
+                // (the shuffle runs in every lane: a lane it reads from must be active)
+                const int pr = __shfl(rt_pid, row, kWave);
+                yoff[j] = (row < mrt && col < c1) ? op.y_off(pr, col) : kOob;
+                if constexpr (Op::kAddInputs) yv[j] = buf_ld8(ry, yoff[j]);
+            }
             f32x4_t d[4];
             const u32x4_t h0 = xa_op(rt, xb, false);
             u32x4_t h1 = zero4();
@@ -281,16 +309,18 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
             for (int ct = 0; ct < 4; ++ct)
                 *reinterpret_cast<f32x4_t *>(dt + c * kSegDt + 16 * ct + 4 * kq) = d[ct];
             __builtin_amdgcn_wave_barrier();
-            const int rt_pid = rt == 0 ? pid[0] : rt == 1 ? pid[1] : rt == 2 ? pid[2] : pid[3];
-            const int mrt = rt == 0 ? mt[0] : rt == 1 ? mt[1] : rt == 2 ? mt[2] : mt[3];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 4 * j + kq;
                 const f32x4_t o = *reinterpret_cast<const f32x4_t *>(dt + row * kSegDt + 4 * c);
-                const int pr = __shfl(rt_pid, row, kWave);
-                const int col = col0 + 4 * c;
-                buf_st8(ry, (row < mrt && col < c1) ? op.y_off(pr, col) : kOob,
-                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])));
+                float v[4] = {o[0], o[1], o[2], o[3]};
+                if constexpr (Op::kAddInputs) {
+                    v[0] += bf_lo(yv[j].x);
+                    v[1] += bf_hi(yv[j].x);
+                    v[2] += bf_lo(yv[j].y);
+                    v[3] += bf_hi(yv[j].y);
+                }
+                buf_st8(ry, yoff[j], make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
             }
             __builtin_amdgcn_wave_barrier();
         }

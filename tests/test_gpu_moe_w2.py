@@ -106,7 +106,7 @@ def test_w2_no_pairs():
     assert out.size == 0 and counts.tolist() == [0, 0, 0, 0]
 
 
-def test_w2_single_expert_top1_equals_dense_fused():
+def test_w2_single_expert_top1_matches_dense_fused():
     c = small_w2(6, T=130, E=1, top_k=1, L=4, I=520, H=520, R=16, neg_frac=0.2)
     c.lora_ids[c.lora_ids >= c.L] = -1
     c.topk_ids[:] = 0
@@ -119,7 +119,17 @@ def test_w2_single_expert_top1_equals_dense_fused():
     B.lora_delta_fused(d16(c.x2), a_pool, b_pool, torch.full((c.L,), c.scale, device="cuda"), (c.H,),
                        meta, y, ws=ws)
     assert_ws_ok(ws, calls=1)
-    assert np.array_equal(out, h16(y))
+    # one expert at top-1 is the dense delta with the adapter as slot: the two
+    # calls (different kernels, different summation order) agree within the
+    # tolerance, and both match the oracle
+    dense = h16(y)
+    rows = np.flatnonzero((c.lora_ids >= 0) & (c.lora_ids < c.L))
+    assert np.array_equal(out[c.lora_ids < 0], c.y[c.lora_ids < 0])
+    assert np.array_equal(dense[c.lora_ids < 0], c.y[c.lora_ids < 0])
+    orc = O.case_moe_w2_pairs(c, rows, False)
+    assert_close(bf64(out[rows]), orc, "w2 at E=1, top-1")
+    assert_close(bf64(dense[rows]), orc, "dense fused at E=1, top-1")
+    assert_close(bf64(out[rows]), bf64(dense[rows]), "w2 vs dense fused")
 
 
 def test_w2_unit_weights_equal_unweighted():
