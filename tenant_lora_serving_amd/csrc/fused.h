@@ -59,7 +59,6 @@
 namespace tl {
 
 constexpr int kFT = 256;      // threads per workgroup
-constexpr int kKP = 512;      // k per shrink unit
 constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x tile
 constexpr int kXaBytes = kTileRows * kMaxRank * 4;  // LDS for a tile's xa (fp32, or bf16 hi/lo pairs)
 constexpr int kBStage = 128 * 32 + (128 * 32 / 128) * 8;  // bf16 per wave: 128 columns x 32 ranks + padding
@@ -67,7 +66,6 @@ constexpr int kEB = 512;      // output columns per expand batch (128 per wave);
 constexpr int kDtStride = 68;  // fp32 row stride of a wave's 16 x 64 output tile in LDS (64 + 4 pad)
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its units take several k steps
-constexpr int kFlagWords = 64;      // 64-bit words per tile: piece flags, then the finished-consumer count
 
 // ============================================================ tile record, per wave
 // Lane i holds word (i mod 32) of the record; the scalar fields are read

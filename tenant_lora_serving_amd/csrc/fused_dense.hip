@@ -4,23 +4,6 @@
 
 namespace tl {
 
-// Workspace: [control line, 256 B] [per tile: kFlagWords 64-bit words, P piece
-// flags .. the finished-consumer count] [tagged partials: tile_bound x P x n_rr x 16 uint64].
-// Sized for the most pieces any launch of this shape can use: one per 512 k,
-// at most kFlagWords - 1 (launch_fused_op picks the actual count).
-FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out) {
-    (void)n_out;
-    FusedPlan p{};
-    p.tile_bound = tile_bound_of(n, num_slots);
-    const int steps = (k_in + kKP - 1) / kKP;
-    const int ks = std::max(1, (steps + kFlagWords - 2) / (kFlagWords - 1));
-    const int p_max = (steps + ks - 1) / ks;
-    p.flag_bytes = align_up(256 + (size_t)p.tile_bound * kFlagWords * sizeof(uint64_t), 256);
-    p.part_bytes = align_up((size_t)p.tile_bound * p_max * n_sh * R * kTileRows * sizeof(uint64_t), 256);
-    p.total_bytes = p.flag_bytes + p.part_bytes;
-    return p;
-}
-
 hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
                         void *ws, int mfma_min, hipStream_t st) {
     DenseOp op{};

@@ -2,12 +2,15 @@
 // HIP kernels (meta.hip, delta.hip).  Internal to the library.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace tl {
 
+constexpr int kKP = 512;          // k per shrink step of the fused kernel
+constexpr int kFlagWords = 64;    // 64-bit words per tile in the fused workspace: piece flags, then a count
+constexpr int kMetaChunk = 1024;  // rows per workgroup (chunk) of the metadata build
 constexpr int kMaxSlices = 8;
 constexpr int kMaxRank = 128;
 constexpr int kMetaMaxSlotsMulti = 8192;  // slot limit when n spans several 1024-row chunks

@@ -29,7 +29,7 @@
 
 namespace tl {
 
-constexpr int kMT = 1024;  // threads per workgroup = rows per chunk
+constexpr int kMT = kMetaChunk;  // threads per workgroup = rows per chunk
 constexpr int kMetaTable = 16384;  // LDS ints for the assembling workgroup's [chunk][slot] table and slot arrays
 constexpr int kAsmBatch = 8;       // chunks whose entries the assembling workgroup loads at once
 constexpr int kSplitMaxChunks = 64;  // a split build's workgroups each read every chunk's entries
@@ -549,7 +549,6 @@ static bool small_fits(int n, int S) {
 
 static size_t small_lds(int n, int S) { return ((size_t)S * (small_threads(n) / kWave) + 3 * (size_t)S) * sizeof(int); }
 
-int meta_chunks(int n) { return n <= 0 ? 1 : (n + kMT - 1) / kMT; }
 
 size_t meta_dyn_lds(int n, int S) {
     const int c = meta_chunks(n);
