@@ -27,15 +27,17 @@ oracle is timed on the same batch on the host cores (cpu_baseline).
 
 The other workloads (prefill SGMV, one adapter per row, MoE gemm1 regular and
 shared-A, MoE w2 with and without gemm1's routing) print a secondary line of
-the same form for profiling: K calls back to back on the launch stream,
-bracketed by HIP events, inputs rotating over copies worth > 1 GiB where they
-are smaller; no graph, no CPU baseline, traffic null (counters are recorded
-beside the kernel traces instead).
+the same form: the median of K single calls, each after a 1 GiB write that
+evicts the Infinity Cache and the L2s, timed by HIP events on the launch
+stream; the fp64 oracle timed on a bounded sample of the same inputs
+(cpu_baseline, scaled to GB/s over the workload's algorithmic bytes per row
+or pair).
 
-HBM traffic of the fused kernel (roofline.traffic) comes from rocprofv3
-FETCH_SIZE / WRITE_SIZE runs recorded in profiles/fused_decode_traffic.txt,
-scaled by what the same counters read for the plain copy; it is reported only
-while the kernel sources still hash to the recorded value, else null.
+HBM traffic of a workload's main kernel (roofline.traffic) comes from
+rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+profiles/<kernel>_<workload>_traffic.txt, scaled by what the same counters read for a
+plain copy; it is reported only while the kernel sources still hash to the
+recorded value, else null.
 """
 from __future__ import annotations
 
@@ -54,28 +56,31 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "effective HBM GB/s and tokens/sec of routed LoRA delta (% of peak), 1 MI355X"
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_traffic.txt")
-KERNEL_SOURCES = ["common.h", "kernels.h", "ops.h", "fused.h", "fused_dense.hip"]
+KERNEL_DIR = os.path.join(ROOT, "tenant_lora_serving_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source file (so recorded counters match the code)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tenant_lora_serving_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(KERNEL_DIR)):
+        with open(os.path.join(KERNEL_DIR, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(bytes_step: int):
-    """HBM bytes per fused launch from the recorded counter runs, or None when
-    missing or taken on other kernel sources."""
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the workload's main kernel from the recorded
+    counter runs (profiles/<kernel>_<workload>_traffic.txt), or None when missing or
+    taken on other kernel sources."""
+    tag = "fused" if workload in ("decode", "prefill", "no_reuse") else "segment"
+    path = os.path.join(ROOT, "profiles", f"{tag}_{workload}_traffic.txt")
     try:
-        kv = dict(ln.strip().split("=", 1) for ln in open(TRAFFIC_FILE) if "=" in ln and not ln.startswith("#"))
+        kv = dict(ln.strip().split("=", 1) for ln in open(path) if "=" in ln and not ln.startswith("#"))
     except OSError:
         return None
     if kv.get("source_sha256_16") != kernel_source_hash():
         return None
-    return int(float(kv["hbm_bytes_per_launch"]))
+    return {"bytes": int(float(kv["hbm_bytes_per_launch"])), "kernel": kv.get("kernel")}
 
 
 def calibrate_copy():
@@ -134,11 +139,33 @@ def moe_bytes(topk_ids, lora_ids, L, E, a_elems, b_elems, x_row, out_row, out_al
     return int(valid.sum()) * (x_row + out_row) + w
 
 
+def oracle_rate(bytes_per_unit: float, fn, units_per_pass: int, min_s: float, max_s: float, what: str) -> dict:
+    """The fp64 oracle timed on a bounded sample (fn computes units_per_pass
+    rows or pairs), scaled to GB/s over the workload's algorithmic bytes per
+    row or pair."""
+    from oracle import oracle as O
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or el >= max_s:
+            break
+    return {"value": round(bytes_per_unit * units_per_pass * passes / el / 1e9, 4), "unit": "GB/s",
+            "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{what}: {units_per_pass} of them per pass, {passes} passes in {el:.1f} s, "
+                      "rate scaled by the workload's algorithmic bytes per unit"}
+
+
 def secondary(args):
-    """One of the non-headline workloads, timed as K back-to-back calls."""
+    """One of the non-headline workloads: median of single calls, each after a
+    1 GiB write that evicts the Infinity Cache and the L2s (cold), timed by
+    HIP events on the launch stream; the oracle on a bounded sample of the
+    same inputs; HBM traffic of the call's main kernel from recorded counters."""
     import numpy as np
     import torch
 
+    from oracle import oracle as O
     from tenant_lora_serving_amd import inputs as I
     from tenant_lora_serving_amd import lora as B
 
@@ -147,92 +174,110 @@ def secondary(args):
     def d16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
-    def rotate(footprint):
-        return args.copies or max(1, math.ceil((1 << 30) / footprint)) if footprint < (1 << 29) else 1
-
     w = args.workload
     if w in ("prefill", "no_reuse"):
         case = I.prefill_sgmv() if w == "prefill" else I.no_reuse()
         nbytes = algorithmic_bytes(case)
         rows = case.n
-        copies = rotate(case.a_pool.nbytes + case.b_pool.nbytes + case.x.nbytes + case.y.nbytes)
         meta = B.lora_meta_build(torch.from_numpy(case.slot).cuda(), case.num_slots)
         ws = B.fused_workspace(case.n, case.num_slots, case.num_slices, case.max_rank, case.k_in)
         sc = torch.from_numpy(case.scale).cuda()
-        sets = [dict(x=d16(case.x), a=d16(case.a_pool), b=d16(case.b_pool), y=d16(case.y)) for _ in range(copies)]
-        call = lambda s: B.lora_delta_fused(s["x"], s["a"], s["b"], sc, case.slice_sizes, meta, s["y"], ws=ws)
-        kernel = "fused_kernel (shrink + expand)"
+        x, a, b, y = d16(case.x), d16(case.a_pool), d16(case.b_pool), d16(case.y)
+        call = lambda: B.lora_delta_fused(x, a, b, sc, case.slice_sizes, meta, y, ws=ws)  # noqa: E731
+        kernel = "fused_kernel (shrink + expand in one launch)"
         desc = {"workload": case.name, "rows": case.n, "k_in": case.k_in, "slices": list(case.slice_sizes),
                 "num_slots": case.num_slots, "max_rank": case.max_rank,
                 "note": "metadata built once, outside the timed calls"}
+        act = np.flatnonzero((case.slot >= 0) & (case.slot < case.num_slots))
+        sample = act[:: max(1, len(act) // 64)][:64]
+        cpu = lambda: oracle_rate(nbytes / rows, lambda: O.case_fused_rows(case, sample), len(sample),  # noqa
+                                  args.cpu_seconds, 30.0, "rows of the batch (fused delta, fp64)")
     elif w in ("moe", "moe_shared"):
         c = I.moe_gemm1()
         E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
-        if w == "moe_shared":
+        shared = w == "moe_shared"
+        if shared:
             mats = [d16(c.a_shared), d16(c.b_fused)]
-            (ta, _), (tb, sb) = B.fill_w_ptr(mats[0]), B.fill_w_ptr(mats[1])
+            (ta, sa), (tb, sb) = B.fill_w_ptr(mats[0]), B.fill_w_ptr(mats[1])
             a_el, b_el = R * H, 2 * I_ * R
         else:
             mats = [d16(m) for m in (c.a_gate, c.a_up, c.b_gate, c.b_up)]
-            (ta, _), (tb, sb) = B.fill_w_ptr(mats[0], mats[1]), B.fill_w_ptr(mats[2], mats[3])
+            (ta, sa), (tb, sb) = B.fill_w_ptr(mats[0], mats[1]), B.fill_w_ptr(mats[2], mats[3])
             a_el, b_el = 2 * R * H, 2 * I_ * R
         nbytes = moe_bytes(c.topk_ids, c.lora_ids, L, E, a_el, b_el, H * 2, 2 * I_ * 2, True)
-        rows, copies = c.T, 1
+        rows = c.T
         x, tk, lo = d16(c.x), torch.from_numpy(c.topk_ids).cuda(), torch.from_numpy(c.lora_ids).cuda()
         ws = B.moe_workspace(c.T, c.top_k, E, L, R, H)
         out = torch.empty((c.T, c.top_k, 2 * I_), dtype=torch.bfloat16, device="cuda")
-        sets = [None]
-        call = lambda s: B.moe_lora_gemm1_delta(x, ta, R * H, tb, sb, tk, lo, R, I_, num_loras=L,
-                                                scale=c.scale, out=out, ws=ws)
-        kernel = "meta_kernel (pairs) + fused_kernel"
-        desc = {"workload": c.name + (" shared-A" if w == "moe_shared" else " regular"), "tokens": c.T,
+        call = lambda: B.moe_lora_gemm1_delta(x, ta, sa, tb, sb, tk, lo, R, I_, num_loras=L,  # noqa: E731
+                                              scale=c.scale, out=out, ws=ws)
+        kernel = "meta_kernel + meta_assemble_kernel (pair metadata) + segment_kernel"
+        desc = {"workload": c.name + (" shared-A" if shared else " regular"), "tokens": c.T,
                 "pairs": c.T * c.top_k, "note": "one call builds the pair metadata and applies the delta"}
+        pairs = np.arange(0, c.T * c.top_k, 8)[:1024]
+        cpu = lambda: oracle_rate(nbytes / (c.T * c.top_k), lambda: O.case_moe_pairs(c, shared, pairs),  # noqa
+                                  len(pairs), args.cpu_seconds, 30.0, "(token, slot) pairs (gemm1 delta, fp64)")
     elif w in ("w2", "w2_reuse"):
         c = I.moe_w2()
         E, L, R, H, I_ = c.E, c.L, c.R, c.H, c.I
         mats = [d16(c.a_down), d16(c.b_down)]
-        (ta, _), (tb, _) = B.fill_w_ptr(mats[0]), B.fill_w_ptr(mats[1])
+        (ta, sa), (tb, sb) = B.fill_w_ptr(mats[0]), B.fill_w_ptr(mats[1])
         nbytes = moe_bytes(c.topk_ids, c.lora_ids, L, E, R * I_, H * R, I_ * 2, H * 4, False)
-        rows, copies = c.T, 1
+        rows = c.T
         x2, y = d16(c.x2), d16(c.y)
         tk, lo = torch.from_numpy(c.topk_ids).cuda(), torch.from_numpy(c.lora_ids).cuda()
         wt = torch.from_numpy(c.topk_weights).cuda()
         ws = B.moe_w2_workspace(c.T, c.top_k, E, L, R, I_)
         reuse = w == "w2_reuse"
         if reuse:  # the routing of an earlier call on this workspace stands in for gemm1's
-            B.moe_lora_w2_delta(x2, ta, R * I_, tb, H * R, tk, lo, R, y, num_loras=L, topk_weights=wt, ws=ws)
-        sets = [None]
-        call = lambda s: B.moe_lora_w2_delta(x2, ta, R * I_, tb, H * R, tk, lo, R, y, num_loras=L,
-                                             topk_weights=wt, scale=c.scale, ws=ws, reuse_routing=reuse)
-        kernel = "fused_kernel" if reuse else "meta_kernel (pairs) + fused_kernel"
+            B.moe_lora_w2_delta(x2, ta, sa, tb, sb, tk, lo, R, y, num_loras=L, topk_weights=wt, ws=ws)
+        call = lambda: B.moe_lora_w2_delta(x2, ta, sa, tb, sb, tk, lo, R, y, num_loras=L,  # noqa: E731
+                                           topk_weights=wt, scale=c.scale, ws=ws, reuse_routing=reuse)
+        kernel = "segment_kernel" if reuse else "meta_kernel + meta_assemble_kernel + segment_kernel"
         desc = {"workload": c.name + (" reusing gemm1's routing" if reuse else ""), "tokens": c.T,
                 "pairs": c.T * c.top_k}
+        lo_p = np.repeat(c.lora_ids, c.top_k)
+        valid = np.flatnonzero((lo_p >= 0) & (lo_p < L))
+        pairs = valid[:: max(1, len(valid) // 1024)][:1024]
+        cpu = lambda: oracle_rate(nbytes / len(valid), lambda: O.case_moe_w2_pairs(c, pairs, True),  # noqa
+                                  len(pairs), args.cpu_seconds, 30.0, "routed pairs (w2 delta, fp64)")
     else:
         raise SystemExit(f"unknown workload {w!r}")
 
-    for i in range(args.warmup):
-        call(sets[i % len(sets)])
+    for _ in range(args.warmup):
+        call()
     torch.cuda.synchronize()
     K = args.steps
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    times = []
     for i in range(K):
-        call(sets[i % len(sets)])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / K
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    ms = float(np.median(times))
     gbs = nbytes / (ms * 1e-3) / 1e9
-    desc.update({"bytes_per_call": int(nbytes), "input_copies": copies, "mfma_min_rows": B.mfma_min_rows(),
-                 "kernel_sources": kernel_source_hash()})
-    print(json.dumps({
+    desc.update({"bytes_per_call": int(nbytes), "mfma_min_rows": B.mfma_min_rows(),
+                 "kernel_sources": kernel_source_hash(), "timing": "median of single cold calls"})
+    traffic = recorded_traffic(w)
+    res = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded)", "secondary": True,
         "config": desc, "tokens_per_s": round(rows / (ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kernel,
-                     "kernel_us": round(ms * 1e3, 3)}}), flush=True)
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_kernel": traffic["kernel"] if traffic else None,
+                     "kernel": kernel, "call_us": round(ms * 1e3, 3)}}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu()
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -352,7 +397,7 @@ def main():
 
     value = bytes_step * K / wall / 1e9
     fused_gbs = bytes_step / (fused_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(bytes_step)
+    traffic = recorded_traffic("decode")
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -375,8 +420,10 @@ def main():
         "tokens_per_s": round(case.n * K / wall, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "fused_kernel<3, 1, 0, DenseOp>", "kernel_us": round(fused_ms * 1e3, 3)},
+                     "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "kernel": "fused_kernel<3, 1, 0, DenseOpR<16>> (rank-16 decode instantiation)",
+                     "kernel_us": round(fused_ms * 1e3, 3)},
         "meta_kernel_us": round(meta_ms * 1e3, 3),
         "plain_copy_same_bytes": {"us": round(copy_ms * 1e3, 3),
                                   "GB/s": round(2 * half / (copy_ms * 1e-3) / 1e9, 2),
