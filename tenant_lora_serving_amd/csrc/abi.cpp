@@ -272,7 +272,7 @@ struct MoeLayout {
 static_assert(LORA_MOE_CTL_OFFSET >= 8 * sizeof(int32_t) && LORA_MOE_CTL_OFFSET + 64 <= 256 &&
                   LORA_MOE_CTL_OFFSET % 64 == 0,
               "the control line sits in the header, clear of the counts");
-MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int k_in, int n_sh) {
+static MoeLayout moe_layout(int T, int top_k, int E, int L, int R, int k_in, int n_sh) {
     MoeLayout m{};
     const int n = T * top_k, S = L * E, cap = n < S ? n : S;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };

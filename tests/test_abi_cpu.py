@@ -43,6 +43,20 @@ def test_library_exports_every_declared_symbol(L):
     assert sorted(B.EXPORTED) == declared_functions()
 
 
+def test_library_exports_no_other_c_symbols(L):
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm is not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    # unmangled text symbols are the C entry points (the host build's launcher
+    # stand-ins add stub_* and the two HIP runtime calls it replaces)
+    c_syms = {s for s in syms if not s.startswith(("_Z", "stub_", "hipGetDevice", "hipStreamGetDevice"))}
+    assert sorted(c_syms) == declared_functions()
+
+
 def test_tile_bound_and_workspace_sizes(L):
     assert L.lora_meta_max_tiles(0, 4) == 0
     assert L.lora_meta_max_tiles(8, 4) == 5          # ceil(8/16) + min(8, 4) + 0 split segments
