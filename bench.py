@@ -14,8 +14,10 @@ that no step finds its adapters in the 256 MB Infinity Cache.
 Timed region: exactly K steps, replayed from one HIP graph, bracketed by
 torch.cuda.synchronize().  value = algorithmic bytes of the K steps / wall
 time (GB/s).  The fused kernel's own average duration is measured with two
-HIP events on the launch stream bracketing a second region of K back-to-back
-eager launches (elapsed / K); it gives the roofline fraction against 8 TB/s.
+HIP events on the launch stream bracketing the replay of a graph of K
+back-to-back launches of that kernel alone (elapsed / K; a graph, so that the
+host's launch rate cannot set the pace); it gives the roofline fraction
+against 8 TB/s.
 The metadata kernel is timed the same way, and so is a plain device copy
 moving the same number of bytes (plain_copy_same_bytes: what the memory
 system gives a transfer of this size, next to the kernel).  The fp64 CPU
@@ -357,43 +359,40 @@ def main():
     ms_step = wall * 1e3 / K
 
     # ---- kernel durations: HIP events on the launch stream bracketing K
-    # back-to-back launches of one kernel (the metadata is built beforehand)
+    # back-to-back launches of one kernel (the metadata is built beforehand),
+    # replayed from a graph so that the host's launch rate cannot set the pace
     B.lora_meta_build(sets[0]["slot"], case.num_slots, sets[0]["meta"])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def region(launch):
+    def region(launch, items):
+        for i in range(3):
+            launch(items[i % len(items)])
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(K):
+                launch(items[i % len(items)])
+        gr.replay()  # graph upload
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(K):
-            launch(sets[i % copies])
+        gr.replay()
         e1.record(stream)
         torch.cuda.synchronize()
+        del gr
         return e0.elapsed_time(e1) / K
 
     fused_ms = region(lambda s: B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes,
-                                                   s["meta"], s["y"], ws=s["ws"]))
-    meta_ms = region(lambda s: B.lora_meta_build(s["slot"], case.num_slots, s["meta"]))
+                                                   s["meta"], s["y"], ws=s["ws"]), sets)
+    meta_ms = region(lambda s: B.lora_meta_build(s["slot"], case.num_slots, s["meta"]), sets)
     # what a plain device copy moving the same bytes (half read, half written)
     # takes when timed the same way, rotating over as many buffers
     half = bytes_step // 2
     bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1),
              torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(copies)]
-    cbufs = [{"src": a_, "dst": b_} for a_, b_ in bufs]
-
-    def copy_region():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(K):
-            c_ = cbufs[i % copies]
-            c_["dst"].copy_(c_["src"])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
-
-    copy_region()
-    copy_ms = copy_region()
-    del bufs, cbufs
+    copy_ms = region(lambda c_: c_[1].copy_(c_[0]), bufs)
+    del bufs
 
     value = bytes_step * K / wall / 1e9
     fused_gbs = bytes_step / (fused_ms * 1e-3) / 1e9
@@ -428,7 +427,8 @@ def main():
         "plain_copy_same_bytes": {"us": round(copy_ms * 1e3, 3),
                                   "GB/s": round(2 * half / (copy_ms * 1e-3) / 1e9, 2),
                                   "note": "device copy of half the step's bytes (read + write = the step's "
-                                          "bytes), K launches bracketed by events, buffers rotated"},
+                                          "bytes), K copies replayed from a graph bracketed by events, "
+                                          "buffers rotated"},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(case, bytes_step, args.cpu_seconds, 30.0)

@@ -433,21 +433,29 @@ __device__ __forceinline__ void shrink_mfma_pair(const Op &op, const Hdr &h0, co
 }
 
 // ============================================================ expand units
-// Wait until pieces [0, P) of the tile carry this call's tag (threads p < P
-// poll flag p with relaxed loads); false if a bounded wait gave up.  A flag is
-// the word {tag, tag}: whatever an earlier call of another layout left at its
-// address (a flag, or a partial word {value, older tag}) has an older tag in
-// its upper half.
+// Wait until all but at most one of pieces [0, P) of the tile carry this
+// call's tag (wave 0 polls the P <= 63 flags, lane p flag p, with relaxed
+// loads); false if a bounded wait gave up.  The staging that follows reads
+// every piece's partial words and re-reads a word until it shows the tag, so
+// the last piece to finish is awaited on its data: one round trip after it
+// lands instead of two (its flag, then its words).  A flag is the word
+// {tag, tag}: whatever an earlier call of another layout left at its address
+// (a flag, or a partial word {value, older tag}) has an older tag in its
+// upper half.
 __device__ __forceinline__ bool wait_pieces(const uint64_t *flags, int P, uint32_t tag, int *ctl, int *ok_lds) {
     if (threadIdx.x == 0) *ok_lds = 1;
-    __syncthreads();
-    for (int p = threadIdx.x; p < P; p += kFT) {
+    if (wave_id() == 0) {
+        const int lane = lane_id(), need = P > 1 ? P - 1 : P;
         int spins = 0;
-        while ((uint32_t)(load_word64(flags + p) >> 32) != tag) {
+        while (true) {
+            const bool done = lane < P && (uint32_t)(load_word64(flags + lane) >> 32) == tag;
+            if (__popcll(__ballot(done)) >= need) break;
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
-                atomicExch(ctl + kCtlError, 1);
-                *ok_lds = 0;
+                if (lane == 0) {
+                    atomicExch(ctl + kCtlError, 1);
+                    *ok_lds = 0;
+                }
                 break;
             }
         }
@@ -1221,8 +1229,9 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
             }
             uint64_t *fl = fa.flags + (int64_t)t * kFlagWords;
             // piece 0 zeroes the tile's consumer count (whatever an earlier
-            // call left there); the exchange returns before its flag is
-            // stored, and every consumer counts only after seeing that flag
+            // call left there); the exchange returns before its flag and its
+            // partials are stored, and every consumer counts only after seeing
+            // one of them
             int old = 0;
             if (p == 0 && threadIdx.x == 0) old = xchg_relaxed(reinterpret_cast<int *>(fl + kFlagWords - 1), 0);
             // (k0 written as a multiple of kKP: the loads' addressing depends on it)
