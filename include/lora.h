@@ -214,6 +214,31 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in,
                      int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
                      int32_t offset_start, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The routing metadata and the fused delta in one call (vLLM punica_base.py:
+ * the wrapper's metadata update for the step, then add_lora_linear; metrale
+ * lora_delta docs, apply_lora_bgmv): meta is written exactly as
+ * lora_meta_build(slot, n, num_slots, meta, ...) writes it, so that later
+ * calls of the same step (the other LoRA layers) can pass it to
+ * lora_delta_fused, and y is updated exactly as lora_delta_fused(..., meta,
+ * ...) would update it.  Batches of at most 256 rows over at most 64 slots
+ * whose call runs one 512-column batch per expand unit (decode-sized; the
+ * Llama-3-8B QKV shape at rank 16 is one) do both in one launch: each
+ * workgroup of the delta derives its own tile's record from slot, and one
+ * more workgroup writes meta.  Other batches run the metadata kernel, then
+ * the fused kernel.  ws must hold lora_fused_workspace_bytes(n, num_slots,
+ * num_slices, max_rank, k_in) + lora_meta_workspace_bytes(n, num_slots)
+ * bytes (the metadata build's part after the fused part); it carries the
+ * fused control line at its start as for lora_delta_fused, and the same
+ * workspace may be passed to either call.  Errors as for lora_meta_build and
+ * lora_delta_fused (slot may be null only when n == 0).
+ */
+int lora_delta_fused_build(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in,
+                           const uint16_t *a_pool, const uint16_t *b_pool, const float *scale,
+                           int32_t num_slots, int32_t num_slices, const int32_t *slice_sizes,
+                           int32_t max_rank, const int32_t *slot, lora_meta_t meta, uint16_t *y,
+                           int64_t ldy, int32_t offset_start, void *ws, size_t ws_bytes, void *stream);
+
 /* Bytes of the fixed device buffer behind lora_delta_fused_noalloc. */
 #define LORA_NOALLOC_SCRATCH_BYTES (16u << 20)
 

@@ -200,10 +200,14 @@ namespace {
 
 // The fused call with its workspace given (ws != null) or, for the
 // allocation-free variant (ws == null), the library's fixed device buffer.
+// build (lora_delta_fused_build): the call builds meta from slot too,
+// in the fused launch itself where fused_builds_meta allows, else with the
+// metadata kernel first (its workspace carved after the fused workspace).
 int fused_call(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
                const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
                const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
-               int32_t offset_start, void *ws, size_t ws_bytes, bool own_scratch, void *stream) {
+               int32_t offset_start, void *ws, size_t ws_bytes, bool own_scratch, bool build,
+               const int32_t *slot, void *stream) {
     tl::DenseShape d{};
     if (int rc = dense_shape(d, n, k_in, num_slots, num_slices, slice_sizes, max_rank)) return rc;
     if (int rc = check_x(x, ldx, k_in)) return rc;
@@ -213,6 +217,29 @@ int fused_call(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const ui
     const tl::FusedPlan plan =
         tl::fused_plan(n, num_slots, num_slices, max_rank, k_in, d.slice_off[num_slices]);
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (build) {
+        if (int rc = check_meta_shape(n, num_slots)) return rc;
+        if (n > 0 && !slot) return LORA_EINVAL;
+        const size_t need = plan.total_bytes + meta_ws_bytes(n, num_slots);
+        if (!ws || ws_bytes < need || !aligned16(ws)) return LORA_EWORKSPACE;
+        tl::MetaOut mo{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
+                       tile_bound(n, num_slots)};
+        void *meta_ws = static_cast<char *>(ws) + plan.total_bytes;
+        if (n == 0) return launched(tl::launch_meta_dense(slot, n, num_slots, mo, carve_meta_ws(meta_ws, n), st));
+        d.x = x;
+        d.ldx = ldx;
+        d.a_pool = a_pool;
+        d.b_pool = b_pool;
+        d.scale = scale;
+        d.y = y;
+        d.ldy = ldy;
+        d.offset_start = offset_start;
+        if (tl::fused_builds_meta(d, plan))
+            return launched(tl::launch_fused(d, nullptr, nullptr, plan, ws, mfma_min_rows(), st, slot, &mo));
+        const hipError_t e = tl::launch_meta_dense(slot, n, num_slots, mo, carve_meta_ws(meta_ws, n), st);
+        if (e != hipSuccess) return LORA_ELAUNCH;
+        return launched(tl::launch_fused(d, meta.tiles, meta.counts, plan, ws, mfma_min_rows(), st));
+    }
     if (own_scratch) {
         if (plan.total_bytes > (size_t)LORA_NOALLOC_SCRATCH_BYTES) return LORA_ESCRATCH;
         if (n == 0) return LORA_OK;
@@ -247,7 +274,7 @@ int lora_delta_fused(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, co
                      const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y, int64_t ldy,
                      int32_t offset_start, void *ws, size_t ws_bytes, void *stream) {
     return fused_call(x, ldx, n, k_in, a_pool, b_pool, scale, num_slots, num_slices, slice_sizes, max_rank, meta,
-                      y, ldy, offset_start, ws, ws_bytes, false, stream);
+                      y, ldy, offset_start, ws, ws_bytes, false, false, nullptr, stream);
 }
 
 int lora_delta_fused_noalloc(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
@@ -255,7 +282,16 @@ int lora_delta_fused_noalloc(const uint16_t *x, int64_t ldx, int32_t n, int32_t 
                              const int32_t *slice_sizes, int32_t max_rank, lora_meta_t meta, uint16_t *y,
                              int64_t ldy, int32_t offset_start, void *stream) {
     return fused_call(x, ldx, n, k_in, a_pool, b_pool, scale, num_slots, num_slices, slice_sizes, max_rank, meta,
-                      y, ldy, offset_start, nullptr, 0, true, stream);
+                      y, ldy, offset_start, nullptr, 0, true, false, nullptr, stream);
+}
+
+int lora_delta_fused_build(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
+                           const uint16_t *b_pool, const float *scale, int32_t num_slots, int32_t num_slices,
+                           const int32_t *slice_sizes, int32_t max_rank, const int32_t *slot, lora_meta_t meta,
+                           uint16_t *y, int64_t ldy, int32_t offset_start, void *ws, size_t ws_bytes,
+                           void *stream) {
+    return fused_call(x, ldx, n, k_in, a_pool, b_pool, scale, num_slots, num_slices, slice_sizes, max_rank, meta,
+                      y, ldy, offset_start, ws, ws_bytes, false, true, slot, stream);
 }
 
 // MoE workspace: a fixed 256-byte header (counts, 8 int32 at byte 0; the

@@ -53,6 +53,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "ops.h"
+#include "slot_meta.h"
 
 #include <algorithm>
 
@@ -62,7 +63,6 @@ constexpr int kFT = 256;      // threads per workgroup
 constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x tile
 constexpr int kXaBytes = kTileRows * kMaxRank * 4;  // LDS for a tile's xa (fp32, or bf16 hi/lo pairs)
 constexpr int kBStage = 128 * 32 + (128 * 32 / 128) * 8;  // bf16 per wave: 128 columns x 32 ranks + padding
-constexpr int kEB = 512;      // output columns per expand batch (128 per wave); a unit has 1, 2 or 4
 constexpr int kDtStride = 68;  // fp32 row stride of a wave's 16 x 64 output tile in LDS (64 + 4 pad)
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its units take several k steps
@@ -75,14 +75,17 @@ struct Hdr {
     int slot, pos0, m, mseg;
 };
 
-__device__ __forceinline__ Hdr load_hdr(const int32_t *tiles, int t) {
+__device__ __forceinline__ Hdr hdr_of_word(int word) {
     Hdr h;
-    h.rec = tiles[(int64_t)t * kTileWords + (lane_id() & 31)];
+    h.rec = word;
     h.slot = __builtin_amdgcn_readlane(h.rec, kRecSlot);
     h.pos0 = __builtin_amdgcn_readlane(h.rec, kRecPos);
     h.m = __builtin_amdgcn_readlane(h.rec, kRecRows);
     h.mseg = __builtin_amdgcn_readlane(h.rec, kRecSegRows);
     return h;
+}
+__device__ __forceinline__ Hdr load_hdr(const int32_t *tiles, int t) {
+    return hdr_of_word(tiles[(int64_t)t * kTileWords + (lane_id() & 31)]);
 }
 // original row id of tile row j; j must be wave-uniform
 __device__ __forceinline__ int hdr_row(const Hdr &h, int j) {
@@ -1170,6 +1173,12 @@ struct FusedArgs {
     int *ctl;        // control line
     uint64_t *flags;  // [tile_bound][kFlagWords]: piece flags, then the tile's finished consumers
     int mfma_min, add_inputs;
+    // metadata built in the same launch (Op::kBuild: mode 0, small batches):
+    // each unit derives its tile's record from the slot array, and the last
+    // workgroup writes the whole metadata to meta_out
+    const int32_t *slot;
+    int n_rows, n_slots;
+    MetaOut meta_out;
 };
 
 // Modes 0 and 2 ask for three waves per SIMD: their registers fit without
@@ -1190,18 +1199,35 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
     constexpr int kLdsExpand =  // wide modes at rank <= 32 stage the xa of tile pairs
         (WM != 0 && NRS == 1 ? 2 : 1) * kXaBytes + (kLdsStage > kLdsTile ? kLdsStage : kLdsTile);
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
+    static_assert(sizeof(lds) >= (kSmallBallotSlots * (kFT / kWave + 3) + kTileWords + 1) * sizeof(int) +
+                                     (kFT / kWave + 1) * sizeof(Int3) + 2 * sizeof(int),
+                  "the in-launch metadata build fits the unit LDS");
     __shared__ int ok;
     __shared__ float rw[Op::kRowWeights ? 2 * kTileRows : 1];
     const int P = fa.P, C = fa.C;
     const int n_rr = op.n_rr();
+    if (Op::kBuild && blockIdx.x == gridDim.x - 1) {
+        // the batch's metadata, as the metadata kernel writes it (no unit of
+        // this launch reads it: it is for later calls that reuse it)
+        int *sm = reinterpret_cast<int *>(lds);
+        Int3 *scan3 = reinterpret_cast<Int3 *>(sm + fa.n_slots * (kFT / kWave + 3));
+        small_meta_build<kFT>(SlotSrcDense{fa.slot}, fa.n_rows, fa.n_slots, fa.meta_out, sm, scan3,
+                              reinterpret_cast<int *>(scan3 + kFT / kWave + 1));
+        return;
+    }
     const Unit un = unit_of(blockIdx.x, fa.tile_bound, P, C);
     if (un.kind == kUnitShrink || un.kind == kUnitExpand) {
         const int t = un.t;
         if (t >= fa.tile_bound) return;
         const uint32_t tag = next_tag((uint32_t)load_relaxed(fa.ctl + kCtlGen));
+        int slot_tiles = 0;
+        int slot_word = 0;
+        if constexpr (Op::kBuild)
+            slot_word = slot_tile_record(fa.slot, fa.n_rows, fa.n_slots, t, reinterpret_cast<int *>(lds), slot_tiles);
+        auto tile_hdr = [&]() { return Op::kBuild ? hdr_of_word(slot_word) : load_hdr(fa.tiles, t); };
         if (un.kind == kUnitShrink) {
             const int p = un.sub;
-            const Hdr h = load_hdr(fa.tiles, t);
+            const Hdr h = tile_hdr();
             if (h.m == 0) return;
             const int k0p = (p * fa.KS) * kKP, k1p = min(op.k_in, k0p + fa.KS * kKP);
             // wide calls: MFMA segments with at most 64 rank rows are shrunk two
@@ -1260,8 +1286,8 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
             return;
         }
         const int cc = un.sub;
-        const int n_tiles = fa.counts[4];
-        const Hdr h = load_hdr(fa.tiles, t);
+        const int n_tiles = Op::kBuild ? slot_tiles : fa.counts[4];
+        const Hdr h = tile_hdr();
         if (h.m == 0) return;
         int l, c0, c1;
         chunk_of(op, cc, fa.EC, l, c0, c1);
@@ -1329,8 +1355,9 @@ template <int RPL, int NRS, class Op>
 static hipError_t launch_fused_t(const Op &op, const FusedArgs &fa, bool mfma_lean, long long grid, ZeroFill zf,
                                  hipStream_t st) {
     const dim3 g((unsigned)grid), b(kFT);
-    if constexpr (Op::kRank != 0) {
-        // compile-time ranks serve mode 0 only (the caller checks narrow_call)
+    if constexpr (Op::kRank != 0 || Op::kBuild) {
+        // compile-time ranks and in-launch metadata serve mode 0 only (the
+        // callers check narrow_call)
         hipLaunchKernelGGL((fused_kernel<RPL, NRS, 0, Op>), g, b, 0, st, op, fa, zf);
     } else {
         if (fa.EC <= kEB && fa.KS == 1)
@@ -1360,10 +1387,19 @@ static hipError_t launch_fused_r(const Op &op, const FusedArgs &fa, bool mfma_le
 
 // mfma_lean: the call averages at least mfma_min rows per slot, so most of
 // its tiles are expected on the MFMA path (selects expand mode 2 over 1).
+// In-launch metadata (FusedArgs::slot): the slot array, its shape and the
+// caller's metadata arrays; null: the tile records come from tiles.
+struct SlotBuild {
+    const int32_t *slot;
+    int n, S;
+    MetaOut out;
+};
+
 template <class Op>
 static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
                                   int C, int EC, void *ws, int *ctl, int mfma_min, bool mfma_lean,
-                                  int add_inputs, ZeroFill zf, int zero_units, hipStream_t st) {
+                                  int add_inputs, ZeroFill zf, int zero_units, hipStream_t st,
+                                  const SlotBuild *sb = nullptr) {
     char *w = static_cast<char *>(ws);
     FusedArgs fa{};
     fa.tiles = tiles;
@@ -1393,8 +1429,16 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     // producers and consumers measured slower on the large configs: consumers
     // that start before their producers hold workgroup slots.)
     const long long n_shrink = ((long long)plan.tile_bound * fa.P + kXcds - 1) / kXcds * kXcds;
-    const long long grid = plan.tile_bound > 0 ? n_shrink + (long long)plan.tile_bound * C + zero_units
-                                               : zero_units;
+    long long grid = plan.tile_bound > 0 ? n_shrink + (long long)plan.tile_bound * C + zero_units : zero_units;
+    if ((sb != nullptr) != Op::kBuild) return hipErrorInvalidValue;
+    if (sb) {  // one more workgroup, the last, writes the metadata
+        if (EC > kEB || fa.KS != 1) return hipErrorInvalidValue;  // mode 0 only
+        fa.slot = sb->slot;
+        fa.n_rows = sb->n;
+        fa.n_slots = sb->S;
+        fa.meta_out = sb->out;
+        grid += 1;
+    }
     if (grid == 0) return hipSuccess;
     switch (rpl_of(op.n_sh * op.R)) {
     case 1: return launch_fused_r<1>(op, fa, mfma_lean, grid, zf, st);
@@ -1402,28 +1446,6 @@ static hipError_t launch_fused_op(const Op &op, const int32_t *tiles, const int3
     case 3: return launch_fused_r<3>(op, fa, mfma_lean, grid, zf, st);
     default: return launch_fused_r<4>(op, fa, mfma_lean, grid, zf, st);
     }
-}
-
-// Mode 0 (one 512-column batch per expand unit, one 512-k step per shrink
-// unit): what launch_fused_op picks for these expand units and this k_in.
-static bool narrow_call(int k_in, int EC) {
-    const int steps = (k_in + kKP - 1) / kKP;
-    return EC <= kEB && steps <= kFlagWords - 1;
-}
-
-static int chunks_of(const int *off, int n_windows, int EC) {
-    int c = 0;
-    for (int l = 0; l < n_windows; ++l) c += (off[l + 1] - off[l] + EC - 1) / EC;
-    return c;
-}
-
-// Columns per expand unit: 512 while that keeps the expand units of a call
-// within about 2048 workgroups, else 1024 or 2048, so that each unit's read
-// of the tile's partials and its fixed chain latency cover more columns.
-static int expand_width(const int *off, int n_windows, int tile_bound) {
-    int ec = kEB;
-    while (ec < 4 * kEB && (long long)tile_bound * chunks_of(off, n_windows, ec) > 2048) ec *= 2;
-    return ec;
 }
 
 }  // namespace tl

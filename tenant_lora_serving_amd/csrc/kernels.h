@@ -9,8 +9,11 @@
 namespace tl {
 
 constexpr int kKP = 512;          // k per shrink step of the fused kernel
+constexpr int kEB = 512;          // output columns per expand batch of the fused kernel (128 per wave)
 constexpr int kFlagWords = 64;    // 64-bit words per tile in the fused workspace: piece flags, then a count
 constexpr int kMetaChunk = 1024;  // rows per workgroup (chunk) of the metadata build
+constexpr int kSlotThreads = 256;       // threads (rows) of an in-launch metadata build
+constexpr int kSmallBallotSlots = 64;   // slots a one-workgroup build ranks with one ballot per slot bit
 constexpr int kMaxSlices = 8;
 constexpr int kMaxRank = 128;
 constexpr int kMetaMaxSlotsMulti = 8192;  // slot limit when n spans several 1024-row chunks
@@ -100,8 +103,19 @@ hipError_t launch_shrink(const DenseShape &d, const int32_t *tiles, int tile_bou
                          hipStream_t st);
 hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *tiles, int tile_bound,
                          int add_inputs, int mfma_min, hipStream_t st);
+// slot != null (and meta_out): the launch also builds the batch's metadata
+// from slot and writes it to meta_out; tiles and counts are then unused.
+// Only where fused_builds_meta holds (hipErrorInvalidValue otherwise).
 hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                        void *ws, int mfma_min, hipStream_t st);
+                        void *ws, int mfma_min, hipStream_t st, const int32_t *slot = nullptr,
+                        const MetaOut *meta_out = nullptr);
+bool fused_builds_meta(const DenseShape &d, const FusedPlan &plan);
+// Launch shape of the fused kernel (plan.cpp): narrow_call, the call runs in
+// mode 0; chunks_of, expand units per tile at EC columns each;
+// expand_width, the columns per expand unit.
+bool narrow_call(int k_in, int EC);
+int chunks_of(const int *off, int n_windows, int EC);
+int expand_width(const int *off, int n_windows, int tile_bound);
 
 // Address of the library's fixed device buffer (LORA_NOALLOC_SCRATCH_BYTES)
 // on `device`, which must be the current device; resolved on the first call

@@ -26,6 +26,7 @@
 // No step waits on another workgroup, so nothing can hang.
 #include "common.h"
 #include "kernels.h"
+#include "slot_meta.h"
 
 namespace tl {
 
@@ -36,10 +37,6 @@ constexpr int kSplitMaxChunks = 64;  // a split build's workgroups each read eve
 
 __host__ __device__ inline bool meta_table_fits(int n_chunks, int S) { return (long long)(4 + n_chunks) * S <= kMetaTable; }
 
-struct SlotSrcDense {
-    const int32_t *slot;
-    __device__ int32_t key(int i) const { return slot[i]; }
-};
 
 // MoE pair p = t*top_k + j: adapter l = lora_ids[t], expert e = topk_ids[p].
 // key = l*E + e; -1 when l < 0; L*E (invalid) when l >= L or e outside [0, E).
@@ -120,17 +117,6 @@ __device__ __forceinline__ void radix_pass(uint32_t &key, int32_t &val, int shif
     __syncthreads();
 }
 
-__device__ __forceinline__ void write_tile_header(int32_t *rec, int slot, int pos, int rows, int seg_rows,
-                                                  int seg, int jt) {
-    rec[kRecSlot] = slot;
-    rec[kRecPos] = pos;
-    rec[kRecRows] = rows;
-    rec[kRecSegRows] = seg_rows;
-    rec[kRecSeg] = seg;
-    rec[kRecSegTile] = jt;
-    rec[6] = 0;
-    rec[7] = 0;
-}
 
 // Assembly of a multi-chunk build from the chunks' sorted entries in the
 // workspace: rows per slot (and per chunk), a scan over slots, then the
@@ -384,158 +370,13 @@ __global__ __launch_bounds__(kMT) void meta_assemble_kernel(int n, int S, int n_
 }
 
 // ------------------------------------------------------------ small batches
-// n <= 1024 rows and a slot table that fits LDS: one workgroup of NT >= n
-// threads, one row per thread.  Each wave ranks its rows among equal slots
-// with one ballot per distinct slot present in the wave and records how many
-// rows of each slot it holds in a [slot][wave] table; one block scan over
-// the slots turns the table into every (slot, wave)'s first sorted position
-// and gives each slot its segment index and first tile.  Since waves hold
-// rows in order, rows stay in ascending order within a slot.
-constexpr int kSmallTable = 16384;  // slots x waves entries of the count table
-constexpr int kSmallMaxSlots = 4096;
-constexpr int kSmallBallotSlots = 64;  // up to this many slots: one ballot per slot value
-
+// (small_meta_build, slot_meta.h) as a kernel of one workgroup.
 template <int NT, class Src>
 __global__ __launch_bounds__(NT) void meta_small_kernel(Src src, int n, int S, MetaOut out) {
-    constexpr int W = NT / kWave;
     extern __shared__ int dyn[];
-    int *tab = dyn;                        // [S][W]: counts, then first sorted positions
-    int *seg_idx = tab + (size_t)S * W;    // [S]
-    int *tile_off = seg_idx + S;           // [S]
-    int *start = tile_off + S;             // [S]
-    __shared__ Int3 scan3[W + 1];
-    __shared__ int n_long, n_invalid;
-    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-    const int raw = tid < n ? src.key(tid) : -1;
-    const bool active = tid < n && raw >= 0 && raw < S;
-    const int key = active ? raw : -1;
-    for (int i = tid; i < S * W; i += NT) tab[i] = 0;
-    if (tid == 0) n_long = n_invalid = 0;
-    __syncthreads();
-    if (tid < n && raw >= S) atomicAdd(&n_invalid, 1);
-    // rank among the wave's rows of the same slot.  Few slots: one ballot per
-    // bit of the slot number, a lane's group being the lanes that agree on
-    // every bit; else one ballot per distinct slot present in the wave.
-    int rank = 0;
-    const bool few = S <= kSmallBallotSlots;
-    if (few) {
-        uint64_t same = __ballot(active);
-        const int nbits = S > 1 ? 32 - __clz(S - 1) : 0;
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (key >> b) & 1;
-            const uint64_t mb = __ballot(active && bit);
-            same &= bit ? mb : ~mb;
-        }
-        if (active) {
-            rank = __popcll(same & lanemask_lt());
-            if (rank == 0) tab[key * W + w] = __popcll(same);  // the group's first lane
-        }
-    } else {
-        uint64_t pending = __ballot(active);
-        while (pending) {
-            const int leader = __builtin_ctzll(pending);
-            const int k = __builtin_amdgcn_readlane(key, leader);
-            const uint64_t same = __ballot(key == k);
-            if (key == k) rank = __popcll(same & lanemask_lt());
-            if (lane == leader) tab[k * W + w] = __popcll(same);
-            pending &= ~same;
-        }
-    }
-    __syncthreads();
-    Int3 tot;
-    if (few) {
-        // wave 0 scans the slots, lane k holding slot k
-        if (w == 0) {
-            const int k = lane;
-            int t = 0;
-            if (k < S) {
-#pragma unroll
-                for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
-            }
-            const Int3 v = {t, t > 0, seg_tiles(t, n)};
-            const Int3 inc = wave_incl_scan3(v);
-            const Int3 run = {inc.a - v.a, inc.b - v.b, inc.c - v.c};
-            if (k < S) {
-                int base = run.a;
-#pragma unroll
-                for (int ww = 0; ww < W; ++ww) {
-                    const int c = tab[k * W + ww];
-                    tab[k * W + ww] = base;
-                    base += c;
-                }
-                seg_idx[k] = run.b;
-                tile_off[k] = run.c;
-                start[k] = run.a;
-                if (t > 0) {
-                    out.seg_offsets[run.b] = run.a;
-                    out.seg_slot[run.b] = k;
-                }
-            }
-            const uint64_t lng = __ballot(k < S && t >= kTileRows);
-            if (lane == kWave - 1) {
-                scan3[0] = inc;  // the last lane's inclusive sums are the totals
-                n_long = __popcll(lng);
-            }
-        }
-        __syncthreads();
-        tot = scan3[0];
-    } else {
-        // per-slot totals: {rows, segments, tiles}, scanned over the slots
-        const int per = (S + NT - 1) / NT;
-        const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
-        Int3 loc = {0, 0, 0};
-        for (int k = s0; k < s1; ++k) {
-            int t = 0;
-#pragma unroll
-            for (int ww = 0; ww < W; ++ww) t += tab[k * W + ww];
-            loc = loc + Int3{t, t > 0, seg_tiles(t, n)};
-            if (t >= kTileRows) atomicAdd(&n_long, 1);
-        }
-        Int3 run = block_excl_scan3<NT>(loc, scan3, tot);
-        for (int k = s0; k < s1; ++k) {
-            int t = 0;
-            int base = run.a;
-#pragma unroll
-            for (int ww = 0; ww < W; ++ww) {
-                const int c = tab[k * W + ww];
-                tab[k * W + ww] = base;
-                base += c;
-                t += c;
-            }
-            seg_idx[k] = run.b;
-            tile_off[k] = run.c;
-            start[k] = run.a;
-            if (t > 0) {
-                out.seg_offsets[run.b] = run.a;
-                out.seg_slot[run.b] = k;
-            }
-            run = run + Int3{t, t > 0, seg_tiles(t, n)};
-        }
-        __syncthreads();
-    }
-    if (active) {
-        const int pos = tab[key * W + w] + rank;
-        const int st = start[key];
-        const int len = (key + 1 < S ? start[key + 1] : tot.a) - st;
-        const int q = pos - st;
-        out.sorted_rows[pos] = tid;
-        const int per = seg_tile_rows(len, n);
-        const int t = tile_off[key] + q / per, j = q % per;
-        int32_t *rec = out.tiles + (int64_t)t * kTileWords;
-        rec[kRecRowIds + j] = tid;
-        if (j == 0) write_tile_header(rec, key, pos, min(per, len - q), len, seg_idx[key], q / per);
-    }
-    if (tid == 0) {
-        out.seg_offsets[tot.b] = tot.a;
-        out.counts[0] = tot.a;
-        out.counts[1] = tot.b;
-        out.counts[2] = n_invalid;
-        out.counts[3] = n_long;
-        out.counts[4] = tot.c;
-        out.counts[5] = out.counts[6] = out.counts[7] = 0;
-    }
-    for (int t = tot.c + tid; t < out.tile_bound; t += NT)
-        write_tile_header(out.tiles + (int64_t)t * kTileWords, 0, 0, 0, 0, 0, 0);
+    __shared__ Int3 scan3[NT / kWave + 1];
+    __shared__ int cnt2[2];
+    small_meta_build<NT>(src, n, S, out, dyn, scan3, cnt2);
 }
 
 static int small_threads(int n) { return n <= 64 ? 64 : (n <= 256 ? 256 : 1024); }

@@ -28,6 +28,7 @@ struct DenseOp {
     int off[kMaxSlices + 1];
     static constexpr bool kRowWeights = false;
     static constexpr int kRank = 0;  // R is a runtime value
+    static constexpr bool kBuild = false;  // tile records come from the metadata
 
     __device__ int n_rr() const { return n_sh * R; }
     __device__ int n_xs() const { return n_sl; }
@@ -69,6 +70,13 @@ struct DenseOpR : DenseOp {
     __device__ const uint16_t *brow(int slot, int c) const { return b_pool + ((int64_t)slot * n_out + c) * RK; }
 };
 
+// A dense op whose launch also builds the batch's metadata: each unit derives
+// its tile's record from the slot array (the fused kernel's mode 0 only).
+template <class Base>
+struct BuildOp : Base {
+    static constexpr bool kBuild = true;
+};
+
 // Routed MoE gemm1 (FlashInfer bgmv_moe_gemm1_lora_delta): key = l*E + e,
 // rows are (token, slot) pairs; output window 0 is gate, window 1 is up.
 struct MoeOp {
@@ -85,6 +93,7 @@ struct MoeOp {
     static constexpr bool kRowWeights = false;
     static constexpr bool kAddInputs = false;  // out is written, not added to
     static constexpr int kRank = 0;
+    static constexpr bool kBuild = false;
 
     __device__ int n_rr() const { return n_sh * R; }
     __device__ int n_xs() const { return 2; }
@@ -183,6 +192,7 @@ struct MoeW2Op {
     int k_in, R, n_sh, n_out, E;
     static constexpr bool kRowWeights = true;
     static constexpr int kRank = 0;
+    static constexpr bool kBuild = false;
 
     __device__ int n_rr() const { return R; }
     __device__ int n_xs() const { return 1; }

@@ -28,4 +28,33 @@ FusedPlan fused_plan(int n, int num_slots, int n_sh, int R, int k_in, int n_out)
     return p;
 }
 
+// Mode 0 (one 512-column batch per expand unit, one 512-k step per shrink
+// unit): what launch_fused_op picks for these expand units and this k_in.
+bool narrow_call(int k_in, int EC) {
+    const int steps = (k_in + kKP - 1) / kKP;
+    return EC <= kEB && steps <= kFlagWords - 1;
+}
+
+int chunks_of(const int *off, int n_windows, int EC) {
+    int c = 0;
+    for (int l = 0; l < n_windows; ++l) c += (off[l + 1] - off[l] + EC - 1) / EC;
+    return c;
+}
+
+// Columns per expand unit: 512 while that keeps the expand units of a call
+// within about 2048 workgroups, else 1024 or 2048, so that each unit's read
+// of the tile's partials and its fixed chain latency cover more columns.
+int expand_width(const int *off, int n_windows, int tile_bound) {
+    int ec = kEB;
+    while (ec < 4 * kEB && (long long)tile_bound * chunks_of(off, n_windows, ec) > 2048) ec *= 2;
+    return ec;
+}
+
+// One launch builds the metadata too: a batch of at most kSlotThreads rows
+// over at most kSmallBallotSlots slots whose call runs in mode 0.
+bool fused_builds_meta(const DenseShape &d, const FusedPlan &plan) {
+    return d.n <= kSlotThreads && d.num_slots <= kSmallBallotSlots &&
+           narrow_call(d.k_in, expand_width(d.slice_off, d.num_slices, plan.tile_bound));
+}
+
 }  // namespace tl

@@ -73,6 +73,10 @@ def lib():
         L.lora_delta_fused_noalloc.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32,
                                                _c_i32, _c_p, _c_i32, _MetaStruct, _c_p, _c_i64, _c_i32,
                                                _c_p]
+        L.lora_delta_fused_build.restype = ctypes.c_int
+        L.lora_delta_fused_build.argtypes = [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                             _c_p, _c_i32, _c_p, _MetaStruct, _c_p, _c_i64, _c_i32, _c_p,
+                                             _c_sz, _c_p]
         L.moe_lora_workspace_bytes.restype = _c_sz
         L.moe_lora_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]
         L.moe_lora_gemm1_delta.restype = ctypes.c_int
@@ -100,6 +104,7 @@ def lib():
 EXPORTED = ["lora_meta_max_tiles", "lora_meta_workspace_bytes", "lora_meta_build",
             "lora_meta_from_offsets", "lora_shrink",
             "lora_expand", "lora_fused_workspace_bytes", "lora_delta_fused", "lora_delta_fused_noalloc",
+            "lora_delta_fused_build",
             "moe_lora_workspace_bytes", "moe_lora_gemm1_delta", "moe_lora_w2_workspace_bytes",
             "moe_lora_w2_delta", "moe_lora_meta_layout", "lora_mfma_min_rows",
             "lora_set_mfma_min_rows", "lora_status_string"]
@@ -311,6 +316,51 @@ def lora_delta_fused(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor
     if check:
         _check_ws("lora_delta_fused", ws, False, stream)
     return y
+
+
+def fused_build_workspace(n: int, num_slots: int, num_slices: int, max_rank: int, k_in: int,
+                          device="cuda") -> torch.Tensor:
+    """Workspace of lora_delta_fused_build: the fused workspace, then the
+    metadata build's (it also serves lora_delta_fused)."""
+    L = lib()
+    b = int(L.lora_fused_workspace_bytes(n, num_slots, num_slices, max_rank, k_in))
+    b += int(L.lora_meta_workspace_bytes(n, num_slots))
+    return torch.zeros(max(b, 16), dtype=torch.uint8, device=device)
+
+
+def lora_delta_fused_build(x: torch.Tensor, a_pool: torch.Tensor, b_pool: torch.Tensor,
+                           scale: torch.Tensor, slice_sizes, slot: torch.Tensor, y: torch.Tensor,
+                           meta: LoraMeta | None = None, offset_start: int = 0,
+                           ws: torch.Tensor | None = None, stream=None, check: bool = False) -> LoraMeta:
+    """lora_meta_build(slot) and lora_delta_fused in one call (one launch for
+    decode-sized batches): y is updated in place and the batch's metadata,
+    for later calls of the step, is written to meta (returned).
+    check: synchronize afterwards and raise if the workspace's error word is set."""
+    _pool_dims(a_pool, b_pool)
+    S, Lsl, R, k_in = a_pool.shape
+    if len(slice_sizes) != Lsl or sum(slice_sizes) != b_pool.shape[1]:
+        raise ValueError("slice sizes do not match the pools")
+    xp, ldx = _rows_ld(x, "x")
+    yp, ldy = _rows_ld(y, "y")
+    n = x.shape[0]
+    if y.shape[0] != n or slot.numel() != n:
+        raise ValueError("x, y and slot row counts differ")
+    if meta is None:
+        meta = LoraMeta.allocate(n, S, x.device)
+    assert meta.n == n and meta.num_slots == S, "metadata buffers sized for another batch"
+    if ws is None:
+        ws = fused_build_workspace(n, S, Lsl, R, k_in, x.device)
+    ss = (ctypes.c_int32 * Lsl)(*[int(v) for v in slice_sizes])
+    st = lib().lora_delta_fused_build(xp, ldx, n, k_in, _dev(a_pool, "a_pool", torch.bfloat16),
+                                      _dev(b_pool, "b_pool", torch.bfloat16),
+                                      _dev(scale, "scale", torch.float32), S, Lsl, ss, R,
+                                      _dev(slot, "slot", torch.int32), meta.struct(), yp, ldy,
+                                      int(offset_start), _dev(ws, "ws", torch.uint8), ws.numel(),
+                                      _stream(stream))
+    _check("lora_delta_fused_build", st)
+    if check:
+        _check_ws("lora_delta_fused_build", ws, False, stream)
+    return meta
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20   # the fixed device buffer behind lora_delta_fused_noalloc

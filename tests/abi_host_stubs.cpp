@@ -85,9 +85,10 @@ hipError_t launch_expand(const DenseShape &d, const float *xa, const int32_t *ti
     return hipSuccess;
 }
 hipError_t launch_fused(const DenseShape &d, const int32_t *tiles, const int32_t *counts, const FusedPlan &plan,
-                        void *ws, int mfma_min, hipStream_t) {
+                        void *ws, int mfma_min, hipStream_t, const int32_t *slot, const MetaOut *meta_out) {
     rec(kFused, {d.n, d.k_in, d.slice_off[d.num_slices], p(tiles), p(counts), plan.tile_bound,
-                 (long long)plan.total_bytes, p(ws), mfma_min});
+                 (long long)plan.total_bytes, p(ws), mfma_min, p(slot), meta_out ? p(meta_out->tiles) : 0,
+                 meta_out ? meta_out->tile_bound : -1});
     return hipSuccess;
 }
 hipError_t noalloc_scratch(int device, void **ptr) {

@@ -165,3 +165,36 @@ def test_shrink_and_expand_pass_the_tile_bound(L):
     ss = (ctypes.c_int32 * 2)(256, 128)
     assert L.lora_expand(0x4000, 0x2000, 4, 2, ss, 8, 40, m, 0x3000, 384, 0, 1, None) == OK
     assert calls(L)[EXPAND] == 1 and val(L, EXPAND, 1) == 384 and val(L, EXPAND, 6) == 1
+
+
+def test_build_call_launches_once_for_decode_batches(L):
+    m = meta(0x100000)
+    ss = (ctypes.c_int32 * 3)(4096, 1024, 1024)
+    need = L.lora_fused_workspace_bytes(256, 32, 3, 16, 4096) + L.lora_meta_workspace_bytes(256, 32)
+
+    def call(n, S, ws_bytes=None):
+        nb = ws_bytes if ws_bytes is not None else (L.lora_fused_workspace_bytes(n, S, 3, 16, 4096) +
+                                                   L.lora_meta_workspace_bytes(n, S))
+        return L.lora_delta_fused_build(0x1000, 4096, n, 4096, 0x2000, 0x3000, 0x4000, S, 3, ss, 16, 0x8000, m,
+                                        0x5000, 6144, 0, 0x9000, nb, None)
+    assert call(256, 32, need - 1) == EWS
+    assert calls(L) == [0] * 9
+    assert call(256, 32) == OK
+    assert calls(L) == [0, 0, 0, 0, 0, 1, 0, 0, 0]          # the fused launch alone
+    assert val(L, FUSED, 9) == 0x8000                        # ... given the slot array
+    assert val(L, FUSED, 10) == 0x100000 + 0x40000           # ... and the metadata to write
+    assert val(L, FUSED, 11) == L.lora_meta_max_tiles(256, 32)
+    for n, S in ((300, 32), (256, 65), (3000, 8)):         # past the one-launch limits: two launches
+        L.raw.stub_reset()
+        assert call(n, S) == OK, (n, S)
+        assert calls(L) == [1, 0, 0, 0, 0, 1, 0, 0, 0], (n, S)
+        assert val(L, FUSED, 9) == 0                         # the fused kernel reads the built records
+        assert val(L, FUSED, 3) == 0x100000 + 0x40000
+        ws_meta = [val(L, META_DENSE, i) for i in range(6, 10)]
+        fused_need = L.lora_fused_workspace_bytes(n, S, 3, 16, 4096)
+        if L.lora_meta_workspace_bytes(n, S):                # carved after the fused part
+            assert min(ws_meta) >= 0x9000 + fused_need
+    L.raw.stub_reset()
+    assert L.lora_delta_fused_build(0x1000, 4096, 8, 4096, 0x2000, 0x3000, 0x4000, 32, 3, ss, 16, None, m,
+                                    0x5000, 6144, 0, 0x9000, need, None) == EINVAL   # no slot array
+    assert calls(L) == [0] * 9

@@ -136,6 +136,23 @@ def test_expand_and_fused_validation(L):
     assert L.lora_delta_fused(*args0, 0x6000, 1 << 20, None) == OK
 
 
+def test_build_validation(L):
+    m = _meta()
+    ss = (ctypes.c_int32 * 2)(256, 128)
+    need = L.lora_fused_workspace_bytes(8, 4, 2, 8, 256) + L.lora_meta_workspace_bytes(8, 4)
+    args = [0x1000, 256, 8, 256, 0x2000, 0x3000, 0x4000, 4, 2, ss, 8, 0x7000, m, 0x5000, 384, 0]
+    assert L.lora_delta_fused_build(*args, 0x6000, need - 1, None) == EWS
+    bad = list(args)
+    bad[11] = None                      # rows but no slot array
+    assert L.lora_delta_fused_build(*bad, 0x6000, need, None) == EINVAL
+    bad = list(args)
+    bad[12] = _meta(0)                  # nowhere to write the metadata
+    assert L.lora_delta_fused_build(*bad, 0x6000, need, None) == EINVAL
+    bad = list(args)
+    bad[10] = 12                        # rank not a multiple of 8
+    assert L.lora_delta_fused_build(*bad, 0x6000, need, None) == EUNSUP
+
+
 def test_moe_validation(L):
     base = dict(x=0x1000, ldx=4096, T=16, H=4096, wa=0x2000, lsa=16 * 4096, wb=0x3000, lsb=1408 * 16,
                 shared=0, topk=0x4000, top_k=8, lora=0x5000, E=64, L=8, R=16, I=1408, out=0x6000)
