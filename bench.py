@@ -5,23 +5,25 @@ Workload: decode BGMV at the Llama-3-8B QKV shape (256 one-token rows,
 k_in 4096, fused output slices 4096/1024/1024, 32 adapters at max rank 16 with
 true ranks in {8, 16}, Zipf(1) routing, 5% unadapted rows, scale 32/r).
 
-A step is one pass of the hot path over one batch: lora_meta_build (rows
-sorted by slot, segments, tiles) then lora_delta_fused (shrink + expand in one
-launch, MFMA for segments of at least 16 rows, vector ALU below).  Inputs are
-resident in HBM and rotate over enough independent copies (> 1 GiB in total)
-that no step finds its adapters in the 256 MB Infinity Cache.
+A step is one pass of the hot path over one batch: lora_delta_fused_build,
+which builds the routing metadata (rows sorted by slot, segments, tile
+records; written out for later layers) and applies the fused delta (shrink +
+expand, MFMA for segments of at least 16 rows, vector ALU below) in one
+launch at this size.  Inputs are resident in HBM and rotate over enough
+independent copies (> 1 GiB in total) that no step finds its adapters in the
+256 MB Infinity Cache.
 
 Timed region: exactly K steps, replayed from one HIP graph, bracketed by
 torch.cuda.synchronize().  value = algorithmic bytes of the K steps / wall
-time (GB/s).  The fused kernel's own average duration is measured with two
-HIP events on the launch stream bracketing the replay of a graph of K
-back-to-back launches of that kernel alone (elapsed / K; a graph, so that the
-host's launch rate cannot set the pace); it gives the roofline fraction
-against 8 TB/s.
-The metadata kernel is timed the same way, and so is a plain device copy
+time (GB/s).  The step kernel's average duration is measured with two HIP
+events on the launch stream bracketing the replay of a graph of K launches
+(elapsed / K; a graph, so that the host's launch rate cannot set the pace);
+it gives the roofline fraction against 8 TB/s.  Timed the same way and
+reported beside it: the same work in two launches (lora_meta_build, then
+lora_delta_fused), each of those kernels alone, and a plain device copy
 moving the same number of bytes (plain_copy_same_bytes: what the memory
-system gives a transfer of this size, next to the kernel).  The fp64 CPU
-oracle is timed on the same batch on the host cores (cpu_baseline).
+system gives a transfer of this size).  The fp64 CPU oracle is timed on the
+same batch on the host cores (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --calibrate-copy   # a plain 512 MiB device copy, for counter scaling
@@ -327,7 +329,7 @@ def main():
     # the data rotates over independent copies; the metadata buffers and the
     # workspace are one set reused by every step, as a serving loop reuses them
     meta = B.LoraMeta.allocate(case.n, case.num_slots)
-    ws = B.fused_workspace(case.n, case.num_slots, case.num_slices, case.max_rank, case.k_in)
+    ws = B.fused_build_workspace(case.n, case.num_slots, case.num_slices, case.max_rank, case.k_in)
     for _ in range(copies):
         s = {k: v.clone() for k, v in base.items()}
         s["meta"] = meta
@@ -336,9 +338,16 @@ def main():
     del base
 
     def step(s):
+        # the routing metadata (written to meta for later layers) and the
+        # fused delta: one launch at this size
+        B.lora_delta_fused_build(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes, s["slot"], s["y"],
+                                 meta=s["meta"], ws=s["ws"])
+
+    def meta_step(s):
         B.lora_meta_build(s["slot"], case.num_slots, s["meta"])
-        B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes, s["meta"], s["y"],
-                           ws=s["ws"])
+
+    def delta_step(s):
+        B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes, s["meta"], s["y"], ws=s["ws"])
 
     for i in range(args.warmup):
         step(sets[i % copies])
@@ -359,10 +368,8 @@ def main():
     ms_step = wall * 1e3 / K
 
     # ---- kernel durations: HIP events on the launch stream bracketing K
-    # back-to-back launches of one kernel (the metadata is built beforehand),
-    # replayed from a graph so that the host's launch rate cannot set the pace
-    B.lora_meta_build(sets[0]["slot"], case.num_slots, sets[0]["meta"])
-    torch.cuda.synchronize()
+    # back-to-back launches, replayed from a graph so that the host's launch
+    # rate cannot set the pace
     stream = torch.cuda.current_stream()
 
     def region(launch, items):
@@ -383,9 +390,14 @@ def main():
         del gr
         return e0.elapsed_time(e1) / K
 
-    fused_ms = region(lambda s: B.lora_delta_fused(s["x"], s["a"], s["b"], s["scale"], case.slice_sizes,
-                                                   s["meta"], s["y"], ws=s["ws"]), sets)
-    meta_ms = region(lambda s: B.lora_meta_build(s["slot"], case.num_slots, s["meta"]), sets)
+    build_ms = region(step, sets)
+    # the same work in two launches (metadata kernel, then the fused kernel
+    # reading the records it wrote), and each of the two alone
+    two_ms = region(lambda s_: (meta_step(s_), delta_step(s_)), sets)
+    meta_step(sets[0])
+    torch.cuda.synchronize()
+    delta_ms = region(delta_step, sets)
+    meta_ms = region(meta_step, sets)
     # what a plain device copy moving the same bytes (half read, half written)
     # takes when timed the same way, rotating over as many buffers
     half = bytes_step // 2
@@ -395,7 +407,7 @@ def main():
     del bufs
 
     value = bytes_step * K / wall / 1e9
-    fused_gbs = bytes_step / (fused_ms * 1e-3) / 1e9
+    build_gbs = bytes_step / (build_ms * 1e-3) / 1e9
     traffic = recorded_traffic("decode")
     res = {
         "metric": METRIC,
@@ -415,14 +427,18 @@ def main():
                    "max_rank": case.max_rank, "active_rows": int(act.sum()),
                    "active_slots": int(len(np.unique(case.slot[act]))),
                    "bytes_per_step": bytes_step, "input_copies": copies,
+                   "step": "lora_delta_fused_build: metadata build + fused delta in one launch",
                    "mfma_min_rows": B.mfma_min_rows(), "kernel_sources": kernel_source_hash()},
         "tokens_per_s": round(case.n * K / wall, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(build_gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(build_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic["bytes"] if traffic else None,
-                     "kernel": "fused_kernel<3, 1, 0, DenseOpR<16>> (rank-16 decode instantiation)",
-                     "kernel_us": round(fused_ms * 1e3, 3)},
+                     "kernel": "fused_kernel<3, 1, 0, BuildOp<DenseOpR<16>>> (metadata + delta, one launch)",
+                     "kernel_us": round(build_ms * 1e3, 3)},
+        "two_launch_step_us": round(two_ms * 1e3, 3),
+        "delta_kernel_us": round(delta_ms * 1e3, 3),
+        "delta_kernel_frac": round(bytes_step / (delta_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "meta_kernel_us": round(meta_ms * 1e3, 3),
         "plain_copy_same_bytes": {"us": round(copy_ms * 1e3, 3),
                                   "GB/s": round(2 * half / (copy_ms * 1e-3) / 1e9, 2),
