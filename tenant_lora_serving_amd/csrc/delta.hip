@@ -8,7 +8,8 @@
 //
 // Work units.  The metadata cuts every segment into tiles of at most 16 rows
 // (one 128-byte record each: slot, first sorted position, row count, segment
-// size, row ids).  A workgroup (4 waves) takes one unit:
+// size, row ids).  A workgroup takes one unit (4 waves; a shrink unit of a
+// call with few units, 8 waves over 2048-wide k passes):
 //   shrink unit  (tile, shrink slice): every rank row of the slice over all of k
 //   expand unit  (tile, 512-column chunk): every row of the tile
 // Segments with at least `mfma_min` rows (16 by default) run on
@@ -25,14 +26,19 @@
 
 namespace tl {
 
-constexpr int kBT = 256;        // threads per compute workgroup
+constexpr int kBT = 256;        // threads per expand workgroup
+// Shrink units: 4 waves and 512-wide k passes when a call has enough units
+// to fill the chip, else 8 waves and 2048-wide passes (a unit's k range in
+// fewer dependent passes; one workgroup per CU at the larger LDS stage).
 constexpr int kCW = 512;        // expand columns per unit
 constexpr int kRRMfma = 128;    // shrink rank rows per pass on the MFMA path
 constexpr int kRRValu = 64;     // shrink rank rows per pass on the vector ALU
-constexpr int kKC = 512;        // x columns staged in LDS per pass
-constexpr int kXS = kKC + 8;    // padded LDS row stride (elements) of the staged x tile
-constexpr int kXsBytes = kTileRows * kXS * 2;
-constexpr int kRedStride = 48 * 16;  // per-wave partial block when waves split k
+// per-wave partial blocks when the NW waves split k: KW * n_rr * 16 floats, and
+// KW * n_rr < 32 * NW rank rows (wave_split)
+template <int NW>
+constexpr int shrink_red_floats() { return 512 * NW; }
+template <int KC>
+constexpr int shrink_xs() { return KC + 8; }  // padded LDS row stride (elements) of the staged x tile
 constexpr int kOutStride = 132;      // padded fp32 row stride of the MFMA output tile
 
 // ============================================================ tile header
@@ -77,20 +83,27 @@ __device__ __forceinline__ bool load_tile(const Op &op, const int32_t *tiles, in
 
 __device__ __forceinline__ u32x4_t lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 
-// How the 4 waves share a unit: GW waves split the rank-row groups, KW = 4/GW
-// split the k range (their partials are summed in wave order).
+// How the NW waves of a shrink unit share it: GW waves (a power of two, at
+// most the rank-row groups and NW) split the groups, KW = NW / GW split the
+// k range (their partials are summed in wave order).  With GW the largest
+// power of two <= groups (or NW), KW * n_rr stays below 32 * NW rank rows (16
+// per MFMA group, 8 per vector-ALU group): the partial blocks fit
+// shrink_red_floats<NW>().
+template <int NW>
 __device__ __forceinline__ void wave_split(int groups, int &GW, int &KW) {
-    GW = groups >= 4 ? 4 : (groups >= 2 ? 2 : 1);
-    KW = 4 / GW;
+    GW = (groups >= 8 && NW >= 8) ? 8 : (groups >= 4 ? 4 : (groups >= 2 ? 2 : 1));
+    KW = NW / GW;
 }
 
-// Sum the KW per-wave partial blocks of `red` into `res` in wave order.
+// Sum the KW per-wave partial blocks of `red` (n_rr * 16 floats each) into
+// `res` in wave order.
+template <int NT>
 __device__ __forceinline__ void reduce_waves(int KW, int n_rr, float *res, const float *red) {
     __syncthreads();
     if (KW > 1) {
-        for (int idx = threadIdx.x; idx < n_rr * 16; idx += kBT) {
+        for (int idx = threadIdx.x; idx < n_rr * 16; idx += NT) {
             float s = red[idx];
-            for (int q = 1; q < KW; ++q) s += red[q * kRedStride + idx];
+            for (int q = 1; q < KW; ++q) s += red[q * n_rr * 16 + idx];
             res[idx] = s;
         }
         __syncthreads();
@@ -98,37 +111,41 @@ __device__ __forceinline__ void reduce_waves(int KW, int n_rr, float *res, const
 }
 
 // ============================================================ shrink
-// Every unit reads its x rows through LDS in chunks of kKC columns (coalesced
+// Every unit reads its x rows through LDS in chunks of KC columns (coalesced
 // 16-byte loads, all issued before any is used) and streams the adapter's
 // A rows straight from HBM into registers, eight 16-byte loads per lane in
 // flight before the first is consumed.
 //
 // Stage x rows j < 16 (zero rows past m), columns [kc0, kc1), into xs[j][.].
+template <int NT, int KC>
 __device__ __forceinline__ void stage_x(const Tile &h, int kc0, int kc1, uint16_t *xs) {
-    u32x4_t v[4];
+    constexpr int kPerRow = KC / 8;                       // 16-byte chunks per staged row
+    constexpr int kLoads = kTileRows * kPerRow / NT;      // per thread
+    u32x4_t v[kLoads];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = threadIdx.x + kBT * i;
-        const int j = idx >> 6, k = kc0 + 8 * (idx & 63);
+    for (int i = 0; i < kLoads; ++i) {
+        const int idx = threadIdx.x + NT * i;
+        const int j = idx / kPerRow, k = kc0 + 8 * (idx % kPerRow);
         v[i] = (j < h.m && k < kc1) ? ld16(h.xrow[j] + k) : zero4();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = threadIdx.x + kBT * i;
-        *reinterpret_cast<u32x4_t *>(xs + (idx >> 6) * kXS + 8 * (idx & 63)) = v[i];
+    for (int i = 0; i < kLoads; ++i) {
+        const int idx = threadIdx.x + NT * i;
+        *reinterpret_cast<u32x4_t *>(xs + (idx / kPerRow) * shrink_xs<KC>() + 8 * (idx % kPerRow)) = v[i];
     }
 }
 
 // res[rl*16 + j] = sum_{k in [k0,k1)} x[row_j][k] * A[slot][rr0 + rl][k] for
 // rl < n_rr <= kRRMfma, on v_mfma_f32_16x16x32_bf16 (tile rows = MFMA rows,
 // rank rows = MFMA columns).
-template <class Op>
+template <int NT, int KC, class Op>
 __device__ __forceinline__ void shrink_mfma(const Op &op, const Tile &h, int rr0, int n_rr, int k0, int k1,
                                             float *res, float *red, uint16_t *xs) {
+    constexpr int kXS = shrink_xs<KC>();
     const int lane = lane_id(), w = wave_id();
     const int groups = (n_rr + 15) >> 4;
     int GW, KW;
-    wave_split(groups, GW, KW);
+    wave_split<NT / kWave>(groups, GW, KW);
     const int gw = w % GW, kw = w / GW;
     const int col = lane & 15, kk = (lane >> 4) * 8;
     const bool has0 = gw < groups, has1 = gw + GW < groups;
@@ -145,13 +162,13 @@ __device__ __forceinline__ void shrink_mfma(const Op &op, const Tile &h, int rr0
             a1[u] = (ap1 && k < kb) ? ld16(ap1 + k) : zero4();
         }
     };
-    for (int kc0 = k0; kc0 < k1; kc0 += kKC) {
-        const int kc1 = min(k1, kc0 + kKC);
+    for (int kc0 = k0; kc0 < k1; kc0 += KC) {
+        const int kc1 = min(k1, kc0 + KC);
         const int per = ((kc1 - kc0 + KW * 32 - 1) / (KW * 32)) * 32;
         const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
         load_a(ka, kb);  // first A batch in flight while x is staged
         __syncthreads();
-        stage_x(h, kc0, kc1, xs);
+        stage_x<NT, KC>(h, kc0, kc1, xs);
         __syncthreads();
         for (int kb0 = ka; kb0 < kb; kb0 += 8 * 32) {
             if (kb0 > ka) load_a(kb0, kb);
@@ -165,7 +182,7 @@ __device__ __forceinline__ void shrink_mfma(const Op &op, const Tile &h, int rr0
         }
     }
     // lane holds D[tile row 4*(lane>>4) + i][rank row rl]
-    float *dst = KW == 1 ? res : red + kw * kRedStride;
+    float *dst = KW == 1 ? res : red + kw * n_rr * 16;
     const int j0 = (lane >> 4) * 4;
     if (has0 && rl0 < n_rr) {
         dst[rl0 * 16 + j0 + 0] = acc0[0];
@@ -179,26 +196,27 @@ __device__ __forceinline__ void shrink_mfma(const Op &op, const Tile &h, int rr0
         dst[rl1 * 16 + j0 + 2] = acc1[2];
         dst[rl1 * 16 + j0 + 3] = acc1[3];
     }
-    reduce_waves(KW, n_rr, res, red);
+    reduce_waves<NT>(KW, n_rr, res, red);
 }
 
 // Same result on the vector ALU (v_dot2c_f32_bf16) for n_rr <= kRRValu:
 // a wave holds 8 rank rows x 8 k lanes; each lane dots 8 k per load and the
 // 8 k lanes of a rank row are summed with xor shuffles at the end.
-template <class Op>
+template <int NT, int KC, class Op>
 __device__ __forceinline__ void shrink_valu(const Op &op, const Tile &h, int rr0, int n_rr, int k0, int k1,
                                             float *res, float *red, uint16_t *xs) {
+    constexpr int kXS = shrink_xs<KC>();
     const int lane = lane_id(), w = wave_id();
     const int rsub = lane >> 3, kl = lane & 7;
     const int groups = n_rr >> 3;
     int GW, KW;
-    wave_split(groups, GW, KW);
+    wave_split<NT / kWave>(groups, GW, KW);
     const int gw = w % GW, kw = w / GW;
     const int m = h.m;
-    float *dst = KW == 1 ? res : red + kw * kRedStride;
+    float *dst = KW == 1 ? res : red + kw * n_rr * 16;
     u32x4_t a[8];
-    for (int kc0 = k0; kc0 < k1; kc0 += kKC) {
-        const int kc1 = min(k1, kc0 + kKC);
+    for (int kc0 = k0; kc0 < k1; kc0 += KC) {
+        const int kc1 = min(k1, kc0 + KC);
         const int per = ((kc1 - kc0 + KW * 64 - 1) / (KW * 64)) * 64;
         const int ka = kc0 + kw * per, kb = min(kc1, ka + per);
         // first A batch of this wave's first group in flight while x is staged
@@ -209,7 +227,7 @@ __device__ __forceinline__ void shrink_valu(const Op &op, const Tile &h, int rr0
             a[u] = (ap_first && k < kb) ? ld16_stream(ap_first + k) : zero4();
         }
         __syncthreads();
-        stage_x(h, kc0, kc1, xs);
+        stage_x<NT, KC>(h, kc0, kc1, xs);
         __syncthreads();
         for (int q = gw; q < groups; q += GW) {
             const int rl = 8 * q + rsub;
@@ -255,18 +273,18 @@ __device__ __forceinline__ void shrink_valu(const Op &op, const Tile &h, int rr0
             }
         }
     }
-    reduce_waves(KW, n_rr, res, red);
+    reduce_waves<NT>(KW, n_rr, res, red);
 }
 
 // Rank rows [rr0, rr0 + n_rr) of one tile over k in [k0, k1) into res
 // (n_rr <= kRRMfma on the MFMA path, <= kRRValu on the vector ALU).
-template <class Op>
+template <int NT, int KC, class Op>
 __device__ __forceinline__ void shrink_compute(const Op &op, const Tile &h, bool mf, int rr0, int n_rr,
                                                int k0, int k1, float *res, float *red, uint16_t *xs) {
     if (mf)
-        shrink_mfma(op, h, rr0, n_rr, k0, k1, res, red, xs);
+        shrink_mfma<NT, KC>(op, h, rr0, n_rr, k0, k1, res, red, xs);
     else
-        shrink_valu(op, h, rr0, n_rr, k0, k1, res, red, xs);
+        shrink_valu<NT, KC>(op, h, rr0, n_rr, k0, k1, res, red, xs);
 }
 
 // ============================================================ expand
@@ -550,8 +568,8 @@ __device__ __forceinline__ void expand_unit(const Op &op, const Tile &h, bool mf
 }
 
 // ============================================================ kernels
-template <class Op>
-__global__ __launch_bounds__(kBT) void shrink_kernel(Op op, const int32_t *tiles, float *xa, int n, int mfma_min) {
+template <int NT, int KC, class Op>
+__global__ __launch_bounds__(NT) void shrink_kernel(Op op, const int32_t *tiles, float *xa, int n, int mfma_min) {
     extern __shared__ __align__(16) char smem[];
     __shared__ TileLds tl_sh;
     Tile h;
@@ -560,15 +578,15 @@ __global__ __launch_bounds__(kBT) void shrink_kernel(Op op, const int32_t *tiles
     if (!load_tile(op, tiles, t, tl_sh, h)) return;
     const bool mf = h.mseg >= mfma_min;
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-    float *res = reinterpret_cast<float *>(smem + kXsBytes);
+    float *res = reinterpret_cast<float *>(smem + kTileRows * shrink_xs<KC>() * 2);
     float *red = res + kRRMfma * 16;
     const int R = op.R;
     const float sc = op.scale_of(h.slot);
     const int chunk = mf ? kRRMfma : kRRValu;
     for (int r0 = 0; r0 < R; r0 += chunk) {
         const int cnt = min(chunk, R - r0);
-        shrink_compute(op, h, mf, sl * R + r0, cnt, 0, op.k_in, res, red, xs);
-        for (int idx = threadIdx.x; idx < h.m * cnt; idx += kBT) {
+        shrink_compute<NT, KC>(op, h, mf, sl * R + r0, cnt, 0, op.k_in, res, red, xs);
+        for (int idx = threadIdx.x; idx < h.m * cnt; idx += NT) {
             const int j = idx / cnt, r = idx % cnt;
             xa[((int64_t)sl * n + h.rows[j]) * R + r0 + r] = sc * res[r * 16 + j];
         }
@@ -591,8 +609,10 @@ __global__ __launch_bounds__(kBT) void expand_kernel(Op op, const int32_t *tiles
 // ============================================================ host side
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+template <int NT, int KC>
 static size_t shrink_lds() {
-    return (size_t)kXsBytes + (size_t)(kRRMfma * 16 + 4 * kRedStride) * sizeof(float);
+    return (size_t)kTileRows * shrink_xs<KC>() * 2 +
+           (size_t)(kRRMfma * 16 + shrink_red_floats<NT / kWave>()) * sizeof(float);
 }
 
 static size_t expand_lds(int n_xa_slices, int R) {
@@ -633,9 +653,17 @@ hipError_t launch_shrink(const DenseShape &d, const int32_t *tiles, int tile_bou
                          hipStream_t st) {
     if (tile_bound == 0) return hipSuccess;
     const DenseOp op = dense_op(d);
-    const size_t lds = shrink_lds();
-    hipLaunchKernelGGL(shrink_kernel<DenseOp>, dim3(tile_bound * d.num_slices), dim3(kBT), lds, st, op, tiles, xa,
-                       d.n, mfma_min);
+    const long long units = (long long)tile_bound * d.num_slices;
+    if (units >= 512) {  // enough units for two per CU: 4 waves, 512-wide k passes
+        const size_t lds = shrink_lds<256, 512>();
+        hipLaunchKernelGGL((shrink_kernel<256, 512, DenseOp>), dim3(units), dim3(256), lds, st, op, tiles, xa,
+                           d.n, mfma_min);
+    } else {
+        const size_t lds = shrink_lds<512, 2048>();
+        allow_lds(shrink_kernel<512, 2048, DenseOp>, lds);
+        hipLaunchKernelGGL((shrink_kernel<512, 2048, DenseOp>), dim3(units), dim3(512), lds, st, op, tiles, xa,
+                           d.n, mfma_min);
+    }
     return hipGetLastError();
 }
 
