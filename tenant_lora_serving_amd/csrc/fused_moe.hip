@@ -46,7 +46,7 @@ hipError_t launch_moe_delta(const MoeShape &m, const MetaOut &meta, const FusedP
     const bool fits = (long long)m.T * m.ldx * 2 < (1ll << 31) && (long long)n_pairs * op.n_out * 2 < (1ll << 31);
     if (n_pairs > 0 && fits && (long long)n_pairs <= 64 * S) {
         const SegArgs sa{tiles,  plan.tile_bound, meta.sorted_rows, meta.seg_offsets, meta.seg_slot, counts, (int)cap,
-                         n_pairs, ctl};
+                         n_pairs, ctl, m.E};
         switch (m.R * 8 + G) {
         case 8 * 8 + 1: return launch_segment<1, 8>(op, sa, zf, zero_units, st);
         case 16 * 8 + 1: return launch_segment<1, 16>(op, sa, zf, zero_units, st);

@@ -40,7 +40,7 @@ hipError_t launch_moe_w2_delta(const MoeW2Shape &m, const MetaOut &meta, const F
     const bool fits = n_pairs * m.ldx * 2 < (1ll << 31) && n_pairs * m.ldy * 2 < (1ll << 31);
     if (n_pairs > 0 && fits && n_pairs <= 64 * S) {
         const SegArgs sa{tiles, plan.tile_bound, meta.sorted_rows, meta.seg_offsets, meta.seg_slot, counts, (int)cap,
-                         (int)n_pairs, ctl};
+                         (int)n_pairs, ctl, m.E};
         switch (m.R) {
         case 8: return launch_segment_w2<1, 8>(op, sa, st);
         case 16: return launch_segment_w2<1, 16>(op, sa, st);

@@ -62,7 +62,81 @@ struct SegArgs {
     int n_units;            // units before the zero units: the most segments the call can have
     int n_rows;             // pairs of the call (the metadata's n)
     int *ctl;               // the workspace's control line (its call tag is advanced)
+    int key_div;            // > 0: segment units grouped by adapter (key / key_div) on XCDs; 0: in order
 };
+
+// Segment units by adapter.  A token's x row is read by the segments of its
+// top_k experts, all of its own adapter l (keys l*E .. l*E + E-1), so when one
+// XCD runs all of adapter l's segments the row is fetched from HBM once for
+// that XCD's L2 instead of once per segment.  Workgroups go to the 8 XCDs
+// round robin: unit u runs on XCD x = u mod 8 and takes the (u / 8)-th segment
+// of class x (segments whose adapter is x mod 8, in segment order).  A class
+// with more segments than its XCD has units passes the rest, in class order,
+// to the units left without a segment, also in class order.  Returns the
+// unit's segment, or -1.  sm: 4 * 8 * (kSegMapMax / 256) + 40 ints of LDS.
+constexpr int kSegMapMax = 1024;  // most units the mapping takes (else units run in segment order)
+__device__ __forceinline__ int unit_segment(const SegArgs &sa, int u, int n_seg, int *sm) {
+    constexpr int Q = kSegMapMax / 256, NC = 8;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    int *cnt = sm;                   // [Q][4 waves][NC] segments of each class, then their first class rank
+    int *tot = cnt + Q * 4 * NC;     // [NC] segments per class
+    int *found = tot + NC;           // the unit's segment
+    int cls[Q], rank[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int sg = tid + 256 * q;
+        cls[q] = sg < n_seg ? (sa.seg_slot[sg] / sa.key_div) & (NC - 1) : -1;
+    }
+    if (tid == 0) *found = -1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        rank[q] = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const uint64_t b = __ballot(cls[q] == c);
+            if (cls[q] == c) rank[q] = __popcll(b & lanemask_lt());
+            if (lane == c) cnt[(q * 4 + w) * NC + c] = __popcll(b);
+        }
+    }
+    __syncthreads();
+    if (tid < NC) {  // exclusive prefix over (q, wave) blocks, in segment order, per class
+        int run = 0;
+        for (int i = 0; i < Q * 4; ++i) {
+            const int v = cnt[i * NC + tid];
+            cnt[i * NC + tid] = run;
+            run += v;
+        }
+        tot[tid] = run;
+    }
+    __syncthreads();
+    // the unit's (class, rank): its own class's, or an overflow one
+    const int x = u & (NC - 1), i = u / NC;
+    auto cap = [&](int c) { return c < sa.n_units ? (sa.n_units - c + NC - 1) / NC : 0; };
+    int tc = -1, tr = -1;
+    if (i < tot[x]) {
+        tc = x;
+        tr = i;
+    } else {
+        int k = i - tot[x];
+        for (int c = 0; c < x; ++c) k += max(0, cap(c) - tot[c]);
+        for (int c = 0; c < NC && tc < 0; ++c) {
+            const int over = max(0, tot[c] - cap(c));
+            if (k < over) {
+                tc = c;
+                tr = cap(c) + k;
+            } else {
+                k -= over;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (cls[q] >= 0 && cls[q] == tc && cnt[(q * 4 + w) * NC + cls[q]] + rank[q] == tr) *found = tid + 256 * q;
+    __syncthreads();
+    const int sg = __builtin_amdgcn_readfirstlane(*found);
+    __syncthreads();  // (the unit's LDS stages reuse these words)
+    return sg;
+}
 
 // bytes of a row of the LDS xa block: for each of nx blocks, hi[R] then lo[R] (bf16), + 16 pad
 __host__ __device__ constexpr int seg_xa_stride(int nx, int R) { return nx * 4 * R + 16; }
@@ -99,10 +173,14 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
     const int u = blockIdx.x;
     int slot, g_start, mg;
     if (u < sa.n_units) {
-        if (u >= __builtin_amdgcn_readfirstlane(sa.counts[1])) return;
-        g_start = __builtin_amdgcn_readfirstlane(sa.seg_offsets[u]);
-        mg = min(kSegTiles * 16, __builtin_amdgcn_readfirstlane(sa.seg_offsets[u + 1]) - g_start);
-        slot = __builtin_amdgcn_readfirstlane(sa.seg_slot[u]);
+        const int n_seg = __builtin_amdgcn_readfirstlane(sa.counts[1]);
+        const int sg = (sa.key_div > 0 && sa.n_units <= kSegMapMax)
+                           ? unit_segment(sa, u, n_seg, reinterpret_cast<int *>(lds))
+                           : (u < n_seg ? u : -1);
+        if (sg < 0) return;
+        g_start = __builtin_amdgcn_readfirstlane(sa.seg_offsets[sg]);
+        mg = min(kSegTiles * 16, __builtin_amdgcn_readfirstlane(sa.seg_offsets[sg + 1]) - g_start);
+        slot = __builtin_amdgcn_readfirstlane(sa.seg_slot[sg]);
     } else {
         const int rec = sa.tiles[(int64_t)(u - sa.n_units) * kTileWords + (lane & 31)];
         const int jt = __builtin_amdgcn_readlane(rec, kRecSegTile);
