@@ -37,14 +37,20 @@ int mfma_min_rows() { return t_mfma_min > 0 ? t_mfma_min : default_mfma_min(); }
 
 int tile_bound(int n, int S) { return tl::tile_bound_of(n, S); }
 
+// Multi-chunk metadata workspace: 64 bytes of counters, rows / keys /
+// offset+length per chunk row, then [chunk][slot] counts when that table
+// fits an assembling workgroup's LDS (the build then assembles in a second
+// launch that reads them).
+bool meta_hist(int n, int S) { return tl::meta_table_fits(tl::meta_chunks(n), S); }
+
 size_t meta_ws_bytes(int n, int S) {
-    (void)S;
     const int chunks = tl::meta_chunks(n);
     if (chunks <= 1) return 0;
-    return 64 + (size_t)3 * chunks * 1024 * sizeof(int32_t);
+    return 64 + (size_t)3 * chunks * 1024 * sizeof(int32_t) +
+           (meta_hist(n, S) ? (size_t)chunks * S * sizeof(int32_t) : 0);
 }
 
-tl::MetaWs carve_meta_ws(void *ws, int n) {
+tl::MetaWs carve_meta_ws(void *ws, int n, int S) {
     tl::MetaWs w{};
     if (tl::meta_chunks(n) <= 1) return w;
     char *b = static_cast<char *>(ws);
@@ -53,6 +59,7 @@ tl::MetaWs carve_meta_ws(void *ws, int n) {
     w.rows = reinterpret_cast<int32_t *>(b + 64);
     w.keys = w.rows + per;
     w.offlen = w.keys + per;
+    w.hist = meta_hist(n, S) ? w.offlen + per : nullptr;
     return w;
 }
 
@@ -134,7 +141,7 @@ int lora_meta_build(const int32_t *slot, int32_t n, int32_t num_slots, lora_meta
     if (need && (!ws || ws_bytes < need)) return LORA_EWORKSPACE;
     tl::MetaOut out{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
                     tile_bound(n, num_slots)};
-    return launched(tl::launch_meta_dense(slot, n, num_slots, out, carve_meta_ws(ws, n),
+    return launched(tl::launch_meta_dense(slot, n, num_slots, out, carve_meta_ws(ws, n, num_slots),
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -149,7 +156,7 @@ int lora_meta_from_offsets(const uint32_t *expert_offsets, int32_t num_experts, 
     tl::MetaOut out{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
                     tile_bound(n, num_slots)};
     return launched(tl::launch_meta_blocks(expert_offsets, expert_slot, num_experts, n, num_slots, out,
-                                           carve_meta_ws(ws, n), static_cast<hipStream_t>(stream)));
+                                           carve_meta_ws(ws, n, num_slots), static_cast<hipStream_t>(stream)));
 }
 
 int lora_shrink(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const uint16_t *a_pool,
@@ -224,8 +231,8 @@ int fused_call(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const ui
         if (!ws || ws_bytes < need || !aligned16(ws)) return LORA_EWORKSPACE;
         tl::MetaOut mo{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
                        tile_bound(n, num_slots)};
-        void *meta_ws = static_cast<char *>(ws) + plan.total_bytes;
-        if (n == 0) return launched(tl::launch_meta_dense(slot, n, num_slots, mo, carve_meta_ws(meta_ws, n), st));
+        const tl::MetaWs meta_ws = carve_meta_ws(static_cast<char *>(ws) + plan.total_bytes, n, num_slots);
+        if (n == 0) return launched(tl::launch_meta_dense(slot, n, num_slots, mo, meta_ws, st));
         d.x = x;
         d.ldx = ldx;
         d.a_pool = a_pool;
@@ -236,7 +243,7 @@ int fused_call(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const ui
         d.offset_start = offset_start;
         if (tl::fused_builds_meta(d, plan))
             return launched(tl::launch_fused(d, nullptr, nullptr, plan, ws, mfma_min_rows(), st, slot, &mo));
-        const hipError_t e = tl::launch_meta_dense(slot, n, num_slots, mo, carve_meta_ws(meta_ws, n), st);
+        const hipError_t e = tl::launch_meta_dense(slot, n, num_slots, mo, meta_ws, st);
         if (e != hipSuccess) return LORA_ELAUNCH;
         return launched(tl::launch_fused(d, meta.tiles, meta.counts, plan, ws, mfma_min_rows(), st));
     }
@@ -367,7 +374,7 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
                    reinterpret_cast<int32_t *>(b + lay.tiles), tile_bound(n, S)};
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
-                                       carve_meta_ws(b + lay.meta_ws, n), st);
+                                       carve_meta_ws(b + lay.meta_ws, n, S), st);
     if (e != hipSuccess) return LORA_ELAUNCH;
     if (n == 0) return LORA_OK;
     tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
@@ -412,7 +419,7 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, con
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (!reuse_routing) {
         const hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
-                                                 carve_meta_ws(b + lay.meta_ws, n), st);
+                                                 carve_meta_ws(b + lay.meta_ws, n, S), st);
         if (e != hipSuccess) return LORA_ELAUNCH;
     }
     if (n == 0) return LORA_OK;

@@ -61,13 +61,20 @@ struct MetaOut {
 // Workspace of a multi-chunk meta build: ctl[0] the single assembler's
 // ticket (unused when the build assembles in a second launch), ctl[1] invalid
 // rows (both zero between calls), then rows / keys / offset+length per chunk
-// row.
+// row, then (hist, when the [chunk][slot] table fits, else null) the rows of
+// each slot in each chunk, [chunk][S].
 struct MetaWs {
     int32_t *ctl;
     int32_t *rows;
     int32_t *keys;
     int32_t *offlen;
+    int32_t *hist;
 };
+constexpr int kMetaTable = 16384;    // LDS ints for an assembling workgroup's [chunk][slot] table and slot arrays
+constexpr int kSplitMaxChunks = 64;  // a split build's workgroups each read every chunk's slot counts
+__host__ __device__ inline bool meta_table_fits(int n_chunks, int S) {
+    return (long long)(4 + n_chunks) * S <= kMetaTable;
+}
 
 int meta_chunks(int n);
 size_t meta_dyn_lds(int n, int S);

@@ -31,11 +31,8 @@
 namespace tl {
 
 constexpr int kMT = kMetaChunk;  // threads per workgroup = rows per chunk
-constexpr int kMetaTable = 16384;  // LDS ints for the assembling workgroup's [chunk][slot] table and slot arrays
 constexpr int kAsmBatch = 8;       // chunks whose entries the assembling workgroup loads at once
-constexpr int kSplitMaxChunks = 64;  // a split build's workgroups each read every chunk's entries
 
-__host__ __device__ inline bool meta_table_fits(int n_chunks, int S) { return (long long)(4 + n_chunks) * S <= kMetaTable; }
 
 
 // MoE pair p = t*top_k + j: adapter l = lora_ids[t], expert e = topk_ids[p].
@@ -133,14 +130,36 @@ __device__ void meta_assemble(int n, int S, int n_chunks, MetaOut out, MetaWs ws
     const bool table = meta_table_fits(n_chunks, S);
     const bool writer = only < 0 || only == 0;  // writes the per-segment outputs and counts
     int *cb = dyn + 4 * S;
-    if (table) {
+    // One chunk's placement with the per-chunk slot counts at hand (a split
+    // build): each slot's rows in all chunks and in the chunks before this
+    // one, from [chunk][slot] counts, kAsmBatch chunks' loads in flight.
+    const bool from_hist = only >= 0 && ws.hist && table;
+    if (from_hist) {
+        for (int s = tid; s < S; s += kMT) {
+            int acc = 0, before = 0;
+            for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
+                int v[kAsmBatch];
+#pragma unroll
+                for (int u = 0; u < kAsmBatch; ++u) v[u] = c0 + u < n_chunks ? ws.hist[(int64_t)(c0 + u) * S + s] : 0;
+#pragma unroll
+                for (int u = 0; u < kAsmBatch; ++u) {
+                    if (c0 + u == only) before = acc;
+                    acc += v[u];
+                }
+            }
+            rc[s] = acc;
+            cb[(int64_t)only * S + s] = before;
+        }
+        __syncthreads();
+    }
+    if (table && !from_hist) {
         for (int i = tid; i < n_chunks * S; i += kMT) cb[i] = 0;
     }
-    for (int s = tid; s < S; s += kMT) rc[s] = 0;
+    for (int s = tid; !from_hist && s < S; s += kMT) rc[s] = 0;
     __syncthreads();
     // rows per slot (and per chunk): each run's first entry carries its length;
     // the loads of kAsmBatch chunks are issued before any is used
-    for (int c0 = 0; c0 < n_chunks; c0 += kAsmBatch) {
+    for (int c0 = 0; !from_hist && c0 < n_chunks; c0 += kAsmBatch) {
         uint32_t kb[kAsmBatch];
         int ob[kAsmBatch];
 #pragma unroll
@@ -160,7 +179,7 @@ __device__ void meta_assemble(int n, int S, int n_chunks, MetaOut out, MetaWs ws
         }
     }
     __syncthreads();
-    if (table) {
+    if (table && !from_hist) {
         for (int s2 = tid; s2 < S; s2 += kMT) {
             int acc = 0;
             for (int cc = 0; cc < n_chunks; ++cc) {
@@ -345,7 +364,16 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
         ws.offlen[idx] = off | (len << 16);
     }
     if (tid == 0 && n_inv_chunk) atomicAdd(&ws.ctl[1], n_inv_chunk);
-    if (split) return;  // meta_assemble_kernel follows in the same stream
+    if (split) {  // meta_assemble_kernel follows in the same stream
+        if (ws.hist) {  // this chunk's rows of every slot (the run lengths, zero for absent slots)
+            for (int s = tid; s < S; s += kMT) dyn[s] = 0;
+            __syncthreads();
+            if (leader && act) dyn[key] = len;
+            __syncthreads();
+            for (int s = tid; s < S; s += kMT) ws.hist[(int64_t)c * S + s] = dyn[s];
+        }
+        return;
+    }
     __threadfence();
     __syncthreads();
     if (tid == 0) sh.flag_last = atomic_add_acqrel(&ws.ctl[0], 1) == n_chunks - 1;
@@ -424,8 +452,8 @@ static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hip
     // every workgroup of the second launch reads all chunks' entries (work
     // quadratic in the chunk count), so very long batches assemble alone
     const int split = chunks > 1 && chunks <= kSplitMaxChunks && meta_table_fits(chunks, S);
-    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), split ? 0 : dyn, st, src, n, S, chunks, out, ws,
-                       split);
+    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), split ? (size_t)S * sizeof(int) : dyn, st, src, n,
+                       S, chunks, out, ws, split);
     if (!split) return hipGetLastError();
     if (dyn > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_assemble_kernel),
