@@ -28,6 +28,8 @@
 #include "kernels.h"
 #include "slot_meta.h"
 
+#include <algorithm>
+
 namespace tl {
 
 constexpr int kMT = kMetaChunk;  // threads per workgroup = rows per chunk
@@ -114,6 +116,43 @@ __device__ __forceinline__ void radix_pass(uint32_t &key, int32_t &val, int shif
     __syncthreads();
 }
 
+
+// The chunk sorted by key in one pass (stable, as the radix passes), for
+// S <= kBallotSortSlots: each wave ranks its lanes among equal keys with one
+// ballot per key bit (few_rank), a [key][wave] table of group sizes is
+// scanned key-major in wave order, and every entry moves to its position.
+// tab: (S + 1) * 16 ints of LDS.
+constexpr int kBallotSortSlots = 512;
+__device__ __forceinline__ void ballot_sort(uint32_t &key, int32_t &val, int S, MetaShared &sh, int *tab) {
+    constexpr int W = kMT / kWave;
+    const int tid = threadIdx.x, w = wave_id();
+    const int n_ent = (S + 1) * W;
+    for (int i = tid; i < n_ent; i += kMT) tab[i] = 0;
+    __syncthreads();
+    int group;
+    const int rank = few_rank((int)key, true, S + 1, group);
+    if (rank == 0) tab[key * W + w] = group;
+    __syncthreads();
+    const int per = (n_ent + kMT - 1) / kMT;  // contiguous entries per thread
+    const int e0 = min(n_ent, tid * per), e1 = min(n_ent, e0 + per);
+    int loc = 0;
+    for (int i = e0; i < e1; ++i) loc += tab[i];
+    int total;
+    int base = block_excl_scan<kMT>(loc, sh.scan, total);
+    for (int i = e0; i < e1; ++i) {
+        const int v = tab[i];
+        tab[i] = base;
+        base += v;
+    }
+    __syncthreads();
+    const int pos = tab[key * W + w] + rank;
+    sh.key[pos] = key;
+    sh.val[pos] = val;
+    __syncthreads();
+    key = sh.key[tid];
+    val = sh.val[tid];
+    __syncthreads();
+}
 
 // Assembly of a multi-chunk build from the chunks' sorted entries in the
 // workspace: rows per slot (and per chunk), a scan over slots, then the
@@ -305,8 +344,12 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
     uint32_t key = (real && raw >= 0 && raw < S) ? (uint32_t)raw : (uint32_t)S;
     int32_t val = e;
 
-    const int nbits = 32 - __clz(S);  // bits holding 0..S
-    for (int shift = 0; shift < nbits; shift += 4) radix_pass(key, val, shift, sh);
+    if (S <= kBallotSortSlots) {
+        ballot_sort(key, val, S, sh, dyn);
+    } else {
+        const int nbits = 32 - __clz(S);  // bits holding 0..S
+        for (int shift = 0; shift < nbits; shift += 4) radix_pass(key, val, shift, sh);
+    }
 
     // runs of equal keys in the sorted chunk
     const uint32_t prev = tid > 0 ? sh.key[tid - 1] : 0xFFFFFFFFu;
@@ -445,15 +488,19 @@ static hipError_t launch_meta(Src src, int n, int S, MetaOut out, MetaWs ws, hip
         }
     }
     const int chunks = meta_chunks(n);
-    const size_t dyn = meta_dyn_lds(n, S);
-    if (dyn > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_kernel<Src>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    // every workgroup of the second launch reads all chunks' entries (work
-    // quadratic in the chunk count), so very long batches assemble alone
+    // every chunk workgroup's LDS: the one-pass sort's table, the assembly's
+    // table and slot arrays (the single assembler), the chunk's slot counts
+    // (a split build)
     const int split = chunks > 1 && chunks <= kSplitMaxChunks && meta_table_fits(chunks, S);
-    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), split ? (size_t)S * sizeof(int) : dyn, st, src, n,
-                       S, chunks, out, ws, split);
+    const size_t sort_lds = S <= kBallotSortSlots ? (size_t)(S + 1) * (kMT / kWave) * sizeof(int) : 0;
+    const size_t dyn = meta_dyn_lds(n, S);
+    const size_t first = std::max(sort_lds, split ? (size_t)S * sizeof(int) : dyn);
+    if (first > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_kernel<Src>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)first);
+    // every workgroup of the second launch reads all chunks' slot counts
+    // (work quadratic in the chunk count), so very long batches assemble alone
+    hipLaunchKernelGGL(meta_kernel<Src>, dim3(chunks), dim3(kMT), first, st, src, n, S, chunks, out, ws, split);
     if (!split) return hipGetLastError();
     if (dyn > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(meta_assemble_kernel),
