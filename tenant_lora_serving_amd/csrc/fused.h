@@ -608,7 +608,16 @@ struct XaSrc {
     int *ctl;
     int *ok;    // LDS
     float *rw;  // LDS: the tile rows' weights (ops with row weights)
+    int *count;  // the tile's finished-consumer count, or null (counted by the caller)
 };
+
+// A consumer counts itself at its tile as soon as it holds the tile's xa
+// (every unit of the call has read the call's tag by then: see finish), so
+// the count's round trip overlaps the unit's expand; the caller takes the
+// returned old value at the end.  -1: nothing counted.
+__device__ __forceinline__ int count_consumer(const XaSrc &xs) {
+    return (xs.count && threadIdx.x == 0) ? atomic_add_relaxed(xs.count, 1) : -1;
+}
 
 // Row weights of the tile into xs.rw (wave 0, lanes 0..15); called after the
 // unit's B and y loads are issued and before wait_pieces, whose barriers
@@ -801,8 +810,8 @@ __device__ __forceinline__ void valu_load_y(const Op &op, const Hdr &h, int c, i
 // starts, which frees the registers (and LDS) of the prefetch for calls
 // whose tiles are mostly on the MFMA path.
 template <int WM, int NRS, class Op>
-__device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
-                                            const XaSrc &xs, char *lds) {
+__device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
+                                           const XaSrc &xs, char *lds) {
     constexpr bool WIDE = WM != 0, PREFETCH = WM == 1;
     const int lane = lane_id(), w = wave_id();
     const int R = Op::kRank ? Op::kRank : op.R, m = h.m;
@@ -821,10 +830,11 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
     uint16_t *bst = reinterpret_cast<uint16_t *>(lds + kXaBytes) + w * kBStage;
     if (tr) valu_transpose(raw, R, bst, bq);
     load_row_weights(op, h, xs);
-    if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
+    if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return count_consumer(xs);
     stage_xa_passes<false, Op::kRowWeights>(xs.pt, xs.P, op.n_rr(), xs.xb, R, m, xs.sc, xs.rw, xs.tag, xs.ctl,
                                             lds);
     __syncthreads();
+    const int counted = count_consumer(xs);
     const float *xf = reinterpret_cast<const float *>(lds);
     for (int b = 0; b < nb; ++b) {
         const int c = c0 + kEB * b + cl;
@@ -880,6 +890,7 @@ __device__ __forceinline__ void expand_valu(const Op &op, const Hdr &h, int c0, 
             for (int j = 0; j < kTileRows; ++j) yv[j] = yv_n[j];
         }
     }
+    return counted;
 }
 
 // MFMA expand of columns [c0, c1) in batches of kEB: in a batch, wave w owns
@@ -920,8 +931,8 @@ __device__ __forceinline__ void mfma_load_y(uint16_t *const (&yr)[4], int cw0, i
 }
 
 template <int NRS, bool WIDE, class Op>
-__device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
-                                            const XaSrc &xs, char *lds) {
+__device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
+                                           const XaSrc &xs, char *lds) {
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
     const int R = Op::kRank ? Op::kRank : op.R;
@@ -942,10 +953,11 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
     mfma_load_b<NRS>(op, h, c0 + 128 * w, c1, R, bo);
     mfma_load_y(yr, c0 + 128 * w, c1, add_inputs, yv);
     load_row_weights(op, h, xs);
-    if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return;
+    if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return count_consumer(xs);
     stage_xa<true, Op::kRowWeights, 2 * NRS>(xs.pt, xs.P, op.n_rr(), xs.xb, R, h.m, xs.sc, xs.rw, xs.tag, xs.ctl,
                                              lds);
     __syncthreads();
+    const int counted = count_consumer(xs);
     const uint16_t *xl = reinterpret_cast<const uint16_t *>(lds) + col * 2 * R;
     u32x4_t hv[NRS], lv[NRS];
 #pragma unroll
@@ -1006,6 +1018,7 @@ __device__ __forceinline__ void expand_mfma(const Op &op, const Hdr &h, int c0, 
             for (int ct = 0; ct < 8; ++ct) yv[ct] = yv_n[ct];
         }
     }
+    return counted;
 }
 
 // MFMA expand of two consecutive tiles of one segment (wide calls, ranks up
@@ -1292,16 +1305,24 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
         int l, c0, c1;
         chunk_of(op, cc, fa.EC, l, c0, c1);
         // the last consumer of a tile counts the tile as finished; the last
-        // finished tile of the call advances the generation (two levels, so
-        // no single address takes one atomic per consumer)
-        auto finish = [&](int tt) {
-            int *tile_done = reinterpret_cast<int *>(fa.flags + (int64_t)tt * kFlagWords + kFlagWords - 1);
-            if (atomic_add_relaxed(tile_done, 1) == C - 1) {
-                if (atomic_add_relaxed(fa.ctl + kCtlDone, 1) == n_tiles - 1) {
-                    store_relaxed(fa.ctl + kCtlDone, 0);
-                    store_relaxed(fa.ctl + kCtlGen, (int)tag);
-                }
+        // finished tile of the call stores the call's tag as the last one
+        // (two levels, so no single address takes one atomic per consumer).
+        // A consumer counts once it holds its tile's xa: every unit of the
+        // call has read the call's tag by then (each consumer at its start,
+        // each producer before raising the flags its consumers waited for),
+        // so the next call can take the next tag; what the unit still does
+        // (its expand, its stores) is ordered before the next call by the
+        // stream.
+        int *tile_done = reinterpret_cast<int *>(fa.flags + (int64_t)t * kFlagWords + kFlagWords - 1);
+        auto tile_finished = [&]() {
+            if (atomic_add_relaxed(fa.ctl + kCtlDone, 1) == n_tiles - 1) {
+                store_relaxed(fa.ctl + kCtlDone, 0);
+                store_relaxed(fa.ctl + kCtlGen, (int)tag);
             }
+        };
+        auto finish = [&](int tt) {
+            int *td = reinterpret_cast<int *>(fa.flags + (int64_t)tt * kFlagWords + kFlagWords - 1);
+            if (atomic_add_relaxed(td, 1) == C - 1) tile_finished();
         };
         // wide calls: MFMA segments of rank <= 32 are expanded two tiles at a
         // time by the units of the pair's first tile, which count both tiles
@@ -1313,9 +1334,9 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
                 const Hdr h1 = load_hdr(fa.tiles, t + 1);
                 const float sc = op.scale_of(h.slot);
                 const XaSrc xs0{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P,
-                                op.xblk(l), true, sc, tag, fa.ctl, &ok, rw};
+                                op.xblk(l), true, sc, tag, fa.ctl, &ok, rw, nullptr};
                 const XaSrc xs1{fa.part + (int64_t)(t + 1) * P * n_rr * 16, fa.flags + (int64_t)(t + 1) * kFlagWords,
-                                P, op.xblk(l), true, sc, tag, fa.ctl, &ok, rw + kTileRows};
+                                P, op.xblk(l), true, sc, tag, fa.ctl, &ok, rw + kTileRows, nullptr};
                 expand_mfma_pair<NRS>(op, h, h1, c0, c1, fa.add_inputs != 0, xs0, xs1, lds);
                 if (threadIdx.x == 0) {
                     finish(t);
@@ -1325,12 +1346,11 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
             }
         }
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P, op.xblk(l),
-                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw};
-        if (h.mseg >= fa.mfma_min)
-            expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
-        else
-            expand_valu<WM, NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
-        if (threadIdx.x == 0) finish(t);
+                       fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw, tile_done};
+        const int counted = h.mseg >= fa.mfma_min
+                                ? expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds)
+                                : expand_valu<WM, NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
+        if (threadIdx.x == 0 && counted == C - 1) tile_finished();
         return;
     }
     // zero rows of pairs that get no delta (MoE only)
