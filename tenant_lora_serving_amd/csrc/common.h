@@ -113,13 +113,23 @@ __device__ __forceinline__ float group_sum(float v, int lg) {
 }
 
 // ---------------------------------------------------------------- wave/block scans
+// Inclusive scans over the 64 lanes of a wave with DPP moves, no LDS
+// traffic: shifts by 1, 2, 4 and 8 lanes within each row of 16 lanes (a
+// lane whose source lies outside its row adds 0), then lane 15 of each row
+// added to the next row (rows 1 and 3) and lane 31 added to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_in(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, true);
+}
+constexpr int kDppRowShr = 0x110, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int t = __shfl_up(v, d, kWave);
-        if (lane >= d) v += t;
-    }
+    v += dpp_in<kDppRowShr + 1, 0xf>(v);
+    v += dpp_in<kDppRowShr + 2, 0xf>(v);
+    v += dpp_in<kDppRowShr + 4, 0xf>(v);
+    v += dpp_in<kDppRowShr + 8, 0xf>(v);
+    v += dpp_in<kDppBcast15, 0xa>(v);
+    v += dpp_in<kDppBcast31, 0xc>(v);
     return v;
 }
 
@@ -134,13 +144,7 @@ struct Int3 {
 __device__ __forceinline__ Int3 operator+(Int3 x, Int3 y) { return {x.a + y.a, x.b + y.b, x.c + y.c}; }
 
 __device__ __forceinline__ Int3 wave_incl_scan3(Int3 v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        Int3 t = {__shfl_up(v.a, d, kWave), __shfl_up(v.b, d, kWave), __shfl_up(v.c, d, kWave)};
-        if (lane >= d) v = v + t;
-    }
-    return v;
+    return {wave_incl_scan(v.a), wave_incl_scan(v.b), wave_incl_scan(v.c)};
 }
 
 // Exclusive scan over the NT threads of a block; every thread must call it.
