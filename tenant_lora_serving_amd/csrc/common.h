@@ -66,9 +66,35 @@ __device__ __forceinline__ u32x4_t ld16(const void *p) {
 }
 __device__ __forceinline__ void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
-// Streamed once: keep it out of the caches' way.
+// Cache policy.  Bytes a kernel touches once -- A rows, output rows, the B
+// rows of adapters that serve few rows -- are loaded and stored with the
+// nontemporal hint, so they do not push out of L2 what is read again: x rows
+// gathered by the experts of a token, B rows shared by the tiles of a long
+// segment.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4_t ld16_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+__device__ __forceinline__ uint32_t ld4_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+__device__ __forceinline__ uint2 ld8_stream(const void *p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st4_stream(void *p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
+}
+__device__ __forceinline__ void st8_stream(void *p, uint2 v) {
+    __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t *>(p));
+}
+__device__ __forceinline__ void st16_stream(void *p, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+}
+// A B row load: streamed (S) or kept in the caches for later tiles.
+template <bool S>
+__device__ __forceinline__ u32x4_t ld16_b(const void *p) {
+    return S ? ld16_stream(p) : ld16(p);
 }
 
 // ---------------------------------------------------------------- buffer addressing
@@ -82,17 +108,20 @@ constexpr uint32_t kOob = 0x80000000u;  // an offset past the end of every resou
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufWord3);
 }
+// (cache-policy operand: 0 default, kNt the nontemporal hint)
+constexpr int kNt = 2;
+template <int CP = 0>
 __device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP));
 }
+template <int CP = 0>
 __device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t off) {
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP));
     return make_uint2(v.x, v.y);
 }
+template <int CP = 0>
 __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, off, 0, CP);
 }
 
 // ---------------------------------------------------------------- DPP lane sums

@@ -337,7 +337,7 @@ __device__ __forceinline__ void prefetch_y(const Op &op, const Tile &h, int cw0,
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int j = 4 * p + (lane >> 4);
-        yv[p] = (add_inputs && j < h.m && cy < cend) ? ld16(op.yrow(h.rows[j]) + cy) : zero4();
+        yv[p] = (add_inputs && j < h.m && cy < cend) ? ld16_stream(op.yrow(h.rows[j]) + cy) : zero4();
     }
 }
 
@@ -366,9 +366,9 @@ __device__ __forceinline__ void store_tile(const Op &op, const Tile &h, const fl
                 o[6] += bf_lo(yv[p].w);
                 o[7] += bf_hi(yv[p].w);
             }
-            st16(op.yrow(h.rows[j]) + cy,
-                 u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                         pack_bf16x2(o[6], o[7])});
+            st16_stream(op.yrow(h.rows[j]) + cy,
+                        u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                pack_bf16x2(o[6], o[7])});
         }
     }
 }

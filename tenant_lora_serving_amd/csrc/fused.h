@@ -111,7 +111,7 @@ __device__ __forceinline__ void load_x(const Op &op, const Hdr &h, int k0, int k
     for (int u = 0; u < 4; ++u) {
         const int j = w + 4 * u;
         const uint16_t *xp = j < h.m ? op.xrow(hdr_row(h, j)) : nullptr;
-        xv[u] = (xp && k < k1) ? ld16(xp + k) : zero4();
+        xv[u] = (xp && k < k1) ? (Op::kXOnce ? ld16_stream(xp + k) : ld16(xp + k)) : zero4();
     }
 }
 __device__ __forceinline__ void store_x(const u32x4_t (&xv)[4], uint16_t *xs) {
@@ -637,7 +637,7 @@ __device__ __forceinline__ void load_row_weights(const Op &op, const Hdr &h, con
 // rows past m are computed from row m - 1's xa and not stored): both of the
 // lane's columns over all R ranks.  Ranks 0..31 are already in bq; later
 // blocks are loaded here, as are ranks 0..31 again for jb > 0 when R > 32.
-template <int JB, class Op>
+template <int JB, bool BS, class Op>
 __device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, int c, bool cok, bool add_inputs,
                                            const uint16_t *bp, int R, u32x4_t (&bq)[2][4],
                                            const uint32_t (&yv)[kTileRows], const float *xf) {
@@ -648,7 +648,7 @@ __device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, in
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    bq[cc][q] = (bp && r0 + 8 * q < R) ? ld16(bp + cc * R + r0 + 8 * q) : zero4();
+                    bq[cc][q] = (bp && r0 + 8 * q < R) ? ld16_b<BS>(bp + cc * R + r0 + 8 * q) : zero4();
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -693,7 +693,7 @@ __device__ __forceinline__ void valu_rows4(const Op &op, const Hdr &h, int m, in
                 v0 += bf_lo(yv[JB + j]);
                 v1 += bf_hi(yv[JB + j]);
             }
-            *reinterpret_cast<uint32_t *>(op.yrow(hdr_row(h, JB + j)) + c) = pack_bf16x2(v0, v1);
+            st4_stream(op.yrow(hdr_row(h, JB + j)) + c, pack_bf16x2(v0, v1));
         }
     }
 }
@@ -731,7 +731,7 @@ __device__ __forceinline__ void valu_rows4_r16(const Op &op, const Hdr &h, int m
                 v0 += bf_lo(yv[JB + j]);
                 v1 += bf_hi(yv[JB + j]);
             }
-            *reinterpret_cast<uint32_t *>(op.yrow(hdr_row(h, JB + j)) + c) = pack_bf16x2(v0, v1);
+            st4_stream(op.yrow(hdr_row(h, JB + j)) + c, pack_bf16x2(v0, v1));
         }
     }
 }
@@ -750,7 +750,7 @@ __device__ __forceinline__ void valu_rows4_r16(const Op &op, const Hdr &h, int m
 // is what a decode-sized call is short of.
 __device__ __forceinline__ int bstage_off(int i) { return i * 8 + (i >> 4) * 8; }  // chunk i -> bf16 offset
 
-template <class Op>
+template <bool BS, class Op>
 __device__ __forceinline__ void valu_load_raw(const Op &op, const Hdr &h, int cw, int c1, int R,
                                               u32x4_t (&raw)[8]) {
     const int lane = lane_id();
@@ -760,7 +760,7 @@ __device__ __forceinline__ void valu_load_raw(const Op &op, const Hdr &h, int cw
     for (int u = 0; u < 8; ++u) {
         const int i = lane + 64 * u;
         const bool ok = base && u < nl && cw + (i * 8) / R < c1;
-        raw[u] = ok ? ld16(base + i * 8) : zero4();
+        raw[u] = ok ? ld16_b<BS>(base + i * 8) : zero4();
     }
 }
 
@@ -783,14 +783,14 @@ __device__ __forceinline__ void valu_transpose(const u32x4_t (&raw)[8], int R, u
     __builtin_amdgcn_wave_barrier();
 }
 
-template <class Op>
+template <bool BS, class Op>
 __device__ __forceinline__ void valu_load_b(const Op &op, const Hdr &h, int c, int c1, int R, const uint16_t *&bp,
                                             u32x4_t (&bq)[2][4]) {
     bp = c < c1 ? op.brow(h.slot, c) : nullptr;  // rows c and c+1 are adjacent
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bq[cc][q] = (bp && 8 * q < R) ? ld16(bp + cc * R + 8 * q) : zero4();
+        for (int q = 0; q < 4; ++q) bq[cc][q] = (bp && 8 * q < R) ? ld16_b<BS>(bp + cc * R + 8 * q) : zero4();
 }
 
 template <class Op>
@@ -799,7 +799,7 @@ __device__ __forceinline__ void valu_load_y(const Op &op, const Hdr &h, int c, i
 #pragma unroll
     for (int j = 0; j < kTileRows; ++j)
         yv[j] = (add_inputs && c < c1 && j < h.m)
-                    ? *reinterpret_cast<const uint32_t *>(op.yrow(hdr_row(h, j)) + c)
+                    ? ld4_stream(op.yrow(hdr_row(h, j)) + c)
                     : 0u;
 }
 
@@ -813,6 +813,7 @@ template <int WM, int NRS, class Op>
 __device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                            const XaSrc &xs, char *lds) {
     constexpr bool WIDE = WM != 0, PREFETCH = WM == 1;
+    constexpr bool BS = WM != 2;  // B streamed unless the call's slots average many rows
     const int lane = lane_id(), w = wave_id();
     const int R = Op::kRank ? Op::kRank : op.R, m = h.m;
     const int nb = WIDE ? (c1 - c0 + kEB - 1) / kEB : 1;
@@ -822,9 +823,9 @@ __device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, i
     uint32_t yv[kTileRows];
     const int cl = 128 * w + 2 * lane;
     if (tr)
-        valu_load_raw(op, h, c0 + 128 * w, c1, R, raw);
+        valu_load_raw<BS>(op, h, c0 + 128 * w, c1, R, raw);
     else
-        valu_load_b(op, h, c0 + cl, c1, R, bp, bq);
+        valu_load_b<BS>(op, h, c0 + cl, c1, R, bp, bq);
     valu_load_y(op, h, c0 + cl, c1, add_inputs, yv);
     // the first batch's B reaches its lanes while the producers still run
     uint16_t *bst = reinterpret_cast<uint16_t *>(lds + kXaBytes) + w * kBStage;
@@ -841,7 +842,7 @@ __device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, i
         const bool cok = c < c1;
         if (tr && b > 0) valu_transpose(raw, R, bst, bq);
         if (WIDE && !PREFETCH && b > 0) {
-            valu_load_b(op, h, c, c1, R, bp, bq);
+            valu_load_b<BS>(op, h, c, c1, R, bp, bq);
             valu_load_y(op, h, c, c1, add_inputs, yv);
         }
         const uint16_t *bp_n = nullptr;
@@ -849,9 +850,9 @@ __device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, i
         uint32_t yv_n[kTileRows];
         if (PREFETCH && b + 1 < nb) {
             if (tr)
-                valu_load_raw(op, h, c0 + kEB * (b + 1) + 128 * w, c1, R, raw);
+                valu_load_raw<BS>(op, h, c0 + kEB * (b + 1) + 128 * w, c1, R, raw);
             else
-                valu_load_b(op, h, c + kEB, c1, R, bp_n, bq_n);
+                valu_load_b<BS>(op, h, c + kEB, c1, R, bp_n, bq_n);
             valu_load_y(op, h, c + kEB, c1, add_inputs, yv_n);
         }
         if constexpr (!WIDE) {
@@ -874,10 +875,10 @@ __device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, i
             }
         }
         // rows in blocks of 4, no per-row branch inside a block
-        if (m > 0) valu_rows4<0>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-        if (m > 4) valu_rows4<4>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-        if (m > 8) valu_rows4<8>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
-        if (m > 12) valu_rows4<12>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 0) valu_rows4<0, BS>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 4) valu_rows4<4, BS>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 8) valu_rows4<8, BS>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
+        if (m > 12) valu_rows4<12, BS>(op, h, m, c, cok, add_inputs, bp, R, bq, yv, xf);
         if (PREFETCH && b + 1 < nb) {
             if (!tr) {
                 bp = bp_n;
@@ -898,7 +899,7 @@ __device__ __forceinline__ int expand_valu(const Op &op, const Hdr &h, int c0, i
 // D[column][tile row] = B[column][ranks] . (xa_hi + xa_lo)[tile row][ranks]
 // as two bf16 MFMAs per 32 ranks (NRS rank steps).  A later batch's B and y
 // are loaded once the MFMAs have consumed the previous batch's B.
-template <int NRS, class Op>
+template <int NRS, bool BS, class Op>
 __device__ __forceinline__ void mfma_load_b(const Op &op, const Hdr &h, int cw0, int c1, int R,
                                             u32x4_t (&bo)[8][NRS]) {
     const int lane = lane_id();
@@ -910,7 +911,7 @@ __device__ __forceinline__ void mfma_load_b(const Op &op, const Hdr &h, int cw0,
 #pragma unroll
         for (int s = 0; s < NRS; ++s) {
             const int rk = 32 * s + 8 * kq;
-            bo[ct][s] = (bp && rk < R) ? ld16(bp + rk) : zero4();
+            bo[ct][s] = (bp && rk < R) ? ld16_b<BS>(bp + rk) : zero4();
         }
     }
 }
@@ -925,12 +926,12 @@ __device__ __forceinline__ void mfma_load_y(uint16_t *const (&yr)[4], int cw0, i
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int cy = cw0 + 64 * hf + cl;
-            yv[4 * hf + j] = (add_inputs && yr[j] && cy < c1) ? *reinterpret_cast<const uint2 *>(yr[j] + cy)
+            yv[4 * hf + j] = (add_inputs && yr[j] && cy < c1) ? ld8_stream(yr[j] + cy)
                                                               : make_uint2(0u, 0u);
         }
 }
 
-template <int NRS, bool WIDE, class Op>
+template <int NRS, bool WIDE, bool BS, class Op>
 __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                            const XaSrc &xs, char *lds) {
     const int lane = lane_id(), w = wave_id();
@@ -950,7 +951,7 @@ __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, i
     float *dt = reinterpret_cast<float *>(lds + kXaBytes) + w * kTileRows * kDtStride;
     u32x4_t bo[8][NRS];
     uint2 yv[8];
-    mfma_load_b<NRS>(op, h, c0 + 128 * w, c1, R, bo);
+    mfma_load_b<NRS, BS>(op, h, c0 + 128 * w, c1, R, bo);
     mfma_load_y(yr, c0 + 128 * w, c1, add_inputs, yv);
     load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return count_consumer(xs);
@@ -985,7 +986,7 @@ __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, i
             }
             if (WIDE && hf == 1 && b + 1 < nb) {
                 // the MFMAs above were the last readers of this batch's B
-                mfma_load_b<NRS>(op, h, cw0 + kEB, c1, R, bo);
+                mfma_load_b<NRS, BS>(op, h, cw0 + kEB, c1, R, bo);
                 mfma_load_y(yr, cw0 + kEB, c1, add_inputs, yv_n);
             }
             // the half's 16 x 64 block through the wave's LDS tile: written in
@@ -1007,8 +1008,7 @@ __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, i
                         v[2] += bf_lo(yy.y);
                         v[3] += bf_hi(yy.y);
                     }
-                    *reinterpret_cast<uint2 *>(yr[j] + cy) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    st8_stream(yr[j] + cy, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -1045,7 +1045,7 @@ __device__ __forceinline__ void expand_mfma_pair(const Op &op, const Hdr &h0, co
     float *dt = reinterpret_cast<float *>(lds + 2 * kXaBytes) + w * kTileRows * kDtStride;
     u32x4_t bo[8][NRS];
     uint2 yv[2][8];
-    mfma_load_b<NRS>(op, h0, c0 + 128 * w, c1, R, bo);
+    mfma_load_b<NRS, false>(op, h0, c0 + 128 * w, c1, R, bo);
     mfma_load_y(yr[0], c0 + 128 * w, c1, add_inputs, yv[0]);
     mfma_load_y(yr[1], c0 + 128 * w, c1, add_inputs, yv[1]);
     load_row_weights(op, h0, xs0);
@@ -1087,7 +1087,7 @@ __device__ __forceinline__ void expand_mfma_pair(const Op &op, const Hdr &h0, co
                         d[i] = mfma_16x16x32(bo[4 * hf + i][s], lv[rt][s], d[i]);
                     }
                 }
-                if (hf == 1 && rt == 1 && b + 1 < nb) mfma_load_b<NRS>(op, h0, cw0 + kEB, c1, R, bo);
+                if (hf == 1 && rt == 1 && b + 1 < nb) mfma_load_b<NRS, false>(op, h0, cw0 + kEB, c1, R, bo);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<f32x4_t *>(dt + col * kDtStride + 16 * i + 4 * kq) = d[i];
@@ -1106,8 +1106,7 @@ __device__ __forceinline__ void expand_mfma_pair(const Op &op, const Hdr &h0, co
                             v[2] += bf_lo(yy.y);
                             v[3] += bf_hi(yy.y);
                         }
-                        *reinterpret_cast<uint2 *>(yr[rt][j] + cy) =
-                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        st8_stream(yr[rt][j] + cy, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
@@ -1348,7 +1347,7 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
         const XaSrc xs{fa.part + (int64_t)t * P * n_rr * 16, fa.flags + (int64_t)t * kFlagWords, P, op.xblk(l),
                        fa.EC > kEB, op.scale_of(h.slot), tag, fa.ctl, &ok, rw, tile_done};
         const int counted = h.mseg >= fa.mfma_min
-                                ? expand_mfma<NRS, WM != 0>(op, h, c0, c1, fa.add_inputs != 0, xs, lds)
+                                ? expand_mfma<NRS, WM != 0, WM != 2>(op, h, c0, c1, fa.add_inputs != 0, xs, lds)
                                 : expand_valu<WM, NRS>(op, h, c0, c1, fa.add_inputs != 0, xs, lds);
         if (threadIdx.x == 0 && counted == C - 1) tile_finished();
         return;
@@ -1361,7 +1360,7 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
     const int l = zf.lora[pair / zf.top_k], ex = zf.topk[pair];
     if (l >= 0 && l < zf.L && ex >= 0 && ex < zf.E) return;
     uint16_t *o = op.yrow(pair);
-    for (int c = (tid & 15) * 8; c < op.n_out; c += 128) st16(o + c, zero4());
+    for (int c = (tid & 15) * 8; c < op.n_out; c += 128) st16_stream(o + c, zero4());
 }
 
 // ============================================================ host side

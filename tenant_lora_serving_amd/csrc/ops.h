@@ -27,6 +27,7 @@ struct DenseOp {
     int k_in, R, n_sh, n_out, col0, n_sl;
     int off[kMaxSlices + 1];
     static constexpr bool kRowWeights = false;
+    static constexpr bool kXOnce = true;  // each x element is read by one unit
     static constexpr int kRank = 0;  // R is a runtime value
     static constexpr bool kBuild = false;  // tile records come from the metadata
 
@@ -91,6 +92,7 @@ struct MoeOp {
     float sc;
     int k_in, R, n_sh, n_out, E, inter, shared;
     static constexpr bool kRowWeights = false;
+    static constexpr bool kXOnce = false;  // a token's x row serves its top_k pairs
     static constexpr bool kAddInputs = false;  // out is written, not added to
     static constexpr int kRank = 0;
     static constexpr bool kBuild = false;
@@ -191,6 +193,7 @@ struct MoeW2Op {
     float sc;
     int k_in, R, n_sh, n_out, E;
     static constexpr bool kRowWeights = true;
+    static constexpr bool kXOnce = true;  // x rows are per pair
     static constexpr int kRank = 0;
     static constexpr bool kBuild = false;
 

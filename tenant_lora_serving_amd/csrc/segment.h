@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
         const int l = zf.lora[pair / zf.top_k], ex = zf.topk[pair];
         if (l >= 0 && l < zf.L && ex >= 0 && ex < zf.E) return;
         uint16_t *o = op.yrow(pair);
-        for (int cc = (tid & 15) * 8; cc < op.n_out; cc += 128) st16(o + cc, zero4());
+        for (int cc = (tid & 15) * 8; cc < op.n_out; cc += 128) st16_stream(o + cc, zero4());
         return;
     }
     if (blockIdx.x == 0 && tid == 0)  // the call's tag, for later calls that share the workspace
@@ -229,13 +229,13 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
         const int k = s * kSegK + 8 * (tid & 31);
         const bool kok = k < K;
 #pragma unroll
-        for (int i = 0; i < XQ; ++i) xv[i] = buf_ld16(rx, kok ? xo[i] + 2 * k : kOob);
+        for (int i = 0; i < XQ; ++i) xv[i] = buf_ld16<Op::kXOnce ? kNt : 0>(rx, kok ? xo[i] + 2 * k : kOob);
         // thread chunk i covers rank rows 8i .. 8i + 7 (one slice: R is a multiple of 8)
 #pragma unroll
         for (int i = 0; i < AQ; ++i) {
             const int row = (tid >> 5) + 8 * i;
             const int sg = (8 * i) / RK;
-            av[i] = buf_ld16(sg == 0 ? ra0 : ra1, (row < n_rr && kok) ? op.a_off(row - sg * RK, k) : kOob);
+            av[i] = buf_ld16<kNt>(sg == 0 ? ra0 : ra1, (row < n_rr && kok) ? op.a_off(row - sg * RK, k) : kOob);
         }
     };
     auto stage = [&](const u32x4_t (&xv)[XQ], const u32x4_t (&av)[AQ]) {
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
         for (int ct = 0; ct < 4; ++ct) {
             const int cw = cw0 + 16 * ct + c;  // column within window l
             const int rk = RK <= 16 ? 8 * (kq % QH) : 8 * kq;
-            bv[ct] = buf_ld16(l == 0 ? rb0 : rb1, (q < n_chunks && cw < W) ? op.b_off(l, cw, rk) : kOob);
+            bv[ct] = buf_ld16<kNt>(l == 0 ? rb0 : rb1, (q < n_chunks && cw < W) ? op.b_off(l, cw, rk) : kOob);
         }
     };
     // the wave's chunks q = w + 4 j; PB chunks of B in flight (the shrink's
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
                 // (the shuffle runs in every lane: a lane it reads from must be active)
                 const int pr = __shfl(rt_pid, row, kWave);
                 yoff[j] = (row < mrt && col < c1) ? op.y_off(pr, col) : kOob;
-                if constexpr (Op::kAddInputs) yv[j] = buf_ld8(ry, yoff[j]);
+                if constexpr (Op::kAddInputs) yv[j] = buf_ld8<kNt>(ry, yoff[j]);
             }
             f32x4_t d[4];
             const u32x4_t h0 = xa_op(rt, xb, false);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
                     v[2] += bf_lo(yv[j].y);
                     v[3] += bf_hi(yv[j].y);
                 }
-                buf_st8(ry, yoff[j], make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+                buf_st8<kNt>(ry, yoff[j], make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
             }
             __builtin_amdgcn_wave_barrier();
         }
