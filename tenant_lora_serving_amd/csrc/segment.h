@@ -73,21 +73,35 @@ struct SegArgs {
 // of class x (segments whose adapter is x mod 8, in segment order).  A class
 // with more segments than its XCD has units passes the rest, in class order,
 // to the units left without a segment, also in class order.  Returns the
-// unit's segment, or -1.  sm: 4 * 8 * (kSegMapMax / 256) + 40 ints of LDS.
+// unit's segment (sg -1: none) with its sorted pairs [start, end) and key.
+// The segment count and every segment's key and offsets are loaded at once
+// (entries past the count, left by earlier calls, are read and ignored: the
+// arrays hold n_units entries), so the unit knows its pairs one round trip
+// after it starts.  sm: 4 * 8 * (kSegMapMax / 256) + 40 ints of LDS.
 constexpr int kSegMapMax = 1024;  // most units the mapping takes (else units run in segment order)
-__device__ __forceinline__ int unit_segment(const SegArgs &sa, int u, int n_seg, int *sm) {
+struct SegPick {
+    int sg, start, end, slot;
+};
+__device__ __forceinline__ SegPick unit_segment(const SegArgs &sa, int u, int *sm) {
     constexpr int Q = kSegMapMax / 256, NC = 8;
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
     int *cnt = sm;                   // [Q][4 waves][NC] segments of each class, then their first class rank
     int *tot = cnt + Q * 4 * NC;     // [NC] segments per class
-    int *found = tot + NC;           // the unit's segment
-    int cls[Q], rank[Q];
+    int *found = tot + NC;           // the unit's segment, its first and end pair, its key
+    const int n_seg = __builtin_amdgcn_readfirstlane(sa.counts[1]);
+    int key[Q], off0[Q], off1[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int sg = tid + 256 * q;
-        cls[q] = sg < n_seg ? (sa.seg_slot[sg] / sa.key_div) & (NC - 1) : -1;
+        const bool in = sg < sa.n_units;
+        key[q] = in ? sa.seg_slot[sg] : 0;
+        off0[q] = in ? sa.seg_offsets[sg] : 0;
+        off1[q] = in ? sa.seg_offsets[sg + 1] : 0;
     }
-    if (tid == 0) *found = -1;
+    int cls[Q], rank[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) cls[q] = tid + 256 * q < n_seg ? (key[q] / sa.key_div) & (NC - 1) : -1;
+    if (tid == 0) found[0] = -1;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         rank[q] = 0;
@@ -131,11 +145,20 @@ __device__ __forceinline__ int unit_segment(const SegArgs &sa, int u, int n_seg,
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q)
-        if (cls[q] >= 0 && cls[q] == tc && cnt[(q * 4 + w) * NC + cls[q]] + rank[q] == tr) *found = tid + 256 * q;
+        if (cls[q] >= 0 && cls[q] == tc && cnt[(q * 4 + w) * NC + cls[q]] + rank[q] == tr) {
+            found[0] = tid + 256 * q;
+            found[1] = off0[q];
+            found[2] = off1[q];
+            found[3] = key[q];
+        }
     __syncthreads();
-    const int sg = __builtin_amdgcn_readfirstlane(*found);
+    SegPick pk;
+    pk.sg = __builtin_amdgcn_readfirstlane(found[0]);
+    pk.start = __builtin_amdgcn_readfirstlane(found[1]);
+    pk.end = __builtin_amdgcn_readfirstlane(found[2]);
+    pk.slot = __builtin_amdgcn_readfirstlane(found[3]);
     __syncthreads();  // (the unit's LDS stages reuse these words)
-    return sg;
+    return pk;
 }
 
 // bytes of a row of the LDS xa block: for each of nx blocks, hi[R] then lo[R] (bf16), + 16 pad
@@ -173,14 +196,19 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
     const int u = blockIdx.x;
     int slot, g_start, mg;
     if (u < sa.n_units) {
-        const int n_seg = __builtin_amdgcn_readfirstlane(sa.counts[1]);
-        const int sg = (sa.key_div > 0 && sa.n_units <= kSegMapMax)
-                           ? unit_segment(sa, u, n_seg, reinterpret_cast<int *>(lds))
-                           : (u < n_seg ? u : -1);
-        if (sg < 0) return;
-        g_start = __builtin_amdgcn_readfirstlane(sa.seg_offsets[sg]);
-        mg = min(kSegTiles * 16, __builtin_amdgcn_readfirstlane(sa.seg_offsets[sg + 1]) - g_start);
-        slot = __builtin_amdgcn_readfirstlane(sa.seg_slot[sg]);
+        if (sa.key_div > 0 && sa.n_units <= kSegMapMax) {
+            const SegPick pk = unit_segment(sa, u, reinterpret_cast<int *>(lds));
+            if (pk.sg < 0) return;
+            g_start = pk.start;
+            mg = min(kSegTiles * 16, pk.end - pk.start);
+            slot = pk.slot;
+        } else {
+            const int n_seg = __builtin_amdgcn_readfirstlane(sa.counts[1]);
+            if (u >= n_seg) return;
+            g_start = __builtin_amdgcn_readfirstlane(sa.seg_offsets[u]);
+            mg = min(kSegTiles * 16, __builtin_amdgcn_readfirstlane(sa.seg_offsets[u + 1]) - g_start);
+            slot = __builtin_amdgcn_readfirstlane(sa.seg_slot[u]);
+        }
     } else {
         const int rec = sa.tiles[(int64_t)(u - sa.n_units) * kTileWords + (lane & 31)];
         const int jt = __builtin_amdgcn_readlane(rec, kRecSegTile);
