@@ -389,7 +389,8 @@ __device__ __forceinline__ void shrink_mfma_n(const Op &op, const Hdr &h, int k0
 // MFMA shrink of two consecutive tiles of one segment (tile rows of h0, then
 // of h1, staged together), several k steps: each A fragment feeds both
 // tiles' MFMAs, so the segment's A is read once for the pair.  Wave w owns
-// rank-row group w (at most 4 groups).
+// rank-row groups w and w + 4 (at most 8 groups); the second group's A is
+// loaded once the first group's MFMAs have consumed theirs.
 template <class Op>
 __device__ __forceinline__ void shrink_mfma_pair(const Op &op, const Hdr &h0, const Hdr &h1, int k0, int k1,
                                                  uint16_t *xs, uint64_t *pu0, uint64_t *pu1, uint32_t tag,
@@ -397,40 +398,53 @@ __device__ __forceinline__ void shrink_mfma_pair(const Op &op, const Hdr &h0, co
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 15, kq = lane >> 4;
     const int n_rr = op.n_rr(), G = (n_rr + 15) >> 4;
-    const int rr = 16 * w + col;
-    const uint16_t *ap = (w < G && rr < n_rr) ? op.arow(h0.slot, rr) : nullptr;
+    const int rr0 = 16 * w + col, rr1 = rr0 + 64;
+    const uint16_t *ap0 = (w < G && rr0 < n_rr) ? op.arow(h0.slot, rr0) : nullptr;
+    const uint16_t *ap1 = (w + 4 < G && rr1 < n_rr) ? op.arow(h0.slot, rr1) : nullptr;
     u32x4_t av[16];
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
     uint16_t *xs1 = xs + kTileRows * kXS;
-    for (int ks = k0; ks < k1; ks += kKP) {
-        const int ke = min(k1, ks + kKP);
-        u32x4_t xv0[4], xv1[4];
-        load_x(op, h0, ks, ke, xv0);
-        load_x(op, h1, ks, ke, xv1);
+    auto load_a = [&](const uint16_t *ap, int ks, int ke) {
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2) {
             const int k = ks + 32 * s2 + 8 * kq;
             av[s2] = (ap && k < ke) ? ld16_stream(ap + k) : zero4();
         }
+    };
+    auto mma = [&](f32x4_t (&a)[2]) {
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            a[0] = mfma_16x16x32(lds16(xs + col * kXS + 32 * s2 + 8 * kq), av[s2], a[0]);
+            a[1] = mfma_16x16x32(lds16(xs1 + col * kXS + 32 * s2 + 8 * kq), av[s2], a[1]);
+        }
+    };
+    for (int ks = k0; ks < k1; ks += kKP) {
+        const int ke = min(k1, ks + kKP);
+        u32x4_t xv0[4], xv1[4];
+        load_x(op, h0, ks, ke, xv0);
+        load_x(op, h1, ks, ke, xv1);
+        load_a(ap0, ks, ke);
         if (ks > k0) __syncthreads();  // every wave is done with the previous x
         store_x(xv0, xs);
         store_x(xv1, xs1);
         __syncthreads();
         exchange_done(xo);
-        if (w < G) {
-#pragma unroll
-            for (int s2 = 0; s2 < 16; ++s2) {
-                acc0 = mfma_16x16x32(lds16(xs + col * kXS + 32 * s2 + 8 * kq), av[s2], acc0);
-                acc1 = mfma_16x16x32(lds16(xs1 + col * kXS + 32 * s2 + 8 * kq), av[s2], acc1);
-            }
+        if (w < G) mma(acc[0]);
+        if (w + 4 < G) {
+            load_a(ap1, ks, ke);
+            mma(acc[1]);
         }
     }
     // lane holds D[4kq + i][col]: tile rows 4kq..4kq+3 of rank row rr
-    if (w < G && rr < n_rr) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (4 * kq + i < h0.m) store_word64(pu0 + (4 * kq + i) * n_rr + rr, tagged(acc0[i], tag));
-            if (4 * kq + i < h1.m) store_word64(pu1 + (4 * kq + i) * n_rr + rr, tagged(acc1[i], tag));
+    for (int g = 0; g < 2; ++g) {
+        const int rr = g ? rr1 : rr0;
+        if (w + 4 * g < G && rr < n_rr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (4 * kq + i < h0.m) store_word64(pu0 + (4 * kq + i) * n_rr + rr, tagged(acc[g][0][i], tag));
+                if (4 * kq + i < h1.m) store_word64(pu1 + (4 * kq + i) * n_rr + rr, tagged(acc[g][1][i], tag));
+            }
         }
     }
 }
@@ -1242,11 +1256,11 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
             const Hdr h = tile_hdr();
             if (h.m == 0) return;
             const int k0p = (p * fa.KS) * kKP, k1p = min(op.k_in, k0p + fa.KS * kKP);
-            // wide calls: MFMA segments with at most 64 rank rows are shrunk two
+            // wide calls: MFMA segments with at most 128 rank rows are shrunk two
             // tiles at a time, by the unit of the pair's first tile (the tile
             // with an even index within its segment); the second tile's unit
             // has nothing to do
-            if (WM != 0 && h.mseg >= fa.mfma_min && n_rr <= 64) {
+            if (WM != 0 && h.mseg >= fa.mfma_min && n_rr <= 128) {
                 const int jt = __builtin_amdgcn_readlane(h.rec, kRecSegTile);
                 // (segments under 16 rows, cut in two tiles, are never paired)
                 if ((jt & 1) && h.mseg >= kTileRows) return;
