@@ -63,6 +63,7 @@ constexpr int kFT = 256;      // threads per workgroup
 constexpr int kXS = kKP + 8;  // padded LDS row stride (bf16) of the staged x tile
 constexpr int kXaBytes = kTileRows * kMaxRank * 4;  // LDS for a tile's xa (fp32, or bf16 hi/lo pairs)
 constexpr int kBStage = 128 * 32 + (128 * 32 / 128) * 8;  // bf16 per wave: 128 columns x 32 ranks + padding
+constexpr int kBHalf = 64 * 128;  // bytes per wave: B of 64 columns at rank 64, staged in LDS (wide MFMA expand)
 constexpr int kDtStride = 68;  // fp32 row stride of a wave's 16 x 64 output tile in LDS (64 + 4 pad)
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kShrinkUnits = 1024;  // shrink units a call keeps before its units take several k steps
@@ -945,6 +946,40 @@ __device__ __forceinline__ void mfma_load_y(uint16_t *const (&yr)[4], int cw0, i
         }
 }
 
+// Wide MFMA expand at ranks 33..64 (B rows of up to 128 bytes): B is loaded
+// with whole rows per load -- eight lanes per row, so each instruction reads
+// eight full cache lines instead of half of sixteen -- and handed to the
+// MFMA operand layout through the wave's LDS region, half a batch (64
+// columns) at a time.  Row rl of a half keeps its 16-byte chunk c at
+// position c ^ ((rl >> 1) & 7), so the operand reads (16 rows, one chunk
+// each) spread over the banks.  raw[u]: rows 8 (u mod 8) .. + 8 of half u / 8.
+__device__ __forceinline__ int bstage_swz(int rl) { return (rl >> 1) & 7; }
+template <bool BS, class Op>
+__device__ __forceinline__ void staged_load_b(const Op &op, const Hdr &h, int cb, int c1, int R,
+                                              u32x4_t (&raw)[16]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int rl = 8 * (u & 7) + (lane >> 3), cc = cb + 64 * (u >> 3) + rl;
+        const int j = (lane & 7) ^ bstage_swz(rl);
+        const uint16_t *bp = cc < c1 ? op.brow(h.slot, cc) : nullptr;
+        raw[u] = (bp && 8 * j < R) ? ld16_b<BS>(bp + 8 * j) : zero4();
+    }
+}
+// half hf of raw into the wave's region: instruction u writes 1 KB in order
+__device__ __forceinline__ void staged_put_b(const u32x4_t (&raw)[16], int hf, char *breg) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st16(breg + 1024 * u + 16 * lane, raw[8 * hf + u]);
+}
+// operand (column tile t, rank step s): lane (kq, col) takes row 16t + col,
+// chunk 4s + kq
+__device__ __forceinline__ u32x4_t staged_op(const char *breg, int t, int s) {
+    const int lane = lane_id(), col = lane & 15, kq = lane >> 4;
+    const int rl = 16 * t + col;
+    return *reinterpret_cast<const u32x4_t *>(breg + rl * 128 + 16 * ((4 * s + kq) ^ bstage_swz(rl)));
+}
+
 template <int NRS, bool WIDE, bool BS, class Op>
 __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, int c1, bool add_inputs,
                                            const XaSrc &xs, char *lds) {
@@ -962,10 +997,19 @@ __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, i
         const int rid = __shfl(h.rec, kRecRowIds + row, kWave);
         yr[j] = row < h.m ? op.yrow(rid) : nullptr;
     }
-    float *dt = reinterpret_cast<float *>(lds + kXaBytes) + w * kTileRows * kDtStride;
+    // LB: B staged through LDS (wide calls at ranks 33..64); the wave's
+    // region then also holds its output tile, each in turn
+    constexpr bool LB = WIDE && NRS == 2;
+    char *breg = lds + kXaBytes + w * kBHalf;
+    float *dt = LB ? reinterpret_cast<float *>(breg)
+                   : reinterpret_cast<float *>(lds + kXaBytes) + w * kTileRows * kDtStride;
     u32x4_t bo[8][NRS];
+    u32x4_t raw[LB ? 16 : 1];
     uint2 yv[8];
-    mfma_load_b<NRS, BS>(op, h, c0 + 128 * w, c1, R, bo);
+    if constexpr (LB)
+        staged_load_b<BS>(op, h, c0 + 128 * w, c1, R, raw);
+    else
+        mfma_load_b<NRS, BS>(op, h, c0 + 128 * w, c1, R, bo);
     mfma_load_y(yr, c0 + 128 * w, c1, add_inputs, yv);
     load_row_weights(op, h, xs);
     if (!wait_pieces(xs.flags, xs.P, xs.tag, xs.ctl, xs.ok)) return count_consumer(xs);
@@ -988,6 +1032,18 @@ __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, i
         // together, and the second half's overlap the first half's stores
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
+            if constexpr (LB) {
+                // this half's B rows into the region (the previous half's
+                // output tile has been read back: in-order LDS), its operands
+                // out in MFMA layout
+                staged_put_b(raw, hf, breg);
+                __builtin_amdgcn_wave_barrier();
+                if (hf == 1 && b + 1 < nb) staged_load_b<BS>(op, h, cw0 + kEB, c1, R, raw);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int s = 0; s < NRS; ++s) bo[4 * hf + i][s] = staged_op(breg, i, s);
+            }
             f32x4_t d[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -998,9 +1054,10 @@ __device__ __forceinline__ int expand_mfma(const Op &op, const Hdr &h, int c0, i
                     d[i] = mfma_16x16x32(bo[4 * hf + i][s], lv[s], d[i]);
                 }
             }
+            __builtin_amdgcn_wave_barrier();
             if (WIDE && hf == 1 && b + 1 < nb) {
                 // the MFMAs above were the last readers of this batch's B
-                mfma_load_b<NRS, BS>(op, h, cw0 + kEB, c1, R, bo);
+                if constexpr (!LB) mfma_load_b<NRS, BS>(op, h, cw0 + kEB, c1, R, bo);
                 mfma_load_y(yr, cw0 + kEB, c1, add_inputs, yv_n);
             }
             // the half's 16 x 64 block through the wave's LDS tile: written in
@@ -1222,8 +1279,11 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
     // shrink units: the staged x tile; expand units: xa, then the waves' B stages
     constexpr int kLdsShrink = (WM != 0 ? 2 : 1) * kTileRows * kXS * 2;  // wide modes stage tile pairs
     constexpr int kLdsStage = WM == 1 ? 4 * kBStage * 2 : 0, kLdsTile = 4 * kTileRows * kDtStride * 4;
+    constexpr int kLdsBStaged = (WM != 0 && NRS == 2) ? 4 * kBHalf : 0;  // B staged per wave, and its output tile
     constexpr int kLdsExpand =  // wide modes at rank <= 32 stage the xa of tile pairs
-        (WM != 0 && NRS == 1 ? 2 : 1) * kXaBytes + (kLdsStage > kLdsTile ? kLdsStage : kLdsTile);
+        (WM != 0 && NRS == 1 ? 2 : 1) * kXaBytes +
+        (kLdsStage > kLdsTile ? (kLdsStage > kLdsBStaged ? kLdsStage : kLdsBStaged)
+                              : (kLdsTile > kLdsBStaged ? kLdsTile : kLdsBStaged));
     __shared__ __align__(16) char lds[kLdsShrink > kLdsExpand ? kLdsShrink : kLdsExpand];
     static_assert(sizeof(lds) >= (kSmallBallotSlots * (kFT / kWave + 3) + kTileWords + 1) * sizeof(int) +
                                      (kFT / kWave + 1) * sizeof(Int3) + 2 * sizeof(int),
