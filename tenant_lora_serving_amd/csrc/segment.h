@@ -384,21 +384,47 @@ __global__ __launch_bounds__(256, 2) void segment_kernel(Op op, SegArgs sa, Zero
         load_b(q + 4 * PB, bq[b]);  // refill the slot: the chunk PB ahead
         const int l = q / cpw, col0 = op.xoff(l) + 64 * (q - l * cpw), c1 = op.xoff(l + 1);
         const int xb = op.xblk(l);
-#pragma unroll
-        for (int rt = 0; rt < kSegTiles; ++rt) {
-            if (rt >= nt) break;
+        // row tile rt's out rows 4 j + kq, columns col0 + 4c .. + 4
+        auto tile_yoff = [&](int rt, uint32_t (&yoff)[4]) {
             const int rt_pid = rt == 0 ? pid[0] : rt == 1 ? pid[1] : rt == 2 ? pid[2] : pid[3];
             const int mrt = rt == 0 ? mt[0] : rt == 1 ? mt[1] : rt == 2 ? mt[2] : mt[3];
-            // this row tile's out rows 4 j + kq, columns col0 + 4c .. + 4 (w2: their y, read first)
-            uint32_t yoff[4];
-            uint2 yv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 4 * j + kq, col = col0 + 4 * c;
                 // (the shuffle runs in every lane: a lane it reads from must be active)
                 const int pr = __shfl(rt_pid, row, kWave);
                 yoff[j] = (row < mrt && col < c1) ? op.y_off(pr, col) : kOob;
-                if constexpr (Op::kAddInputs) yv[j] = buf_ld8<kNt>(ry, yoff[j]);
+            }
+        };
+        // w2 adds to y: the y of every row tile of the chunk is loaded before
+        // the chunk's first store, so its latency is paid once per chunk (the
+        // compiler keeps a load of y after the stores to y before it)
+        uint32_t yoff_all[Op::kAddInputs ? kSegTiles : 1][4];
+        uint2 yv_all[Op::kAddInputs ? kSegTiles : 1][4];
+        if constexpr (Op::kAddInputs) {
+#pragma unroll
+            for (int rt = 0; rt < kSegTiles; ++rt) {
+                tile_yoff(rt, yoff_all[rt]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (rt >= nt) yoff_all[rt][j] = kOob;
+                    yv_all[rt][j] = buf_ld8<kNt>(ry, yoff_all[rt][j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < kSegTiles; ++rt) {
+            if (rt >= nt) break;
+            uint32_t yoff[4];
+            uint2 yv[4];
+            if constexpr (Op::kAddInputs) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    yoff[j] = yoff_all[rt][j];
+                    yv[j] = yv_all[rt][j];
+                }
+            } else {
+                tile_yoff(rt, yoff);
             }
             f32x4_t d[4];
             const u32x4_t h0 = xa_op(rt, xb, false);
