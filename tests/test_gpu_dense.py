@@ -319,3 +319,20 @@ def test_wide_call_with_split_segments(path):
     assert n_tiles == sum(2 if 8 < m < 16 else -(-m // 16) for m in lens)
     dv.fused()
     check_y(dv, h16(dv.y), None, f"wide split {path}")
+
+
+def test_wide_mfma_rank_48(path):
+    """A wide call at rank 48 (two rank steps of 32, B rows of 96 bytes): on
+    the MFMA path its expand stages B through LDS from whole-row loads (the
+    chunks past rank 48 masked), and its shrink pairs tiles at 96 rank rows;
+    windows of 8200 columns leave ragged last batches."""
+    rng = np.random.default_rng(81)
+    lens = [700, 333, 67]
+    slot = np.concatenate([np.full(m, s, np.int32) for s, m in enumerate(lens)])
+    slot = slot[rng.permutation(slot.size)]
+    c = I.make_dense(82, n=slot.size, k_in=264, slice_sizes=(8200, 8200), num_slots=len(lens), max_rank=48,
+                     rank_choices=[24, 48], slot=slot, scale_num=96.0)
+    print(f"wide rank 48 n={c.n} path={path}", flush=True)
+    dv = Dev(c, ldy_pad=8)
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"wide rank 48 {path}")
