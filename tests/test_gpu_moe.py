@@ -179,3 +179,13 @@ def test_moe_segments_longer_than_64_pairs(shared):
     lens = np.bincount(keys[(keys >= 0) & (keys < c.E * c.L)], minlength=c.E * c.L)
     assert lens.max() > 64 and (keys >= 0).sum() <= 64 * c.E * c.L
     check_moe(c, shared, what="long segments")
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_moe_rank64_wide_fused(shared, path):
+    """Rank 64 takes the fused kernel (the segment kernel serves ranks 8, 16
+    and 32); with long segments and 8200-column windows its units are wide:
+    on the MFMA path the shrink pairs tiles (128 rank rows in the regular
+    form) and the expand stages B through LDS from whole-row loads."""
+    c = small_moe(41, T=512, H=264, E=2, top_k=2, I=8200, R=64, L=1, neg_frac=0.1)
+    check_moe(c, shared, f"rank 64 wide {path}")
