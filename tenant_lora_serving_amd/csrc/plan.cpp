@@ -44,9 +44,19 @@ int chunks_of(const int *off, int n_windows, int EC) {
 // Columns per expand unit: 512 while that keeps the expand units of a call
 // within about 2048 workgroups, else 1024 or 2048, so that each unit's read
 // of the tile's partials and its fixed chain latency cover more columns.
+// Past that, the widest chunk of 5..8 batches that cuts every window into
+// equal whole-batch chunks, if one does (a ragged last chunk per window
+// leaves short units at the end of the call).
 int expand_width(const int *off, int n_windows, int tile_bound) {
     int ec = kEB;
     while (ec < 4 * kEB && (long long)tile_bound * chunks_of(off, n_windows, ec) > 2048) ec *= 2;
+    if (ec == 4 * kEB && (long long)tile_bound * chunks_of(off, n_windows, ec) > 2048) {
+        for (int e = 8; e > 4; --e) {
+            bool even = true;
+            for (int l = 0; l < n_windows; ++l) even = even && ((off[l + 1] - off[l] + kEB - 1) / kEB) % e == 0;
+            if (even) return e * kEB;
+        }
+    }
     return ec;
 }
 

@@ -336,3 +336,19 @@ def test_wide_mfma_rank_48(path):
     dv = Dev(c, ldy_pad=8)
     dv.fused()
     check_y(dv, h16(dv.y), None, f"wide rank 48 {path}")
+
+
+def test_wide_call_eight_batch_chunks(path):
+    """Over 2048 expand units at 2048 columns: windows of 16384 and 8192
+    columns (32 and 16 batches) are cut into equal chunks of eight 512-column
+    batches; tile pairs in the shrink and the expand on the MFMA path."""
+    rng = np.random.default_rng(91)
+    lens = [2600, 1300, 300]
+    slot = np.concatenate([np.full(m, s, np.int32) for s, m in enumerate(lens)])
+    slot = slot[rng.permutation(slot.size)]
+    c = I.make_dense(92, n=slot.size, k_in=64, slice_sizes=(16384, 8192), num_slots=len(lens), max_rank=16,
+                     rank_choices=[8, 16], slot=slot, scale_num=32.0)
+    print(f"wide eight-batch chunks n={c.n} path={path}", flush=True)
+    dv = Dev(c)
+    dv.fused()
+    check_y(dv, h16(dv.y), None, f"wide eight-batch chunks {path}")
