@@ -33,7 +33,7 @@
 namespace tl {
 
 constexpr int kMT = kMetaChunk;  // threads per workgroup = rows per chunk
-constexpr int kAsmBatch = 8;       // chunks whose entries the assembling workgroup loads at once
+constexpr int kAsmBatch = 16;      // chunks whose entries the assembling workgroup loads at once
 
 
 
@@ -173,6 +173,16 @@ __device__ void meta_assemble(int n, int S, int n_chunks, MetaOut out, MetaWs ws
     // build): each slot's rows in all chunks and in the chunks before this
     // one, from [chunk][slot] counts, kAsmBatch chunks' loads in flight.
     const bool from_hist = only >= 0 && ws.hist && table;
+    // a split assembler's own chunk entries, loaded with the slot counts
+    // rather than after the scans
+    uint32_t own_k = (uint32_t)S;
+    int own_ol = 0, own_row = 0;
+    if (from_hist) {
+        const int64_t idx = (int64_t)only * kMT + tid;
+        own_k = (uint32_t)ws.keys[idx];
+        own_ol = ws.offlen[idx];
+        own_row = ws.rows[idx];
+    }
     if (from_hist) {
         for (int s = tid; s < S; s += kMT) {
             int acc = 0, before = 0;
@@ -266,7 +276,22 @@ __device__ void meta_assemble(int n, int S, int n_chunks, MetaOut out, MetaWs ws
         out.counts[4] = tot.c;
         out.counts[5] = out.counts[6] = out.counts[7] = 0;
     }
-    if (table) {
+    // entry (key k2, offset+length ol, row) of chunk cc to its place
+    auto place = [&](int cc, uint32_t k2, int ol, int row) {
+        if (k2 >= (uint32_t)S) return;
+        const int o = cb[cc * S + k2] + (ol & 0xffff);
+        const int dest = start[k2] + o;
+        const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
+        out.sorted_rows[dest] = row;
+        const int per = seg_tile_rows(seg_rows, n);
+        const int t = tileoff[k2] + o / per, j = o % per;
+        int32_t *rec = out.tiles + (int64_t)t * kTileWords;
+        rec[kRecRowIds + j] = row;
+        if (j == 0) write_tile_header(rec, (int)k2, dest, min(per, seg_rows - o), seg_rows, segidx[k2], o / per);
+    };
+    if (from_hist) {
+        place(only, own_k, own_ol, own_row);
+    } else if (table) {
         // every chunk, or only chunk `only`
         const int cbeg = only < 0 ? 0 : only, cend = only < 0 ? n_chunks : only + 1;
         for (int c0 = cbeg; c0 < cend; c0 += kAsmBatch) {
@@ -281,23 +306,7 @@ __device__ void meta_assemble(int n, int S, int n_chunks, MetaOut out, MetaWs ws
                 rb[u] = in ? ws.rows[idx] : 0;
             }
 #pragma unroll
-            for (int u = 0; u < kAsmBatch; ++u) {
-                const int cc = c0 + u;
-                const uint32_t k2 = kb[u];
-                if (k2 >= (uint32_t)S) continue;
-                const int ol = ob[u];
-                const int row = rb[u];
-                const int o = cb[cc * S + k2] + (ol & 0xffff);
-                const int dest = start[k2] + o;
-                const int seg_rows = (k2 + 1 < (uint32_t)S ? start[k2 + 1] : tot.a) - start[k2];
-                out.sorted_rows[dest] = row;
-                const int per = seg_tile_rows(seg_rows, n);
-                const int t = tileoff[k2] + o / per, j = o % per;
-                int32_t *rec = out.tiles + (int64_t)t * kTileWords;
-                rec[kRecRowIds + j] = row;
-                if (j == 0)
-                    write_tile_header(rec, (int)k2, dest, min(per, seg_rows - o), seg_rows, segidx[k2], o / per);
-            }
+            for (int u = 0; u < kAsmBatch; ++u) place(c0 + u, kb[u], ob[u], rb[u]);
         }
     }
     // scatter the chunks in order; rc[s] counts the rows of slot s already placed
