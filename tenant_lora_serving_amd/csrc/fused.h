@@ -11,10 +11,10 @@
 //   shrink unit (tile t, k piece p): every rank row of the tile's adapter over
 //     k in [512p, 512p + 512); writes an fp32 partial block part[t][p][16][rr]
 //     and raises the piece's flag.
-//   expand unit (tile t, column chunk): at most 512, 1024 or 2048 columns of
-//     one output window (more for larger calls), in batches of 512.  It issues its B and y loads, waits for the tile's P flags, sums
-//     the P partials in piece order (bitwise reproducible), scales, and adds
-//     xa @ B^T to y.
+//   expand unit (tile t, column chunk): one to eight 512-column batches of
+//     one output window.  It issues its B and y loads, waits for the tile's
+//     P flags, sums the P partials in piece order (bitwise reproducible),
+//     scales, and adds xa @ B^T to y.
 // A consumer only waits on producers with lower workgroup ids, which never
 // wait themselves; workgroups are dispatched in id order, so every awaited
 // producer is running or done and the wait always ends.  It is still bounded
@@ -28,8 +28,9 @@
 // no acquire (an L2 invalidate).  The piece flags carry the same tag and only
 // tell the consumer when to start reading; a word that still shows an old tag
 // is read again.  The last consumer of a tile counts the tile as finished,
-// and the last finished tile of the call advances the generation.  Tags only grow, so data left by an
-// earlier call, of any shape, is never taken for the current one.
+// and the last finished tile of the call advances the generation.  Tags only
+// grow, so data left by an earlier call, of any shape, is never taken for
+// the current one.
 //
 // The latency chain (tile record -> A/x loads -> reduce -> publish -> poll ->
 // partial loads -> expand -> y store) is what bounds a decode-sized call, so
