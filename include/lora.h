@@ -29,8 +29,10 @@
  *  - Every check that can run on the host runs before any launch and
  *    returns an error code; nothing is enqueued then.
  *  - Workspaces must be zero-filled before their first use.  The meta
- *    workspace's counters return to zero after every call.  The fused and
- *    MoE workspaces hold a control line (below) whose tag of the last
+ *    workspace's counters return to zero after every call; where a fused
+ *    or MoE call builds its metadata, they sit at byte 64 of that
+ *    workspace, which no call of any shape uses for anything else.  The
+ *    fused and MoE workspaces hold a control line (below) whose tag of the last
  *    completed call tags the partial results of the next one; they stay
  *    valid for calls of any shape that fits them, for 2^31 - 2 calls
  *    (then the tags start over: zero-fill the workspace again before that).

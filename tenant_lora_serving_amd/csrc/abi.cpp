@@ -16,6 +16,18 @@ using tl::kMaxSlices;
 constexpr int kMaxRows = 1 << 22;
 constexpr int kMaxSlots = 1 << 20;
 
+// The metadata build's two counters (single assembler's ticket, invalid rows)
+// when the build runs inside a fused or MoE call: bytes 64..71 of the fused
+// workspace's 256-byte control area (control line at bytes 0..63, flags from
+// byte 256) and of the MoE header (counts at bytes 0..31, control line at
+// LORA_MOE_CTL_OFFSET).  Both headers stay in place whatever the shape.
+constexpr size_t kFusedMetaCtl = 64;
+constexpr size_t kMoeMetaCtl = 64;
+static_assert(LORA_FUSED_CTL_OFFSET + 64 <= kFusedMetaCtl && kFusedMetaCtl + 8 <= 256,
+              "the build's counters sit clear of the fused control line and flags");
+static_assert(kMoeMetaCtl >= 8 * sizeof(int32_t) && kMoeMetaCtl + 8 <= LORA_MOE_CTL_OFFSET,
+              "the build's counters sit clear of the MoE counts and control line");
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // The MFMA row threshold: a process-wide default (16, or LORA_MFMA_MIN_ROWS
@@ -50,12 +62,17 @@ size_t meta_ws_bytes(int n, int S) {
            (meta_hist(n, S) ? (size_t)chunks * S * sizeof(int32_t) : 0);
 }
 
-tl::MetaWs carve_meta_ws(void *ws, int n, int S) {
+// ctl: where the two counters live when the metadata workspace is carved
+// from a larger one whose layout changes with the call's shape (the fused
+// and MoE workspaces).  There they sit in that workspace's fixed header, so
+// no region of a call of another shape ever covers them and they are still
+// zero when the next build starts.  Null: the first 64 bytes of `ws`.
+tl::MetaWs carve_meta_ws(void *ws, int n, int S, int32_t *ctl = nullptr) {
     tl::MetaWs w{};
     if (tl::meta_chunks(n) <= 1) return w;
     char *b = static_cast<char *>(ws);
     const size_t per = (size_t)tl::meta_chunks(n) * 1024;
-    w.ctl = reinterpret_cast<int32_t *>(b);
+    w.ctl = ctl ? ctl : reinterpret_cast<int32_t *>(b);
     w.rows = reinterpret_cast<int32_t *>(b + 64);
     w.keys = w.rows + per;
     w.offlen = w.keys + per;
@@ -231,7 +248,9 @@ int fused_call(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_in, const ui
         if (!ws || ws_bytes < need || !aligned16(ws)) return LORA_EWORKSPACE;
         tl::MetaOut mo{meta.sorted_rows, meta.seg_offsets, meta.seg_slot, meta.counts, meta.tiles,
                        tile_bound(n, num_slots)};
-        const tl::MetaWs meta_ws = carve_meta_ws(static_cast<char *>(ws) + plan.total_bytes, n, num_slots);
+        const tl::MetaWs meta_ws =
+            carve_meta_ws(static_cast<char *>(ws) + plan.total_bytes, n, num_slots,
+                          reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kFusedMetaCtl));
         if (n == 0) return launched(tl::launch_meta_dense(slot, n, num_slots, mo, meta_ws, st));
         d.x = x;
         d.ldx = ldx;
@@ -302,7 +321,8 @@ int lora_delta_fused_build(const uint16_t *x, int64_t ldx, int32_t n, int32_t k_
 }
 
 // MoE workspace: a fixed 256-byte header (counts, 8 int32 at byte 0; the
-// fused control line at byte LORA_MOE_CTL_OFFSET), then [sorted_rows n |
+// pair metadata build's counters at byte kMoeMetaCtl; the fused control line
+// at byte LORA_MOE_CTL_OFFSET), then [sorted_rows n |
 // seg_offsets cap+1 | seg_slot cap | tiles] [meta ws] [fused flags and
 // partials].  The header never moves, so the control line's call tag
 // survives calls of any shape; the pair metadata's offsets depend only on
@@ -374,7 +394,7 @@ int moe_lora_gemm1_delta(const uint16_t *x, int64_t ldx, int32_t T, int32_t H, c
                    reinterpret_cast<int32_t *>(b + lay.tiles), tile_bound(n, S)};
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
-                                       carve_meta_ws(b + lay.meta_ws, n, S), st);
+                                       carve_meta_ws(b + lay.meta_ws, n, S, reinterpret_cast<int32_t *>(b + kMoeMetaCtl)), st);
     if (e != hipSuccess) return LORA_ELAUNCH;
     if (n == 0) return LORA_OK;
     tl::MoeShape m{x, ldx, T, H, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, shared_a, topk_ids, top_k,
@@ -419,7 +439,7 @@ int moe_lora_w2_delta(const uint16_t *x2, int64_t ldx, int32_t T, int32_t I, con
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (!reuse_routing) {
         const hipError_t e = tl::launch_meta_moe(topk_ids, lora_ids, top_k, num_experts, num_loras, n, mo,
-                                                 carve_meta_ws(b + lay.meta_ws, n, S), st);
+                                                 carve_meta_ws(b + lay.meta_ws, n, S, reinterpret_cast<int32_t *>(b + kMoeMetaCtl)), st);
         if (e != hipSuccess) return LORA_ELAUNCH;
     }
     if (n == 0) return LORA_OK;

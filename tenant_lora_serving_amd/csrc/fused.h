@@ -22,15 +22,15 @@
 //
 // Hand-off without fences.  Every partial is a 64-bit word {fp32 value, tag}
 // written and read as one agent-scope atomic, and the tag names the call
-// (tag = generation + 1, the generation being the number of completed calls
-// on this workspace).  A reader that sees the current tag therefore sees the
+// (next_tag of the last completed call's tag on this workspace: the top bit
+// set, one more per call).  A reader that sees the current tag therefore sees the
 // value, so the producer needs no release (an L2 write-back) and the consumer
 // no acquire (an L2 invalidate).  The piece flags carry the same tag and only
 // tell the consumer when to start reading; a word that still shows an old tag
 // is read again.  The last consumer of a tile counts the tile as finished,
-// and the last finished tile of the call advances the generation.  Tags only
-// grow, so data left by an earlier call, of any shape, is never taken for
-// the current one.
+// and the last finished tile of the call records its tag.  Tags grow until
+// they start over after 2^31 - 2 calls, so data left by an earlier call, of
+// any shape, is never taken for the current one.
 //
 // The latency chain (tile record -> A/x loads -> reduce -> publish -> poll ->
 // partial loads -> expand -> y store) is what bounds a decode-sized call, so

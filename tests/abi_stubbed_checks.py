@@ -140,6 +140,20 @@ def test_moe_calls_use_the_documented_layout(L):
     fused = val(L, MOE, 7)
     assert fused - ws >= off[4] + 4 * 32 * L.lora_meta_max_tiles(n, S)
     assert fused - ws + val(L, MOE, 6) <= need
+    # pairs in several metadata chunks: the build's counters sit in the header,
+    # its other arrays between the pair metadata and the fused part
+    b = moe_args(T=512)
+    nb, Sb = b["T"] * b["top_k"], b["E"] * b["L"]
+    needb = L.moe_lora_workspace_bytes(b["T"], b["top_k"], b["E"], b["L"], b["R"], b["H"])
+    L.raw.stub_reset()
+    assert L.moe_lora_gemm1_delta(0x1000, b["H"], b["T"], b["H"], 0x2000, b["R"] * b["H"], 0x3000,
+                                  b["I"] * b["R"], 0, 0x4000, b["top_k"], 0x5000, b["E"], b["L"], b["R"], b["I"],
+                                  1.0, 0x6000, ws, needb, None) == OK
+    wsm = [val(L, META_MOE, i) for i in range(6, 10)]             # ctl, rows, keys, offlen
+    assert L.lora_meta_workspace_bytes(nb, Sb) > 0
+    assert wsm[0] == ws + 64
+    assert min(wsm[1:]) >= val(L, META_MOE, 4) + 4 * 32 * L.lora_meta_max_tiles(nb, Sb)
+    assert max(wsm[1:]) < val(L, MOE, 7)
     # w2 reusing gemm1's routing: no metadata launch, the same pair metadata
     need2 = L.moe_lora_w2_workspace_bytes(a["T"], a["top_k"], a["E"], a["L"], a["R"], a["I"])
     L.raw.stub_reset()
@@ -190,10 +204,11 @@ def test_build_call_launches_once_for_decode_batches(L):
         assert calls(L) == [1, 0, 0, 0, 0, 1, 0, 0, 0], (n, S)
         assert val(L, FUSED, 9) == 0                         # the fused kernel reads the built records
         assert val(L, FUSED, 3) == 0x100000 + 0x40000
-        ws_meta = [val(L, META_DENSE, i) for i in range(6, 10)]
+        ws_meta = [val(L, META_DENSE, i) for i in range(6, 10)]   # ctl, rows, keys, offlen
         fused_need = L.lora_fused_workspace_bytes(n, S, 3, 16, 4096)
-        if L.lora_meta_workspace_bytes(n, S):                # carved after the fused part
-            assert min(ws_meta) >= 0x9000 + fused_need
+        if L.lora_meta_workspace_bytes(n, S):                # carved after the fused part ...
+            assert min(ws_meta[1:]) >= 0x9000 + fused_need
+            assert ws_meta[0] == 0x9000 + 64                 # ... its counters in the fixed header
     L.raw.stub_reset()
     assert L.lora_delta_fused_build(0x1000, 4096, 8, 4096, 0x2000, 0x3000, 0x4000, 32, 3, ss, 16, None, m,
                                     0x5000, 6144, 0, 0x9000, need, None) == EINVAL   # no slot array

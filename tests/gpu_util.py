@@ -58,11 +58,13 @@ def assert_close_chunked(gpu_bits: np.ndarray, oracle_of, idx: np.ndarray, what:
 def assert_ws_ok(ws: torch.Tensor, moe: bool = False, calls: int | None = None):
     """The workspace's control line after the stream reached the last call:
     error word 0, no tiles left counted, and (when given) the number of calls
-    completed on it."""
+    completed on it; the metadata build's two counters, at byte 64 of a fused
+    or MoE workspace, back to zero."""
     torch.cuda.synchronize()
     st = B.ws_status(ws, moe)
     assert st.error == 0, f"a bounded wait gave up: {st}"
     assert st.running == 0, f"a call left tiles counted: {st}"
+    assert ws[64:72].view(torch.int32).cpu().tolist() == [0, 0], "the metadata build left a counter set"
     if calls is not None:
         assert st.calls == calls, st
     return st

@@ -95,6 +95,29 @@ def test_build_workspace_shared_with_fused_calls():
         check_y(dv, h16(dv.y), None, f"shared workspace call {i}")
 
 
+def test_build_meta_counters_survive_shapes():
+    """One workspace, builds of two kinds in turn: 6000 rows over 2000 slots
+    (too many for the per-chunk slot table, so one workgroup assembles,
+    taking a ticket) and 3000 rows over 7 slots (one assembling workgroup per
+    chunk).  The larger call's flags cover the place the smaller call's
+    metadata workspace starts at, so the build's counters (the ticket and the
+    invalid-row count) must live where no call of any shape writes anything
+    else; every call is checked in full, its counts included."""
+    kw_t = dict(n=6000, k_in=64, slices=(64,), S=2000, R=8)
+    kw_s = dict(n=3000, k_in=64, slices=(64,), S=7, R=8, zipf=True)
+    cases = [small_case(31, **kw_t), small_case(32, **kw_s), small_case(33, **kw_t), small_case(34, **kw_s)]
+    need = max(B.fused_build_workspace(c.n, c.num_slots, c.num_slices, c.max_rank, c.k_in).numel()
+               for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, c in enumerate(cases):
+        assert ((c.slot >= c.num_slots).any() and (c.slot < 0).any())
+        print(f"counter call {i}: n={c.n} S={c.num_slots}", flush=True)
+        dv = Dev(c)
+        meta, _ = build(dv, ws=ws, calls=i + 1)
+        assert_meta_matches(meta, c.slot, c.num_slots)
+        check_y(dv, h16(dv.y), None, f"counter call {i}")
+
+
 def test_build_zero_rows():
     """n == 0: only the counts are written (zero); no row is read."""
     import ctypes

@@ -167,6 +167,27 @@ def test_moe_workspace_reused_across_shapes(moe_case):
         check_moe(case, False, what=f"reuse call {i}", ws=ws, calls=i + 1)
 
 
+def test_moe_meta_counters_survive_shapes():
+    """One workspace, pair metadata built two ways in turn: 32768 pairs over
+    512 (adapter, expert) keys (too many chunks for the per-chunk slot table:
+    one workgroup assembles, taking a ticket) and 16384 pairs (one assembling
+    workgroup per chunk).  Each shape's metadata regions cover the other's
+    metadata workspace, so the build's counters (the ticket and the invalid
+    pair count) must sit where no shape writes anything else; every call is
+    compared in full, its counts and pair metadata bit for bit."""
+    kw = dict(H=264, E=64, top_k=8, I=40, R=16, L=8, neg_frac=0.1)
+    cases = []
+    for i, T in enumerate([4096, 2048, 4096, 2048]):
+        c = I.make_moe(51 + i, T=T, **kw)
+        rng = np.random.default_rng(51 + i)
+        c.lora_ids[rng.random(c.T) < 0.02] = c.L + 1
+        c.topk_ids[rng.random(c.topk_ids.shape) < 0.01] = c.E + 2
+        cases.append(c)
+    ws = B.moe_workspace(4096, 8, 64, 8, 16, 264)
+    for i, c in enumerate(cases):
+        check_moe(c, False, what=f"counters call {i} T={c.T}", ws=ws, calls=i + 1)
+
+
 @pytest.mark.parametrize("shared", [False, True])
 def test_moe_segments_longer_than_64_pairs(shared):
     """A hot expert: its (adapter, expert) segments run past 64 pairs (their
