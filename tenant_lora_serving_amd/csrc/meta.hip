@@ -8,16 +8,19 @@
 // (slot, row), which makes the result unique, so it is compared bit-exactly.
 //
 // Design (gfx950): one 1024-thread workgroup per chunk of 1024 rows.
-//  1. Each chunk is sorted by slot in LDS with a stable 4-bit radix sort
-//     (per-wave 64-bit ballots give each lane its rank among equal digits;
-//     a 16 x 16 digit-by-wave histogram is scanned for the bucket starts).
-//     Inactive and invalid rows get the key S and sort to the end.
+//  1. Each chunk is sorted by slot in LDS, stably: up to 512 slots in one
+//     pass (per-wave ballots, one per key bit, give each lane its rank among
+//     equal keys; a [key][wave] table is scanned for the positions), else
+//     with 4-bit radix passes ranked the same way.  Inactive and invalid
+//     rows get the key S and sort to the end.  A split build (below) with up
+//     to 512 slots does not move the rows at all: each keeps its rank among
+//     the chunk's rows of its slot, which is all its placement needs.
 //  2. Runs of one slot in the sorted chunk are found with a block scan.
 //  3. One chunk: the workgroup writes every output directly.
 //     Several chunks: each writes its sorted chunk to the workspace.  When a
 //     [chunk][slot] table of run lengths fits LDS and there are at most 64
-//     chunks, a second launch of one workgroup per chunk follows: each builds
-//     the table from the workspace, scans it (rows of a slot in earlier
+//     chunks, a second launch of one workgroup per chunk follows: each reads
+//     every chunk's slot counts from the workspace, scans them (rows of a slot in earlier
 //     chunks come first, so rows keep ascending order within a slot) and
 //     places its own chunk's rows.
 //     Otherwise the last workgroup to finish the first launch (atomic ticket,
@@ -152,6 +155,41 @@ __device__ __forceinline__ void ballot_sort(uint32_t &key, int32_t &val, int S, 
     key = sh.key[tid];
     val = sh.val[tid];
     __syncthreads();
+}
+
+// A chunk of a split build, ranked instead of sorted: the assembling launch
+// places each row from its key, its rank among the chunk's rows of that key
+// (rows keep ascending order) and every chunk's per-slot counts, all that
+// the sorted order would have given it.  Each wave ranks its lanes with one
+// ballot per key bit (few_rank); a [wave][slot] table of group sizes, scanned
+// over the waves per slot, turns wave ranks into chunk ranks and gives the
+// chunk's count of every slot.  tab: S * 16 ints of LDS.
+__device__ __forceinline__ void rank_chunk(uint32_t key, int e, bool invalid, int S, int c, MetaWs ws, int *tab) {
+    constexpr int W = kMT / kWave;
+    const int tid = threadIdx.x, w = wave_id();
+    for (int i = tid; i < S * W; i += kMT) tab[i] = 0;
+    const int n_inv_chunk = __syncthreads_count(invalid);
+    const bool act = key < (uint32_t)S;
+    int group;
+    const int rank = few_rank(act ? (int)key : -1, act, S, group);
+    if (act && rank == 0) tab[w * S + key] = group;
+    __syncthreads();
+    for (int s = tid; s < S; s += kMT) {
+        int acc = 0;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) {
+            const int v = tab[ww * S + s];
+            tab[ww * S + s] = acc;
+            acc += v;
+        }
+        ws.hist[(int64_t)c * S + s] = acc;
+    }
+    __syncthreads();
+    const int64_t idx = (int64_t)c * kMT + tid;
+    ws.rows[idx] = e;
+    ws.keys[idx] = (int)key;
+    ws.offlen[idx] = act ? tab[w * S + key] + rank : 0;
+    if (tid == 0 && n_inv_chunk) atomicAdd(&ws.ctl[1], n_inv_chunk);
 }
 
 // Assembly of a multi-chunk build from the chunks' sorted entries in the
@@ -353,6 +391,10 @@ __global__ __launch_bounds__(kMT) void meta_kernel(Src src, int n, int S, int n_
     uint32_t key = (real && raw >= 0 && raw < S) ? (uint32_t)raw : (uint32_t)S;
     int32_t val = e;
 
+    if (split && ws.hist && S <= kBallotSortSlots) {  // meta_assemble_kernel follows in the same stream
+        rank_chunk(key, e, invalid, S, c, ws, dyn);
+        return;
+    }
     if (S <= kBallotSortSlots) {
         ballot_sort(key, val, S, sh, dyn);
     } else {
