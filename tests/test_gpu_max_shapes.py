@@ -5,7 +5,8 @@ on a sample of rows (the first and last rows, the rows of the first and last
 segments, and random ones), and every row that gets no delta is compared
 bitwise in full.  Widths and rank are small, so the oracle stays cheap while
 every index that grows with n (rows, tiles, pieces, chunks) reaches its
-largest value."""
+largest value.  MoE gemm1 and w2 take 2^19 tokens x top_k 8 over 64 experts
+x 128 adapters."""
 import numpy as np
 import pytest
 
@@ -15,6 +16,7 @@ from gpu_util import assert_close_chunked, h16
 from test_gpu_dense import Dev, active, check_y, small_case
 from test_gpu_meta import check_meta
 from test_gpu_moe import SENTINEL, check_pair_meta, run_moe
+from test_gpu_moe_w2 import run_w2
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +69,22 @@ def test_moe_max_pairs():
     check_pair_meta(c, ws)   # sorted pairs, segments, tiles and counts, bit for bit
     sel = sample_rows(rng, O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L), c.E * c.L)
     assert_close_chunked(out, lambda p: O.case_moe_pairs(c, False, p), sel, "moe max pairs", chunk=2048)
+
+
+def test_moe_w2_max_pairs():
+    """The routed down-projection delta, weighted, over 2^22 pairs and 8192
+    (adapter, expert) keys; unrouted rows of y unchanged bit for bit."""
+    c = I.make_moe_w2(75, T=1 << 19, H=8, E=64, top_k=8, I=8, R=8, L=128, neg_frac=0.1)
+    rng = np.random.default_rng(75)
+    c.lora_ids[rng.random(c.T) < 0.01] = c.L + 3
+    c.topk_ids[rng.random(c.topk_ids.shape) < 0.01] = c.E + 1
+    assert c.T * c.top_k == N_MAX and c.E * c.L == S_MULTI_MAX
+    print(f"moe w2 max pairs: T={c.T} pairs={c.T * c.top_k} keys={c.E * c.L}", flush=True)
+    out, _, ws = run_w2(c, True)
+    lora = np.repeat(c.lora_ids, c.top_k)
+    ex = c.topk_ids.reshape(-1)
+    valid = (lora >= 0) & (lora < c.L) & (ex >= 0) & (ex < c.E)
+    assert np.array_equal(out[~valid], c.y[~valid]), "unrouted pairs must keep y bit for bit"
+    check_pair_meta(c, ws)   # sorted pairs, segments, tiles and counts, bit for bit
+    sel = sample_rows(rng, O.moe_keys(c.topk_ids, c.lora_ids, c.E, c.L), c.E * c.L)
+    assert_close_chunked(out, lambda p: O.case_moe_w2_pairs(c, p, True), sel, "moe w2 max pairs", chunk=2048)
