@@ -202,6 +202,25 @@ def test_moe_segments_longer_than_64_pairs(shared):
     check_moe(c, shared, what="long segments")
 
 
+@pytest.mark.parametrize("R", [32, 128])
+@pytest.mark.parametrize("shared", [False, True])
+def test_moe_ranks_32_and_128(R, shared, path):
+    """Rank 32 on the segment kernel (four rank groups in the regular form,
+    two in the shared one) and rank 128, the largest rank taken, on the fused
+    kernel (256 rank rows in the regular form)."""
+    c = small_moe(43, T=200, H=264, E=3, top_k=2, I=72, R=R, L=2)
+    check_moe(c, shared, f"R={R} {path}")
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_moe_small_rank_many_pairs_per_key(shared, path):
+    """More than 64 pairs per (adapter, expert) key on average: rank 16 takes
+    the fused kernel, which spreads a long segment over many workgroups."""
+    c = small_moe(44, T=300, H=264, E=2, top_k=1, I=40, R=16, L=1, neg_frac=0.1)
+    assert c.T * c.top_k > 64 * c.E * c.L
+    check_moe(c, shared, f"many pairs per key {path}")
+
+
 @pytest.mark.parametrize("shared", [False, True])
 def test_moe_rank64_wide_fused(shared, path):
     """Rank 64 takes the fused kernel (the segment kernel serves ranks 8, 16

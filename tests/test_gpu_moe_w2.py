@@ -86,7 +86,7 @@ def test_w2_small(seed, weighted, path):
     check_w2(c, weighted, what=f"seed={seed} {path}")
 
 
-@pytest.mark.parametrize("R", [8, 32, 64])
+@pytest.mark.parametrize("R", [8, 32, 64, 128])
 def test_w2_ragged_k_and_columns(R, path):
     # I = 1032: three k pieces, the last 8 wide; H = 1096: column tail of 72
     c = small_w2(3, T=90, E=2, top_k=2, I=1032, H=1096, R=R, L=2)
