@@ -1306,7 +1306,14 @@ __global__ __launch_bounds__(kFT, (fused_min_waves<WM, NRS, Op>())) void fused_k
     if (un.kind == kUnitShrink || un.kind == kUnitExpand) {
         const int t = un.t;
         if (t >= fa.tile_bound) return;
-        const uint32_t tag = next_tag((uint32_t)load_relaxed(fa.ctl + kCtlGen));
+        // The last completed call's tag, read with a plain (L2-cached) load:
+        // the word changes only at the end of a call, after every unit of it
+        // has read the word, and the previous call's value reaches this launch
+        // through the stream's kernel boundary.  An agent-scope load here, one
+        // per wave of every unit, would pass the L2 and queue thousands of
+        // requests on one address ahead of the unit's own loads (no reuse:
+        // 155 -> 148 us).
+        const uint32_t tag = next_tag((uint32_t)fa.ctl[kCtlGen]);
         int slot_tiles = 0;
         int slot_word = 0;
         if constexpr (Op::kBuild)
