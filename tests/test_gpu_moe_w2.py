@@ -157,6 +157,25 @@ def test_w2_deterministic(w2_case):
     assert np.array_equal(a, b)
 
 
+def test_w2_config_reusing_its_routing(w2_case):
+    """The full w2 config as the bench times it with reused routing: a call
+    that builds the pair metadata, then one that reuses it on a fresh y, bit
+    for bit the same (the first is checked against the oracle in full by
+    test_w2_config_full); the metadata left in the workspace is the oracle's."""
+    c = w2_case
+    ws = B.moe_w2_workspace(c.T, c.top_k, c.E, c.L, c.R, c.I)
+    first, _, _ = run_w2(c, True, ws, calls=1)
+    keep, ta, sa, tb, sb = device_tables(c)
+    y = d16(c.y)
+    B.moe_lora_w2_delta(d16(c.x2), ta, sa, tb, sb, d32(c.topk_ids), d32(c.lora_ids), c.R, y,
+                        num_loras=c.L, topk_weights=d32(c.topk_weights), scale=c.scale, ws=ws,
+                        reuse_routing=True)
+    assert_ws_ok(ws, moe=True, calls=2)
+    assert np.array_equal(h16(y), first)
+    check_pair_meta(c, ws)
+    del keep
+
+
 def test_w2_workspace_reused_across_shapes(w2_case):
     """One workspace, calls of different T in turn, each with its own inputs
     and routing (big, small, big, big): each matches the oracle on every
